@@ -1,0 +1,250 @@
+"""Plain float64 reference of the DSA hot path: indexer -> top-k -> sparse MLA attention.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): imported by tests, the
+smoke check and the benchmark's CPU-baseline leg, never by the product path.
+
+Sources.  The pages describe the method in prose only:
+
+* [DSA-article] "DeepSeek V3.2-Exp Cuts Prolonged-Context Costs With DeepSeek
+  Sparse Consideration (DSA) Whereas Sustaining Benchmark Parity"
+  (nextbusiness24.com), parts "(1) Lightning indexer (FP8, few heads)",
+  "(2) Fine-grained token selection (top-k)" and "Instantiation".
+* [mundobytes] "DeepSeek V3.2-Exp: Sparse Attention, Long Context, and Cheaper
+  API" (mundobytes.com), sections "How it works: Lightning Indexer and Token
+  Selection", "Quick guide to run it locally" (the serving command with
+  `--page-size 64`) and "Open kernels and ecosystem support" (paged
+  indexer-logit kernels).
+
+Where the pages leave a step open, the reading taken here is stated at the
+function.  Every floating-point step runs in float64 on exactly decoded
+inputs, so the only rounding is float64 rounding.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# Number formats
+# ---------------------------------------------------------------------------
+
+
+def _e4m3fn_value(code: int) -> float:
+    """Value of one OCP 8-bit floating-point E4M3 ("e4m3fn") code.
+
+    [DSA-article] (1) says the indexer runs in FP8; the FP8 of the target GPU
+    is the OCP E4M3 format: bit 7 sign, bits 6..3 exponent with bias 7,
+    bits 2..0 mantissa; exponent field 0 encodes subnormals
+    (-1)^s * 2^-6 * m/8; the all-ones exponent with mantissa 7 is NaN; there
+    is no infinity, so exponent 15 with mantissa 0..6 is an ordinary normal
+    number (largest 448).
+    """
+    s = (code >> 7) & 1
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        mag = math.ldexp(m / 8.0, -6)
+    else:
+        mag = math.ldexp(1.0 + m / 8.0, e - 7)
+    return -mag if s else mag
+
+
+_E4M3FN_TABLE = np.array([_e4m3fn_value(c) for c in range(256)], dtype=np.float64)
+
+
+def decode_e4m3fn(codes) -> np.ndarray:
+    """Decode an array of e4m3fn byte codes (uint8) to float64, exactly."""
+    c = np.asarray(codes)
+    if c.dtype != np.uint8:
+        raise TypeError("e4m3fn codes must be uint8")
+    return _E4M3FN_TABLE[c]
+
+
+def decode_bf16(bits) -> np.ndarray:
+    """Decode bfloat16 bit patterns (uint16) to float64, exactly.
+
+    bfloat16 is the upper half of an IEEE-754 binary32: the value is the
+    binary32 whose bits are ``bits << 16``.
+    """
+    b = np.asarray(bits)
+    if b.dtype != np.uint16:
+        raise TypeError("bf16 values must be passed as uint16 bit patterns")
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Cache addressing (contiguous or 64-token pages)
+# ---------------------------------------------------------------------------
+
+
+def logical_rows(cache: np.ndarray, b: int, n: int, block_table=None, page_size: int = 64) -> np.ndarray:
+    """First ``n`` logical token rows of sequence ``b`` of a cache.
+
+    Contiguous caches are laid out ``[B, L_max, ...]``.  Paged caches follow
+    the serving layout [mundobytes] names (pages of 64 tokens, with the
+    indexer-logit kernels also offered in paged form): ``[P, page_size, ...]``
+    physical pages, and ``block_table[b, j]`` is the physical page holding
+    logical tokens ``j*page_size .. j*page_size+page_size-1`` of sequence b.
+    """
+    if block_table is None:
+        return cache[b, :n]
+    npages = -(-n // page_size)
+    pages = np.asarray(block_table)[b, :npages]
+    rows = cache[pages].reshape((npages * page_size,) + cache.shape[2:])
+    return rows[:n]
+
+
+# ---------------------------------------------------------------------------
+# (a1) Lightning indexer
+# ---------------------------------------------------------------------------
+
+
+def indexer_logits_row(q8_t, qs_t, w_t, k8_rows, ks_rows) -> np.ndarray:
+    """Index logits of one query token against ``n`` key tokens, float64.
+
+    [DSA-article] (1): for a query token, a light scoring function computes an
+    index logit I[t,s] against each earlier token, using a few small indexer
+    heads with a ReLU, in FP8.  The pages print no formula; the reading taken
+    here is
+
+        I[t,s] = qs[t] * ks[s] * sum_j w[t,j] * ReLU( sum_d q[t,j,d] * k[s,d] )
+
+    with q (``[H_I, D_I]``) and k (``[n, D_I]``) the decoded FP8 codes,
+    one key vector per token shared by all indexer heads, a per-head weight
+    w[t,j], and positive per-token dequantisation scales qs, ks (positive
+    scales commute with the ReLU, so applying them outside is exact).
+    """
+    q = decode_e4m3fn(np.asarray(q8_t))                 # [H_I, D_I]
+    k = decode_e4m3fn(np.asarray(k8_rows))              # [n, D_I]
+    w = np.asarray(w_t, dtype=np.float64)               # [H_I]
+    dots = k @ q.T                                      # [n, H_I]   q[t,j] . k[s]
+    relu = np.maximum(dots, 0.0)
+    acc = relu @ w                                      # sum over heads
+    return float(qs_t) * np.asarray(ks_rows, dtype=np.float64) * acc
+
+
+def indexer_logits(q8, qs, w, k8, ks, seq_id, pos, block_table=None, page_size: int = 64) -> np.ndarray:
+    """Index logits for every query token, ``[T, max(pos)+1]`` float64.
+
+    Query t belongs to sequence ``seq_id[t]`` and sits at position ``pos[t]``;
+    it scores the tokens s = 0 .. pos[t] of its sequence.  [DSA-article] (1)
+    says "earlier tokens"; the reading taken here includes the query's own
+    position (s <= t), the causal rule of prefill.  Entries past pos[t] are
+    NaN (they are not defined).
+    """
+    seq_id = np.asarray(seq_id)
+    pos = np.asarray(pos)
+    T = len(pos)
+    width = int(pos.max()) + 1 if T else 0
+    out = np.full((T, width), np.nan)
+    for t in range(T):
+        n = int(pos[t]) + 1
+        b = int(seq_id[t])
+        krows = logical_rows(k8, b, n, block_table, page_size)
+        srows = logical_rows(ks, b, n, block_table, page_size)
+        out[t, :n] = indexer_logits_row(q8[t], qs[t], w[t], krows, srows)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# (a2) Fine-grained token selection
+# ---------------------------------------------------------------------------
+
+
+def topk_select(values, n_valid: int, k: int) -> np.ndarray:
+    """Positions of the top-k entries of one row; ``int32[k]`` in rank order.
+
+    [DSA-article] (2): each query keeps only its top-k key-value entries.  A
+    plain definition: order the valid positions s = 0 .. n_valid-1 by value,
+    largest first, and take the first min(k, n_valid).  Readings where the
+    pages are silent: equal values are ordered by the lower position first;
+    -0 and +0 are equal (IEEE comparison); when fewer than k positions are
+    valid, all of them are kept and the rest of the row is padded with -1.
+    The values are compared exactly as given (the library stores logits in
+    float32, and so are the values passed here).
+    """
+    v = np.asarray(values)[:n_valid]
+    v = np.where(v == 0, np.zeros((), v.dtype), v)      # -0 == +0
+    s = np.arange(n_valid)
+    order = np.lexsort((s, -v))                          # value desc, then position asc
+    take = order[: min(k, n_valid)]
+    out = np.full(k, -1, dtype=np.int32)
+    out[: len(take)] = take
+    return out
+
+
+# ---------------------------------------------------------------------------
+# (a3) Sparse attention under MLA in MQA mode
+# ---------------------------------------------------------------------------
+
+
+def sparse_mla_attention(q_bits, kv_bits, idx, seq_id, scale: float, d_v: int = 512,
+                         block_table=None, page_size: int = 64):
+    """Softmax attention of every query head over its selected latent rows.
+
+    [DSA-article] (2): standard attention runs only over the selected subset.
+    "Instantiation": DSA runs under MLA in MQA mode, so each latent KV entry
+    is shared by all query heads.  Reading: a latent row holds D = 576 values
+    (512 without rope followed by 64 rope); the key is the whole row and the
+    value is its first ``d_v`` = 512 entries; entries of ``idx`` equal to -1
+    are padding and are skipped.
+
+    For query t and head h over the selected rows i:
+        z_i = scale * <q[t,h,:], row_i[:D]>
+        o[t,h,:] = sum_i softmax(z)_i * row_i[:d_v]
+        lse[t,h] = log sum_i exp(z_i)          (natural log)
+    An empty selection gives o = 0 and lse = -inf.
+
+    ``q_bits`` is ``uint16[T, H, D]`` and ``kv_bits`` the bf16 cache as uint16
+    (contiguous ``[B, L_max, D]`` or paged ``[P, page, D]``).  Returns float64
+    ``o[T, H, d_v]`` and ``lse[T, H]``.
+    """
+    q_bits = np.asarray(q_bits)
+    idx = np.asarray(idx)
+    seq_id = np.asarray(seq_id)
+    T, H, D = q_bits.shape
+    out = np.zeros((T, H, d_v))
+    lse = np.full((T, H), -np.inf)
+    for t in range(T):
+        sel = idx[t][idx[t] >= 0].astype(np.int64)
+        if sel.size == 0:
+            continue
+        b = int(seq_id[t])
+        n = int(sel.max()) + 1
+        rows = decode_bf16(logical_rows(kv_bits, b, n, block_table, page_size)[sel])   # [m, D]
+        q = decode_bf16(q_bits[t])                                                    # [H, D]
+        z = scale * (q @ rows.T)                                                      # [H, m]
+        m = z.max(axis=1, keepdims=True)
+        p = np.exp(z - m)
+        l = p.sum(axis=1, keepdims=True)
+        out[t] = (p @ rows[:, :d_v]) / l
+        lse[t] = m[:, 0] + np.log(l[:, 0])
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# (a4) The whole path
+# ---------------------------------------------------------------------------
+
+
+def dsa_forward(iq8, iqs, iw, ik8, iks, q_bits, kv_bits, seq_id, pos, k: int, scale: float,
+                d_v: int = 512, block_table=None, page_size: int = 64):
+    """Indexer -> top-k -> sparse attention, as [DSA-article] chains them
+    ("FP8 index -> top-k selection -> sparse core attention").
+
+    The selection decides integers from floating values, so it takes its
+    decision on the logits rounded to float32, the precision in which the
+    library stores them.  Returns ``(logits_f64, idx, out, lse)``.
+    """
+    logits = indexer_logits(iq8, iqs, iw, ik8, iks, seq_id, pos, block_table, page_size)
+    T = len(pos)
+    idx = np.full((T, k), -1, dtype=np.int32)
+    for t in range(T):
+        n = int(pos[t]) + 1
+        idx[t] = topk_select(logits[t, :n].astype(np.float32), n, k)
+    out, lse = sparse_mla_attention(q_bits, kv_bits, idx, seq_id, scale, d_v, block_table, page_size)
+    return logits, idx, out, lse

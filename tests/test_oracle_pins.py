@@ -1,0 +1,339 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each test pins one part of the oracle to a library routine, a closed form,
+an invariant, or brute force on a tiny input, chosen so that a plausible slip
+(a dropped ReLU, a wrong exponent bias, a transposed operand, an off-by-one
+causal range, a wrong tie rule) fails at least one of them.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_attention_long_03_amd import inputs as I
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- formats
+
+def test_e4m3fn_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = O.decode_e4m3fn(codes)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(lib)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], lib[~nan])
+    # signed zero is kept
+    assert math.copysign(1.0, ours[0x80]) == -1.0
+
+
+def test_e4m3fn_closed_forms():
+    # OCP 8-bit FP, E4M3 variant: bias 7, subnormals at exponent 0, only
+    # S.1111.111 is NaN, so 448 = 2^8 * 1.75 is the largest finite value.
+    with open(os.path.join(GOLDEN, "e4m3fn_points.json")) as f:
+        pts = json.load(f)["points"]
+    for code_hex, val in pts:
+        got = O.decode_e4m3fn(np.array([int(code_hex, 16)], dtype=np.uint8))[0]
+        if val == "nan":
+            assert math.isnan(got), code_hex
+        else:
+            assert got == float(val), (code_hex, got, val)
+
+
+def test_e4m3fn_positive_codes_strictly_increase():
+    v = O.decode_e4m3fn(np.arange(0, 0x7F, dtype=np.uint8))
+    assert np.all(np.diff(v) > 0)
+
+
+def test_bf16_matches_torch():
+    g = np.random.default_rng(3)
+    x = torch.from_numpy(g.standard_normal(4096).astype(np.float32) * 100).to(torch.bfloat16)
+    bits = x.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.decode_bf16(bits), x.to(torch.float64).numpy())
+
+
+# ----------------------------------------------------------------- indexer
+
+def _codes(vals):
+    return torch.tensor(vals, dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_indexer_hand_example():
+    # two heads, two dims; every value is exact in e4m3fn
+    q8 = _codes([[1.0, 2.0], [-1.0, 0.5]])            # head0=(1,2), head1=(-1,0.5)
+    w = np.array([0.5, 2.0])
+    qs = 2.0
+    k8 = _codes([[1.0, 1.0], [-1.0, 1.0], [2.0, -1.0]])
+    ks = np.array([1.0, 0.5, 4.0])
+    # key0: dots (3, -0.5) -> relu (3, 0)   -> 0.5*3         = 1.5 -> *2*1   = 3
+    # key1: dots (1, 1.5)  -> relu (1, 1.5) -> 0.5*1 + 2*1.5 = 3.5 -> *2*0.5 = 3.5
+    # key2: dots (0, -2.5) -> relu (0, 0)   -> 0               -> 0
+    got = O.indexer_logits_row(q8, qs, w, k8, ks)
+    assert np.array_equal(got, np.array([3.0, 3.5, 0.0]))
+
+
+def test_indexer_single_head_is_relu_of_matmul():
+    g = torch.Generator().manual_seed(5)
+    q8, _ = I.quantize_e4m3fn(torch.randn(1, 1, 64, generator=g))
+    k8, _ = I.quantize_e4m3fn(torch.randn(300, 64, generator=g))
+    got = O.indexer_logits_row(q8[0].numpy(), 1.0, np.ones(1), k8.numpy(), np.ones(300))
+    qf = q8[0].view(torch.float8_e4m3fn).to(torch.float64)
+    kf = k8.view(torch.float8_e4m3fn).to(torch.float64)
+    ref = torch.clamp(torch.matmul(kf, qf.T)[:, 0], min=0).numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_indexer_general_vs_torch_route():
+    # non-square head/dim counts so a transposed operand cannot pass
+    g = torch.Generator().manual_seed(6)
+    q8, qs = I.quantize_e4m3fn(torch.randn(1, 5, 48, generator=g))
+    k8, ks = I.quantize_e4m3fn(torch.randn(77, 48, generator=g))
+    w = torch.rand(5, generator=g, dtype=torch.float64)
+    got = O.indexer_logits_row(q8[0].numpy(), float(qs[0]), w.numpy(), k8.numpy(), ks.numpy())
+    qf = q8[0].view(torch.float8_e4m3fn).to(torch.float64)           # [5, 48]
+    kf = k8.view(torch.float8_e4m3fn).to(torch.float64)              # [77, 48]
+    per_head = torch.relu(torch.mm(qf, kf.T))                         # [5, 77]
+    ref = (w[:, None] * per_head).sum(0) * float(qs[0]) * ks.double()
+    np.testing.assert_allclose(got, ref.numpy(), rtol=1e-13, atol=0)
+
+
+def test_indexer_causal_range_includes_own_position():
+    cfg = I.scaled(I.CONFIGS["tiny"], L=300, queries_per_seq=4)
+    x = I.make_inputs(cfg)
+    lg = O.indexer_logits(x.iq8.numpy(), x.iqs.numpy(), x.iw.numpy(), x.ik8.numpy(), x.iks.numpy(),
+                          x.seq_id.numpy(), x.pos.numpy())
+    for t in range(x.T):
+        p = int(x.pos[t])
+        assert not np.isnan(lg[t, : p + 1]).any()
+        assert np.isnan(lg[t, p + 1:]).all()
+        own = O.indexer_logits_row(x.iq8[t].numpy(), float(x.iqs[t]), x.iw[t].numpy(),
+                                   x.ik8[0, p:p + 1].numpy(), x.iks[0, p:p + 1].numpy())
+        assert lg[t, p] == own[0]
+
+
+def test_indexer_weight_doubling_is_exact():
+    x = I.make_inputs(I.scaled(I.CONFIGS["tiny"], L=1024, queries_per_seq=2))
+    args = (x.iq8.numpy(), x.iqs.numpy())
+    a = O.indexer_logits(*args, x.iw.numpy(), x.ik8.numpy(), x.iks.numpy(), x.seq_id.numpy(), x.pos.numpy())
+    b = O.indexer_logits(*args, 2 * x.iw.numpy(), x.ik8.numpy(), x.iks.numpy(), x.seq_id.numpy(), x.pos.numpy())
+    assert np.array_equal(2 * a[~np.isnan(a)], b[~np.isnan(b)])
+    for t in range(x.T):
+        n = int(x.pos[t]) + 1
+        assert np.array_equal(O.topk_select(a[t, :n].astype(np.float32), n, 64),
+                              O.topk_select(b[t, :n].astype(np.float32), n, 64))
+
+
+def test_indexer_head_permutation_invariant():
+    x = I.make_inputs(I.scaled(I.CONFIGS["tiny"], L=512, queries_per_seq=1))
+    perm = np.random.default_rng(0).permutation(x.iq8.shape[1])
+    a = O.indexer_logits_row(x.iq8[0].numpy(), float(x.iqs[0]), x.iw[0].numpy(), x.ik8[0].numpy(), x.iks[0].numpy())
+    b = O.indexer_logits_row(x.iq8[0].numpy()[perm], float(x.iqs[0]), x.iw[0].numpy()[perm],
+                             x.ik8[0].numpy(), x.iks[0].numpy())
+    np.testing.assert_allclose(a, b, rtol=1e-12)
+
+
+def test_indexer_all_negative_heads_give_zero():
+    q8 = _codes([[1.0, 1.0], [2.0, 0.5]])
+    k8 = _codes([[-1.0, -1.0], [-0.5, -2.0]])
+    got = O.indexer_logits_row(q8, 1.0, np.array([0.3, 0.7]), k8, np.array([1.0, 1.0]))
+    assert np.array_equal(got, np.zeros(2))
+
+
+def test_paged_rows_equal_contiguous_rows():
+    g = np.random.default_rng(1)
+    L, ps = 300, 64
+    cont = g.integers(0, 255, size=(2, L, 8), dtype=np.uint8)
+    npg = -(-L // ps)
+    perm = g.permutation(2 * npg)
+    paged = np.zeros((2 * npg, ps, 8), dtype=np.uint8)
+    bt = perm.reshape(2, npg)
+    for b in range(2):
+        for j in range(npg):
+            chunk = cont[b, j * ps:(j + 1) * ps]
+            paged[bt[b, j], : len(chunk)] = chunk
+    for b in range(2):
+        for n in (1, 63, 64, 65, 300):
+            assert np.array_equal(O.logical_rows(paged, b, n, bt, ps), cont[b, :n])
+
+
+# ----------------------------------------------------------------- top-k
+
+def test_topk_hand_examples():
+    v = np.array([3, 1, 3, 2, 3, 0], dtype=np.float32)
+    assert list(O.topk_select(v, 6, 2)) == [0, 2]
+    assert list(O.topk_select(v, 6, 4)) == [0, 2, 4, 3]
+    assert list(O.topk_select(v, 6, 8)) == [0, 2, 4, 3, 1, 5, -1, -1]
+    assert list(O.topk_select(v, 3, 2)) == [0, 2]            # only the first 3 are valid
+    z = np.array([-0.0, 0.0, -1.0, -0.0], dtype=np.float32)
+    assert list(O.topk_select(z, 4, 2)) == [0, 1]            # -0 == +0, lower position first
+
+
+def _rank_ok(v, n, k, sel):
+    """Brute-force characterisation of the top-k set with the lower-position tie rule."""
+    sel_set = set(int(s) for s in sel if s >= 0)
+    assert len(sel_set) == min(k, n)
+    for i in range(n):
+        better = sum(1 for s in range(n) if v[s] > v[i] or (v[s] == v[i] and s < i))
+        assert (better < k) == (i in sel_set), (i, better)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_rank_characterisation(seed):
+    g = np.random.default_rng(seed)
+    n = int(g.integers(1, 200))
+    k = int(g.integers(1, 64))
+    v = g.integers(0, 6, size=n).astype(np.float32)          # many ties
+    if seed % 2:
+        v = np.where(v == 0, np.float32(-0.0), v)
+    _rank_ok(v, n, k, O.topk_select(v, n, k))
+
+
+def test_topk_matches_stable_argsort():
+    g = np.random.default_rng(9)
+    v = g.integers(0, 256, size=5000).astype(np.float32)
+    got = O.topk_select(v, 5000, 2048)
+    ref = np.argsort(-v, kind="stable")[:2048]
+    assert np.array_equal(got, ref)
+
+
+# ----------------------------------------------------------------- attention
+
+def _bits(x64):
+    return torch.tensor(x64, dtype=torch.float64).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_attention_two_row_closed_form():
+    D, dv, H = 576, 512, 2
+    kv = np.zeros((1, 2, D))
+    kv[0, 1, 0] = 1.0                   # key1 . q = 1, key0 . q = 0
+    kv[0, 0, 1] = 2.0
+    kv[0, 1, 1] = -4.0
+    q = np.zeros((1, H, D))
+    q[0, :, 0] = 1.0
+    out, lse = O.sparse_mla_attention(_bits(q), _bits(kv), np.array([[0, 1]]), np.array([0]), 1.0, dv)
+    p1 = math.e / (1 + math.e)
+    p0 = 1 - p1
+    for h in range(H):
+        assert abs(out[0, h, 0] - p1) < 1e-15
+        assert abs(out[0, h, 1] - (2 * p0 - 4 * p1)) < 1e-15
+        assert abs(lse[0, h] - math.log(1 + math.e)) < 1e-15
+    assert np.all(out[0, :, 2:] == 0)
+
+
+def test_attention_zero_query_gives_mean_of_values():
+    g = np.random.default_rng(2)
+    kv = _bits(g.standard_normal((1, 50, 576)))
+    sel = np.array([[3, 7, 49, 0, -1, 11]])
+    out, lse = O.sparse_mla_attention(np.zeros((1, 4, 576), np.uint16), kv, sel, np.array([0]), 0.3)
+    rows = O.decode_bf16(kv[0, [3, 7, 49, 0, 11], :512])
+    for h in range(4):
+        np.testing.assert_allclose(out[0, h], rows.mean(0), rtol=0, atol=1e-15)
+        assert abs(lse[0, h] - math.log(5)) < 1e-15
+
+
+def test_attention_all_selected_equals_dense_causal_sdpa():
+    # With every causal position selected, sparse attention must reduce to
+    # dense causal softmax attention (torch's SDPA, float64, as the library).
+    g = np.random.default_rng(4)
+    L, H, D, dv = 40, 3, 576, 512
+    kv = _bits(g.standard_normal((1, L, D)) / 24)
+    q = _bits(g.standard_normal((L, H, D)) / 24)
+    pos = np.arange(L)
+    idx = np.full((L, 64), -1)
+    for t in range(L):
+        idx[t, : t + 1] = g.permutation(t + 1)          # any order
+    out, lse = O.sparse_mla_attention(q, kv, idx, np.zeros(L, int), 1 / 24, dv)
+    qt = torch.from_numpy(O.decode_bf16(q)).permute(1, 0, 2)[None]               # [1,H,L,D]
+    kvt = torch.from_numpy(O.decode_bf16(kv[0]))                                  # [L,D]
+    K = kvt[None, None].expand(1, H, L, D)
+    V = kvt[:, :dv][None, None].expand(1, H, L, dv)
+    mask = torch.from_numpy(pos[None, :] <= pos[:, None])
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, K, V, attn_mask=mask, scale=1 / 24)
+    np.testing.assert_allclose(out, ref[0].permute(1, 0, 2).numpy(), rtol=1e-11, atol=1e-14)
+    # lse against a library log-sum-exp
+    from scipy.special import logsumexp
+    z = (torch.einsum("hld,sd->hls", qt[0], kvt) / 24).numpy()
+    for t in range(L):
+        np.testing.assert_allclose(lse[t], logsumexp(z[:, t, : t + 1], axis=1), rtol=1e-12)
+
+
+def test_attention_order_and_padding_invariant():
+    g = np.random.default_rng(8)
+    kv = _bits(g.standard_normal((2, 100, 576)))
+    q = _bits(g.standard_normal((2, 5, 576)) / 24)
+    idx = np.stack([g.permutation(100)[:30], g.permutation(100)[:30]])
+    a, la = O.sparse_mla_attention(q, kv, idx, np.array([1, 0]), 1 / 24)
+    idx2 = np.full((2, 40), -1)
+    for t in range(2):
+        idx2[t, g.permutation(40)[:30]] = idx[t][g.permutation(30)]
+    b, lb = O.sparse_mla_attention(q, kv, idx2, np.array([1, 0]), 1 / 24)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(la, lb, rtol=1e-12)
+    # convex hull of the selected value rows
+    for t, b_ in ((0, 1), (1, 0)):
+        rows = O.decode_bf16(kv[b_, idx[t], :512])
+        assert np.all(a[t] >= rows.min(0) - 1e-12) and np.all(a[t] <= rows.max(0) + 1e-12)
+
+
+def test_attention_empty_selection():
+    out, lse = O.sparse_mla_attention(np.zeros((1, 2, 576), np.uint16), np.zeros((1, 4, 576), np.uint16),
+                                      np.full((1, 8), -1), np.array([0]), 1.0)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+# ----------------------------------------------------------------- whole path
+
+def test_forward_with_k_at_least_L_is_dense_attention():
+    # k >= number of visible keys: the selection keeps everything and DSA is
+    # exactly dense causal attention over the latent rows.
+    cfg = I.scaled(I.CONFIGS["tiny"], L=200, k=256, queries_per_seq=5)
+    x = I.make_inputs(cfg)
+    args = [t.numpy() for t in (x.iq8, x.iqs, x.iw, x.ik8, x.iks)]
+    q = I.bf16_bits(x.q)
+    kv = I.bf16_bits(x.kv)
+    _, idx, out, _ = O.dsa_forward(*args, q, kv, x.seq_id.numpy(), x.pos.numpy(), cfg.k, cfg.scale)
+    for t in range(x.T):
+        p = int(x.pos[t])
+        assert sorted(idx[t][idx[t] >= 0].tolist()) == list(range(p + 1))
+        qt = torch.from_numpy(O.decode_bf16(q[t]))                        # [H, D]
+        kvt = torch.from_numpy(O.decode_bf16(kv[0, : p + 1]))
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt[None, :, None, :], kvt[None, None].expand(1, cfg.H, p + 1, 576),
+            kvt[None, None, :, :512].expand(1, cfg.H, p + 1, 512), scale=cfg.scale)[0, :, 0]
+        np.testing.assert_allclose(out[t], ref.numpy(), rtol=1e-11, atol=1e-15)
+
+
+def test_page_constants_from_the_pages():
+    with open(os.path.join(GOLDEN, "page_constants.json")) as f:
+        c = json.load(f)
+    for name in ("decode32k", "decode128k", "prefill64k", "ragged_paged"):
+        assert I.CONFIGS[name].k == c["top_k"]["value"]
+    assert I.CONFIGS["ragged_paged"].page_size == c["page_size"]["value"]
+
+
+def test_planted_far_keys_take_the_whole_selection():
+    # Long-context decode: 2% planted keys in the far half of a 128K context;
+    # the selection must consist of planted far positions only.
+    cfg = I.scaled(I.CONFIGS["decode128k"], B=1)
+    x = I.make_inputs(cfg)
+    lg = O.indexer_logits_row(x.iq8[0].numpy(), float(x.iqs[0]), x.iw[0].numpy(), x.ik8[0].numpy(), x.iks[0].numpy())
+    sel = O.topk_select(lg.astype(np.float32), len(lg), cfg.k)
+    planted = set(x.planted[0].tolist())
+    assert all(int(s) in planted for s in sel)
+    assert max(sel) < cfg.L // 2
+
+
+def test_generator_is_deterministic():
+    import hashlib
+    a = I.make_inputs(I.scaled(I.CONFIGS["ragged_paged"], B=3, L=3000, min_len=100, H_I=4, D_I=64, H=4))
+    b = I.make_inputs(I.scaled(I.CONFIGS["ragged_paged"], B=3, L=3000, min_len=100, H_I=4, D_I=64, H=4))
+    for name in ("iq8", "iqs", "iw", "q", "ik8", "iks", "kv", "block_table", "pos", "seq_id"):
+        ha = hashlib.sha256(getattr(a, name).contiguous().view(torch.uint8).numpy().tobytes()).hexdigest()
+        hb = hashlib.sha256(getattr(b, name).contiguous().view(torch.uint8).numpy().tobytes()).hexdigest()
+        assert ha == hb, name
