@@ -1,0 +1,172 @@
+/*
+ * dsa.h — C ABI of the MI355X (gfx950) DeepSeek Sparse Attention hot path.
+ *
+ * The path, as the DeepSeek-V3.2-Exp articles describe it ("DeepSeek V3.2-Exp
+ * Cuts Prolonged-Context Costs With DeepSeek Sparse Consideration (DSA)",
+ * nextbusiness24.com, parts (1), (2) and "Instantiation"):
+ *
+ *   (1) a lightning indexer scores, for each query token, every earlier token
+ *       of its sequence with a few small FP8 heads and a ReLU;
+ *   (2) each query keeps only its top-k (k = 2048) tokens;
+ *   (3) standard softmax attention runs over that subset, under MLA in MQA
+ *       mode: one latent KV row per token is shared by all query heads.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers documented "device" must point to GPU memory (hipMalloc or
+ *   torch CUDA tensors); descriptor structs are host memory and are read
+ *   before the call returns.
+ * - The caller owns every buffer, including workspaces.  The library
+ *   allocates no memory and keeps no state between calls, so it is
+ *   re-entrant; calls on one stream run in order.
+ * - Every call only enqueues work on `stream` and returns; nothing waits.
+ * - Errors: each call returns DSA_OK (0) or a negative DSA_ERR_* code and
+ *   enqueues nothing when it fails validation.  Validation covers host-side
+ *   scalars, null pointers, alignment and workspace size.  The contents of
+ *   device index arrays (seq_id, pos, valid_len, idx, block_table) are
+ *   trusted: out-of-range values there are undefined behaviour.
+ * - All tensors are dense, row-major, with the strides stated per argument.
+ * - Key positions are logical token positions within a sequence (0-based),
+ *   so results do not depend on whether the caches are paged.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+/* status codes */
+#define DSA_OK 0
+#define DSA_ERR_INVALID_ARG (-1) /* null pointer, bad size, misaligned buffer   */
+#define DSA_ERR_UNSUPPORTED (-2) /* valid request outside the built shapes       */
+#define DSA_ERR_WORKSPACE (-3)   /* workspace missing or smaller than required    */
+#define DSA_ERR_HIP (-4)         /* a HIP launch reported an error                */
+
+/* Query tokens.  Query t belongs to sequence seq_id[t] and sits at logical
+ * position pos[t]; it sees the tokens 0..pos[t] of its sequence (its own
+ * position included: the causal rule).  Decode has one or a few trailing
+ * tokens per sequence; prefill has pos[t] = t for one sequence.           */
+typedef struct dsa_queries {
+  int32_t T;              /* number of query tokens, >= 0                       */
+  int32_t B;              /* number of sequences, >= 1                          */
+  const int32_t* seq_id;  /* device int32[T], each in [0, B)                    */
+  const int32_t* pos;     /* device int32[T], each in [0, max_len)              */
+  int32_t max_len;        /* host: an upper bound of pos[t] + 1 over all t      */
+} dsa_queries;
+
+/* Cache layout, shared by the indexer key cache and the latent KV cache.
+ * Contiguous: tensors are [B, seq_capacity, ...] and token s of sequence b is
+ *   row b * seq_capacity + s.
+ * Paged (the serving layout with 64-token pages, "DeepSeek V3.2-Exp: Sparse
+ *   Attention, Long Context, and Cheaper API", mundobytes.com, "Quick guide to
+ *   run it locally" and "Open kernels and ecosystem support"): tensors are
+ *   [num_pages, page_size, ...]; token s of sequence b lives in physical page
+ *   block_table[b * max_pages + s / page_size], row s % page_size.          */
+typedef struct dsa_kv_layout {
+  int32_t paged;              /* 0 = contiguous, 1 = paged                       */
+  int32_t page_size;          /* paged: must be 64                               */
+  const int32_t* block_table; /* paged: device int32[B, max_pages]               */
+  int32_t max_pages;          /* paged: row stride of block_table                */
+  int32_t num_pages;          /* paged: number of physical pages (>= 1)          */
+  int64_t seq_capacity;       /* contiguous: tokens per sequence (>= max_len)    */
+} dsa_kv_layout;
+
+/* ---------------------------------------------------------------------------
+ * (1) Lightning indexer logits.
+ *   logits[t * ld_logits + s] =
+ *       q_scale[t] * k_scale[s] * sum_j w[t,j] * ReLU( sum_d q[t,j,d] * k[s,d] )
+ * for s in 0..pos[t], where q and k are OCP e4m3fn FP8 codes (the FP8 of
+ * gfx950) and the dot products accumulate in fp32 on the matrix cores.
+ * Entries s > pos[t] of a row are left unwritten.
+ *
+ *   H_I, D_I  : indexer heads and head dim; built: (H_I, D_I) in
+ *               {(64,128), (64,64), (4,128), (4,64)}.
+ *   q_fp8     : device uint8[T, H_I, D_I]       (16-byte aligned)
+ *   q_scale   : device float[T]                 per-token dequantisation scale
+ *   w         : device float[T, H_I]            per-head weights (any sign)
+ *   k_fp8     : device uint8 cache, [*, D_I] per token (layout above; 16-byte aligned)
+ *   k_scale   : device float cache, one per token (layout above)
+ *   logits    : device float[T, ld_logits], ld_logits >= max_len, multiple of 4
+ * ------------------------------------------------------------------------- */
+int dsa_indexer_logits(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,
+                       const uint8_t* q_fp8, const float* q_scale, const float* w, const uint8_t* k_fp8,
+                       const float* k_scale, float* logits, int64_t ld_logits, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * (2) Top-k selection ("DeepSeek V3.2-Exp Cuts Prolonged-Context Costs ...",
+ * part (2)).  Row t holds valid_len[t] values logits[t*ld_logits + s],
+ * s < valid_len[t].  idx[t, :] receives the positions of the k largest values,
+ * equal values ordered by the lower position first and -0 equal to +0; when
+ * valid_len[t] <= k every position is kept and the row is padded with -1.
+ * The positions are written in a deterministic order that is not sorted by
+ * value.  NaN values give an unspecified (but in-range) selection.
+ *
+ *   logits    : device float[T, ld_logits]
+ *   valid_len : device int32[T], each in [0, max_len]
+ *   max_len   : host upper bound of valid_len, <= ld_logits
+ *   k         : 1 <= k <= 2048
+ *   idx       : device int32[T, k]
+ *   workspace : device, >= dsa_workspace_bytes(DSA_OP_TOPK, T, max_len, 0, k), 256-byte aligned
+ * ------------------------------------------------------------------------- */
+int dsa_topk(const float* logits, int64_t ld_logits, const int32_t* valid_len, int32_t T, int32_t max_len,
+             int32_t k, int32_t* idx, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * (3) Sparse attention under MLA in MQA mode ("... Sparse Consideration
+ * (DSA)", parts (2) and "Instantiation").  For query t, head h and the
+ * selected positions i = idx[t, j] != -1 of sequence seq_id[t]:
+ *     z_i = sm_scale * <q[t,h,0:576], kv_row_i[0:576]>
+ *     out[t,h,c] = sum_i softmax(z)_i * kv_row_i[c],   c < 512
+ *     lse[t,h]   = ln sum_i exp(z_i)
+ * An all-padding row gives out = 0 and lse = -inf.
+ *
+ *   H         : query heads; built: 16, 32, 64 or 128
+ *   q_bf16    : device bf16[T, H, 576]          (16-byte aligned)
+ *   kv_bf16   : device bf16 latent cache, 576 per token (layout above; 16-byte aligned)
+ *   idx       : device int32[T, k], entries in [0, pos[t]] or -1
+ *   k         : 1 <= k <= 2048
+ *   out_bf16  : device bf16[T, H, 512]
+ *   lse       : device float[T, H] or NULL
+ *   workspace : device, >= dsa_workspace_bytes(DSA_OP_ATTN, T, 0, H, k), 256-byte aligned
+ * ------------------------------------------------------------------------- */
+int dsa_sparse_mla_attn(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H, const void* q_bf16,
+                        const void* kv_bf16, const int32_t* idx, int32_t k, float sm_scale, void* out_bf16,
+                        float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * (1) -> (2) -> (3) on one stream ("FP8 index -> top-k selection -> sparse
+ * core attention").  Arguments as above; idx_out (device int32[T, k]) receives
+ * the selection, or may be NULL to keep it inside the workspace.
+ *   workspace : device, >= dsa_workspace_bytes(DSA_OP_FORWARD, T, max_len, H, k)
+ * ------------------------------------------------------------------------- */
+int dsa_forward(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,
+                const uint8_t* iq_fp8, const float* iq_scale, const float* iw, const uint8_t* ik_fp8,
+                const float* ik_scale, int32_t H, const void* q_bf16, const void* kv_bf16, int32_t k,
+                float sm_scale, void* out_bf16, float* lse, int32_t* idx_out, void* workspace,
+                size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace sizes (bytes) for an operation; 0 when none is needed. */
+#define DSA_OP_TOPK 1
+#define DSA_OP_ATTN 2
+#define DSA_OP_FORWARD 3
+size_t dsa_workspace_bytes(int32_t op, int32_t T, int32_t max_len, int32_t H, int32_t k);
+
+/* Static string for a status code (never NULL). */
+const char* dsa_status_str(int32_t status);
+
+/* DSA_ABI_VERSION of the built library. */
+int32_t dsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

@@ -1,0 +1,168 @@
+"""ctypes binding of the DSA C ABI (``include/dsa.h``).
+
+Argument marshalling only: tensors become device pointers, the current torch
+stream becomes the ``hipStream_t``, and a non-zero status becomes a
+:class:`DSAError`.  Every step of the computation runs in the HIP library;
+there is no fallback.  The functions keep the C names.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+DSA_OK = 0
+DSA_ERR_INVALID_ARG = -1
+DSA_ERR_UNSUPPORTED = -2
+DSA_ERR_WORKSPACE = -3
+DSA_ERR_HIP = -4
+DSA_OP_TOPK, DSA_OP_ATTN, DSA_OP_FORWARD = 1, 2, 3
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {lib().dsa_status_str(status).decode()} (status {status})")
+        self.status = status
+
+
+class dsa_queries(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("B", ctypes.c_int32), ("seq_id", ctypes.c_void_p),
+                ("pos", ctypes.c_void_p), ("max_len", ctypes.c_int32)]
+
+
+class dsa_kv_layout(ctypes.Structure):
+    _fields_ = [("paged", ctypes.c_int32), ("page_size", ctypes.c_int32), ("block_table", ctypes.c_void_p),
+                ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("seq_capacity", ctypes.c_int64)]
+
+
+EXPORTS = ("dsa_indexer_logits", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward", "dsa_workspace_bytes",
+           "dsa_status_str", "dsa_abi_version")
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load ``libdsa.so`` (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m sparse_attention_long_03_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    Q, KV = ctypes.POINTER(dsa_queries), ctypes.POINTER(dsa_kv_layout)
+    L.dsa_indexer_logits.argtypes = [Q, KV, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp]
+    L.dsa_topk.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp, sz, vp]
+    L.dsa_sparse_mla_attn.argtypes = [Q, KV, i32, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
+    L.dsa_forward.argtypes = [Q, KV, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]
+    L.dsa_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.dsa_workspace_bytes.restype = sz
+    L.dsa_status_str.argtypes = [i32]
+    L.dsa_status_str.restype = ctypes.c_char_p
+    L.dsa_abi_version.restype = i32
+    for name in ("dsa_indexer_logits", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+# ----------------------------------------------------------------- helpers
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to the DSA library must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the DSA library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(status: int, where: str):
+    if status != DSA_OK:
+        raise DSAError(status, where)
+
+
+def queries(seq_id: torch.Tensor, pos: torch.Tensor, B: int, max_len: int) -> dsa_queries:
+    """Build the query descriptor (device int32 ``seq_id``/``pos``)."""
+    if seq_id.dtype != torch.int32 or pos.dtype != torch.int32:
+        raise ValueError("seq_id and pos must be int32")
+    q = dsa_queries(int(pos.shape[0]), int(B), _ptr(seq_id), _ptr(pos), int(max_len))
+    q._keep = (seq_id, pos)
+    return q
+
+
+def contiguous_layout(seq_capacity: int) -> dsa_kv_layout:
+    return dsa_kv_layout(0, 0, None, 0, 0, int(seq_capacity))
+
+
+def paged_layout(block_table: torch.Tensor, num_pages: int, page_size: int = 64) -> dsa_kv_layout:
+    if block_table.dtype != torch.int32:
+        raise ValueError("block_table must be int32")
+    lay = dsa_kv_layout(1, int(page_size), _ptr(block_table), int(block_table.shape[1]), int(num_pages), 0)
+    lay._keep = block_table
+    return lay
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A caller-owned device workspace of at least ``nbytes`` (256-byte aligned)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------- entry points
+
+def dsa_workspace_bytes(op: int, T: int, max_len: int, H: int, k: int) -> int:
+    return int(lib().dsa_workspace_bytes(op, T, max_len, H, k))
+
+
+def dsa_status_str(status: int) -> str:
+    return lib().dsa_status_str(status).decode()
+
+
+def dsa_abi_version() -> int:
+    return int(lib().dsa_abi_version())
+
+
+def dsa_indexer_logits(q: dsa_queries, layout: dsa_kv_layout, H_I: int, D_I: int, q_fp8, q_scale, w, k_fp8, k_scale,
+                       logits: torch.Tensor, stream=None):
+    st = lib().dsa_indexer_logits(ctypes.byref(q), ctypes.byref(layout), H_I, D_I, _ptr(q_fp8), _ptr(q_scale), _ptr(w),
+                                  _ptr(k_fp8), _ptr(k_scale), _ptr(logits), int(logits.shape[-1]), _stream(stream))
+    _check(st, "dsa_indexer_logits")
+
+
+def dsa_topk(logits: torch.Tensor, valid_len: torch.Tensor, max_len: int, k: int, idx: torch.Tensor,
+             ws: torch.Tensor, stream=None):
+    st = lib().dsa_topk(_ptr(logits), int(logits.shape[-1]), _ptr(valid_len), int(logits.shape[0]), int(max_len), int(k),
+                        _ptr(idx), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "dsa_topk")
+
+
+def dsa_sparse_mla_attn(q: dsa_queries, layout: dsa_kv_layout, H: int, q_bf16, kv_bf16, idx: torch.Tensor, k: int,
+                        sm_scale: float, out_bf16, lse=None, ws: Optional[torch.Tensor] = None, stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib().dsa_sparse_mla_attn(ctypes.byref(q), ctypes.byref(layout), H, _ptr(q_bf16), _ptr(kv_bf16), _ptr(idx),
+                                   int(k), float(sm_scale), _ptr(out_bf16), _ptr(lse), _ptr(ws), nbytes,
+                                   _stream(stream))
+    _check(st, "dsa_sparse_mla_attn")
+
+
+def dsa_forward(q: dsa_queries, layout: dsa_kv_layout, H_I: int, D_I: int, iq_fp8, iq_scale, iw, ik_fp8, ik_scale,
+                H: int, q_bf16, kv_bf16, k: int, sm_scale: float, out_bf16, lse=None, idx_out=None,
+                ws: Optional[torch.Tensor] = None, stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib().dsa_forward(ctypes.byref(q), ctypes.byref(layout), H_I, D_I, _ptr(iq_fp8), _ptr(iq_scale), _ptr(iw),
+                           _ptr(ik_fp8), _ptr(ik_scale), H, _ptr(q_bf16), _ptr(kv_bf16), int(k), float(sm_scale),
+                           _ptr(out_bf16), _ptr(lse), _ptr(idx_out), _ptr(ws), nbytes, _stream(stream))
+    _check(st, "dsa_forward")

@@ -1,0 +1,187 @@
+// C ABI of the DSA path: host-side validation, workspace carving, dispatch.
+// Validation runs before any HIP call, so every error path can be exercised
+// without a GPU.  Nothing here allocates memory.
+#include "dsa.h"
+#include "launch.h"
+
+using namespace dsa;
+
+namespace {
+
+constexpr int kMaxK = 2048;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_queries(const dsa_queries* q) {
+  if (q == nullptr) return DSA_ERR_INVALID_ARG;
+  if (q->T < 0 || q->B < 1 || q->max_len < 0) return DSA_ERR_INVALID_ARG;
+  if (q->T > 0 && (q->seq_id == nullptr || q->pos == nullptr || q->max_len < 1)) return DSA_ERR_INVALID_ARG;
+  return DSA_OK;
+}
+
+int check_layout(const dsa_kv_layout* l, const dsa_queries* q, Layout* out) {
+  if (l == nullptr) return DSA_ERR_INVALID_ARG;
+  if (l->paged != 0 && l->paged != 1) return DSA_ERR_INVALID_ARG;
+  if (l->paged) {
+    if (l->block_table == nullptr || l->max_pages < 1 || l->num_pages < 1) return DSA_ERR_INVALID_ARG;
+    if (l->page_size != 64) return DSA_ERR_UNSUPPORTED;
+    if ((int64_t)l->max_pages * 64 < q->max_len) return DSA_ERR_INVALID_ARG;
+  } else {
+    if (l->seq_capacity < q->max_len || l->seq_capacity < 1) return DSA_ERR_INVALID_ARG;
+  }
+  out->block_table = l->block_table;
+  out->seq_capacity = l->seq_capacity;
+  out->max_pages = l->max_pages;
+  out->paged = l->paged;
+  return DSA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+size_t forward_ws(int32_t T, int32_t max_len, int32_t H, int32_t k, bool with_idx) {
+  const int64_t ld = ((int64_t)max_len + 3) & ~int64_t(3);
+  size_t s = align256((size_t)T * ld * 4);              // logits
+  if (with_idx) s += align256((size_t)T * k * 4);       // selection
+  s += topk_workspace_bytes(T, ld);
+  s += align256(attn_workspace_bytes(T, H, k));
+  return s;
+}
+
+int validate_indexer(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,
+                     const uint8_t* q_fp8, const float* q_scale, const float* w, const uint8_t* k_fp8,
+                     const float* k_scale, const float* logits, int64_t ld, Layout* lay) {
+  int st = check_queries(q);
+  if (st) return st;
+  if ((st = check_layout(layout, q, lay))) return st;
+  if (H_I < 1 || D_I < 1) return DSA_ERR_INVALID_ARG;
+  if (!indexer_supported(H_I, D_I)) return DSA_ERR_UNSUPPORTED;
+  if (q->T == 0) return DSA_OK;
+  if (!q_fp8 || !q_scale || !w || !k_fp8 || !k_scale || !logits) return DSA_ERR_INVALID_ARG;
+  if (!aligned(q_fp8, 16) || !aligned(k_fp8, 16) || !aligned(logits, 16)) return DSA_ERR_INVALID_ARG;
+  if (ld < q->max_len || (ld & 3)) return DSA_ERR_INVALID_ARG;
+  return DSA_OK;
+}
+
+int validate_attn(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H, const void* q_bf16,
+                  const void* kv_bf16, const int32_t* idx, int32_t k, float sm_scale, const void* out, Layout* lay) {
+  int st = check_queries(q);
+  if (st) return st;
+  if ((st = check_layout(layout, q, lay))) return st;
+  if (H < 1 || k < 1) return DSA_ERR_INVALID_ARG;
+  if (!(sm_scale > 0.f) || sm_scale != sm_scale) return DSA_ERR_INVALID_ARG;
+  if (k > kMaxK || !attn_supported(H)) return DSA_ERR_UNSUPPORTED;
+  if (q->T == 0) return DSA_OK;
+  if (!q_bf16 || !kv_bf16 || !idx || !out) return DSA_ERR_INVALID_ARG;
+  if (!aligned(q_bf16, 16) || !aligned(kv_bf16, 16) || !aligned(out, 16)) return DSA_ERR_INVALID_ARG;
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char* dsa_status_str(int32_t status) {
+  switch (status) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_INVALID_ARG: return "invalid argument";
+    case DSA_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case DSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case DSA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t dsa_workspace_bytes(int32_t op, int32_t T, int32_t max_len, int32_t H, int32_t k) {
+  if (T < 0 || max_len < 0 || H < 0 || k < 0) return 0;
+  const int64_t ld = ((int64_t)max_len + 3) & ~int64_t(3);
+  switch (op) {
+    case DSA_OP_TOPK: return topk_workspace_bytes(T, ld);
+    case DSA_OP_ATTN: return (H > 0 && k > 0) ? attn_workspace_bytes(T, H, k) : 0;
+    case DSA_OP_FORWARD: return (H > 0 && k > 0) ? forward_ws(T, max_len, H, k, true) : 0;
+    default: return 0;
+  }
+}
+
+int dsa_indexer_logits(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,
+                       const uint8_t* q_fp8, const float* q_scale, const float* w, const uint8_t* k_fp8,
+                       const float* k_scale, float* logits, int64_t ld_logits, hipStream_t stream) {
+  Layout lay;
+  int st = validate_indexer(q, layout, H_I, D_I, q_fp8, q_scale, w, k_fp8, k_scale, logits, ld_logits, &lay);
+  if (st || q->T == 0) return st;
+  return hip_status(launch_indexer(q->T, q->max_len, H_I, D_I, q_fp8, q_scale, w, k_fp8, k_scale, q->seq_id, q->pos,
+                                   lay, logits, ld_logits, stream));
+}
+
+int dsa_topk(const float* logits, int64_t ld_logits, const int32_t* valid_len, int32_t T, int32_t max_len,
+             int32_t k, int32_t* idx, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (T < 0 || max_len < 0 || k < 1) return DSA_ERR_INVALID_ARG;
+  if (k > kMaxK) return DSA_ERR_UNSUPPORTED;
+  if (T == 0) return DSA_OK;
+  if (!logits || !valid_len || !idx) return DSA_ERR_INVALID_ARG;
+  if (ld_logits < max_len || (ld_logits & 3) || !aligned(logits, 16)) return DSA_ERR_INVALID_ARG;
+  const size_t need = topk_workspace_bytes(T, ld_logits);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)) return DSA_ERR_WORKSPACE;
+  return hip_status(launch_topk(logits, ld_logits, valid_len, 0, T, k, idx, workspace, stream));
+}
+
+int dsa_sparse_mla_attn(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H, const void* q_bf16,
+                        const void* kv_bf16, const int32_t* idx, int32_t k, float sm_scale, void* out_bf16,
+                        float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Layout lay;
+  int st = validate_attn(q, layout, H, q_bf16, kv_bf16, idx, k, sm_scale, out_bf16, &lay);
+  if (st || q->T == 0) return st;
+  const size_t need = attn_workspace_bytes(q->T, H, k);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)))
+    return DSA_ERR_WORKSPACE;
+  return hip_status(launch_attn(q->T, H, static_cast<const uint16_t*>(q_bf16), static_cast<const uint16_t*>(kv_bf16),
+                                idx, q->seq_id, lay, k, sm_scale, static_cast<uint16_t*>(out_bf16), lse, workspace,
+                                stream));
+}
+
+int dsa_forward(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,
+                const uint8_t* iq_fp8, const float* iq_scale, const float* iw, const uint8_t* ik_fp8,
+                const float* ik_scale, int32_t H, const void* q_bf16, const void* kv_bf16, int32_t k,
+                float sm_scale, void* out_bf16, float* lse, int32_t* idx_out, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  Layout lay;
+  int st = check_queries(q);
+  if (st) return st;
+  if ((st = check_layout(layout, q, &lay))) return st;
+  if (H_I < 1 || D_I < 1 || H < 1 || k < 1) return DSA_ERR_INVALID_ARG;
+  if (!(sm_scale > 0.f)) return DSA_ERR_INVALID_ARG;
+  if (!indexer_supported(H_I, D_I) || !attn_supported(H) || k > kMaxK) return DSA_ERR_UNSUPPORTED;
+  if (q->T == 0) return DSA_OK;
+  if (!iq_fp8 || !iq_scale || !iw || !ik_fp8 || !ik_scale || !q_bf16 || !kv_bf16 || !out_bf16)
+    return DSA_ERR_INVALID_ARG;
+  if (!aligned(iq_fp8, 16) || !aligned(ik_fp8, 16) || !aligned(q_bf16, 16) || !aligned(kv_bf16, 16) ||
+      !aligned(out_bf16, 16))
+    return DSA_ERR_INVALID_ARG;
+  const int64_t ld = ((int64_t)q->max_len + 3) & ~int64_t(3);
+  const size_t need = forward_ws(q->T, q->max_len, H, k, idx_out == nullptr);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)) return DSA_ERR_WORKSPACE;
+
+  char* p = static_cast<char*>(workspace);
+  float* logits = reinterpret_cast<float*>(p);
+  p += align256((size_t)q->T * ld * 4);
+  int32_t* idx = idx_out;
+  if (idx == nullptr) {
+    idx = reinterpret_cast<int32_t*>(p);
+    p += align256((size_t)q->T * k * 4);
+  }
+  void* ws_topk = p;
+  p += topk_workspace_bytes(q->T, ld);
+  void* ws_attn = p;
+
+  hipError_t e = launch_indexer(q->T, q->max_len, H_I, D_I, iq_fp8, iq_scale, iw, ik_fp8, ik_scale, q->seq_id,
+                                q->pos, lay, logits, ld, stream);
+  if (e != hipSuccess) return DSA_ERR_HIP;
+  e = launch_topk(logits, ld, q->pos, 1, q->T, k, idx, ws_topk, stream);
+  if (e != hipSuccess) return DSA_ERR_HIP;
+  e = launch_attn(q->T, H, static_cast<const uint16_t*>(q_bf16), static_cast<const uint16_t*>(kv_bf16), idx, q->seq_id,
+                  lay, k, sm_scale, static_cast<uint16_t*>(out_bf16), lse, ws_attn, stream);
+  return hip_status(e);
+}
+
+}  // extern "C"

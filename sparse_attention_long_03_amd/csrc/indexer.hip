@@ -1,0 +1,174 @@
+// Lightning indexer logits on gfx950 FP8 matrix cores.
+//
+// "DeepSeek V3.2-Exp Cuts Prolonged-Context Costs With DeepSeek Sparse
+// Consideration (DSA)", part (1): per query token, a few small FP8 indexer
+// heads with a ReLU score every earlier token.  Computed here:
+//   I[t,s] = qs[t] * ks[s] * sum_j w[t,j] * ReLU(q8[t,j,:] . k8[s,:])
+//
+// Mapping.  One query token's heads form the M side of the MFMA (16 heads per
+// M tile), keys form N (16 keys per N tile) and the head dim is K, so one
+// v_mfma_f32_16x16x128_f8f6f4 computes 16 heads x 16 keys of dot products
+// (D_I = 128; D_I = 64 uses two 16x16x32 fp8 MFMAs).  In the 16x16 result a
+// lane holds one key (column) and four heads (rows), so the ReLU and the
+// per-head weights are applied in registers, and the sum over heads needs
+// only two cross-lane steps (lanes n, n+16, n+32, n+48).
+//
+// Each lane group g (lanes 16g..16g+15) feeds the same byte range of the head
+// dim for both operands; the contraction is a plain sum over the K index, so
+// any consistent assignment of bytes to K slots gives the same result.
+//
+// Decode is bound by HBM (one 128-byte key row feeds 64 heads x 128 MACs =
+// 128 flop/byte, far under the FP8 ridge), so the kernel streams keys with
+// wide loads and keeps many 8 KB wave tiles in flight.
+#include "launch.h"
+
+namespace dsa {
+
+constexpr int IDX_WAVES = 4;
+constexpr int IDX_ITERS = 4;                                    // 64-key groups per wave
+constexpr int IDX_KEYS_PER_WG = IDX_WAVES * IDX_ITERS * 64;     // 1024 keys per workgroup
+
+template <int H_I, int D_I>
+struct KeyFrag;
+
+// D_I = 128: 32 bytes per lane (one f8f6f4 MFMA)
+template <int H_I>
+struct KeyFrag<H_I, 128> {
+  v8i v;
+  __device__ __forceinline__ void load(const uint8_t* row_base, int g) {
+    const v4i* p = reinterpret_cast<const v4i*>(row_base + 32 * g);
+    v4i a = p[0], b = p[1];
+    v = v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+  __device__ __forceinline__ void zero() { v = v8i{0, 0, 0, 0, 0, 0, 0, 0}; }
+  __device__ __forceinline__ static v4f mma(const KeyFrag& a, const KeyFrag& b) {
+    v4f c = {0.f, 0.f, 0.f, 0.f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a.v, b.v, c, 0, 0, 0, 0, 0, 0);
+  }
+};
+
+// D_I = 64: 16 bytes per lane (two 16x16x32 fp8 MFMAs)
+template <int H_I>
+struct KeyFrag<H_I, 64> {
+  v4i v;
+  __device__ __forceinline__ void load(const uint8_t* row_base, int g) {
+    v = *reinterpret_cast<const v4i*>(row_base + 16 * g);
+  }
+  __device__ __forceinline__ void zero() { v = v4i{0, 0, 0, 0}; }
+  __device__ __forceinline__ static v4f mma(const KeyFrag& a, const KeyFrag& b) {
+    v4f c = {0.f, 0.f, 0.f, 0.f};
+    long a0 = (long)(((unsigned long)(u32)a.v[1] << 32) | (u32)a.v[0]);
+    long a1 = (long)(((unsigned long)(u32)a.v[3] << 32) | (u32)a.v[2]);
+    long b0 = (long)(((unsigned long)(u32)b.v[1] << 32) | (u32)b.v[0]);
+    long b1 = (long)(((unsigned long)(u32)b.v[3] << 32) | (u32)b.v[2]);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a0, b0, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a1, b1, c, 0, 0, 0);
+    return c;
+  }
+};
+
+template <int H_I, int D_I>
+__global__ __launch_bounds__(IDX_WAVES * 64) void indexer_kernel(const uint8_t* __restrict__ q8,
+                                                                 const float* __restrict__ qs,
+                                                                 const float* __restrict__ w,
+                                                                 const uint8_t* __restrict__ k8,
+                                                                 const float* __restrict__ ks,
+                                                                 const int32_t* __restrict__ seq_id,
+                                                                 const int32_t* __restrict__ pos, Layout lay,
+                                                                 float* __restrict__ logits, int64_t ld) {
+  constexpr int MT = (H_I + 15) / 16;  // M tiles of 16 heads
+  using Frag = KeyFrag<H_I, D_I>;
+
+  const int t = blockIdx.y;
+  const int p = pos[t];
+  const int wg_base = blockIdx.x * IDX_KEYS_PER_WG;
+  if (wg_base > p) return;
+  const int b = seq_id[t];
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+
+  // query operand: row = head mt*16 + n
+  Frag qa[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int h = mt * 16 + n;
+    if (h < H_I)
+      qa[mt].load(q8 + ((int64_t)t * H_I + h) * D_I, g);
+    else
+      qa[mt].zero();
+  }
+  // weights of the heads whose results this lane holds: mt*16 + 4g + i
+  float wv[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = mt * 16 + 4 * g + i;
+      wv[mt][i] = (h < H_I) ? w[(int64_t)t * H_I + h] : 0.f;
+    }
+  const float qscale = qs[t];
+  float* __restrict__ out_row = logits + (int64_t)t * ld;
+
+#pragma unroll
+  for (int it = 0; it < IDX_ITERS; ++it) {
+    const int base = wg_base + (it * IDX_WAVES + wid) * 64;  // 64-aligned: one page when paged
+    if (base > p) break;
+    const int64_t row0 = token_row(lay, b, base);
+    // keys of the four N tiles; positions past p are clamped to p (not stored)
+    Frag kb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s = min(base + 16 * j + n, p);
+      kb[j].load(k8 + (row0 + (s - base)) * D_I, g);
+    }
+    const int s_me = base + lane;
+    const float ksv = ks[row0 + (min(s_me, p) - base)];
+    float res = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float part = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const v4f acc = Frag::mma(qa[mt], kb[j]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part += wv[mt][i] * fmaxf(acc[i], 0.f);
+      }
+      part += __shfl_xor(part, 16, 64);
+      part += __shfl_xor(part, 32, 64);
+      if (g == j) res = part;  // lane 16j+n keeps key base+16j+n = base+lane
+    }
+    if (s_me <= p) out_row[s_me] = (res * qscale) * ksv;
+  }
+}
+
+bool indexer_supported(int H_I, int D_I) {
+  return (H_I == 64 || H_I == 4) && (D_I == 128 || D_I == 64);
+}
+
+template <int H_I, int D_I>
+static hipError_t launch_t(int T, int max_len, const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8,
+                           const float* ks, const int32_t* seq_id, const int32_t* pos, const Layout& lay,
+                           float* logits, int64_t ld, hipStream_t stream) {
+  dim3 grid((max_len + IDX_KEYS_PER_WG - 1) / IDX_KEYS_PER_WG, T);
+  hipLaunchKernelGGL((indexer_kernel<H_I, D_I>), grid, dim3(IDX_WAVES * 64), 0, stream, q8, qs, w, k8, ks, seq_id,
+                     pos, lay, logits, ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer(int T, int max_len, int H_I, int D_I, const uint8_t* q8, const float* qs, const float* w,
+                          const uint8_t* k8, const float* ks, const int32_t* seq_id, const int32_t* pos,
+                          const Layout& lay, float* logits, int64_t ld, hipStream_t stream) {
+  if (T == 0 || max_len == 0) return hipSuccess;
+#define DSA_IDX_CASE(HH, DD) \
+  if (H_I == HH && D_I == DD) return launch_t<HH, DD>(T, max_len, q8, qs, w, k8, ks, seq_id, pos, lay, logits, ld, stream);
+  DSA_IDX_CASE(64, 128)
+  DSA_IDX_CASE(64, 64)
+  DSA_IDX_CASE(4, 128)
+  DSA_IDX_CASE(4, 64)
+#undef DSA_IDX_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dsa

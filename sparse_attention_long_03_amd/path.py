@@ -1,0 +1,77 @@
+"""Convenience wrapper: run the DSA path on a set of GPU-resident inputs.
+
+Builds the C descriptors once, owns the outputs and the workspace, and calls
+the C entry points through :mod:`.binding`.  No arithmetic happens here.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import binding as B
+from .inputs import DSAInputs
+
+
+def round_up(x: int, m: int) -> int:
+    return (x + m - 1) // m * m
+
+
+class DSAPath:
+    def __init__(self, x: DSAInputs):
+        cfg = x.cfg
+        self.x = x
+        self.cfg = cfg
+        self.T = x.T
+        self.q = B.queries(x.seq_id, x.pos, cfg.B, x.max_len)
+        if x.block_table is not None:
+            self.layout = B.paged_layout(x.block_table, x.kv.shape[0], cfg.page_size)
+        else:
+            self.layout = B.contiguous_layout(x.kv.shape[1])
+        self.ld = round_up(max(x.max_len, 1), 4)
+        self.valid_len = (x.pos + 1).to(torch.int32)
+        dev = x.q.device
+        self.dev = dev
+        self.out = torch.empty((self.T, cfg.H, cfg.d_v), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((self.T, cfg.H), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((self.T, cfg.k), dtype=torch.int32, device=dev)
+        self._ws = {}
+
+    def ws(self, op: int) -> torch.Tensor:
+        if op not in self._ws:
+            n = B.dsa_workspace_bytes(op, self.T, self.x.max_len, self.cfg.H, self.cfg.k)
+            self._ws[op] = B.workspace(n, self.dev)
+        return self._ws[op]
+
+    def new_logits(self) -> torch.Tensor:
+        return torch.empty((self.T, self.ld), dtype=torch.float32, device=self.dev)
+
+    def indexer(self, logits: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        x, c = self.x, self.cfg
+        if logits is None:
+            logits = self.new_logits()
+        B.dsa_indexer_logits(self.q, self.layout, c.H_I, c.D_I, x.iq8, x.iqs, x.iw, x.ik8, x.iks, logits, stream)
+        return logits
+
+    def topk(self, logits: torch.Tensor, idx: Optional[torch.Tensor] = None, valid_len=None, k=None,
+             stream=None) -> torch.Tensor:
+        k = self.cfg.k if k is None else k
+        if idx is None:
+            idx = torch.empty((logits.shape[0], k), dtype=torch.int32, device=self.dev)
+        vl = self.valid_len if valid_len is None else valid_len
+        ws = B.workspace(B.dsa_workspace_bytes(B.DSA_OP_TOPK, logits.shape[0], logits.shape[1], 0, k), self.dev)
+        B.dsa_topk(logits, vl, logits.shape[1], k, idx, ws, stream)
+        return idx
+
+    def attn(self, idx: torch.Tensor, stream=None):
+        x, c = self.x, self.cfg
+        B.dsa_sparse_mla_attn(self.q, self.layout, c.H, x.q, x.kv, idx, idx.shape[1], c.scale, self.out, self.lse,
+                              self.ws(B.DSA_OP_ATTN), stream)
+        return self.out, self.lse
+
+    def forward(self, stream=None):
+        x, c = self.x, self.cfg
+        B.dsa_forward(self.q, self.layout, c.H_I, c.D_I, x.iq8, x.iqs, x.iw, x.ik8, x.iks, c.H, x.q, x.kv, c.k,
+                      c.scale, self.out, self.lse, self.idx, self.ws(B.DSA_OP_FORWARD), stream)
+        return self.out, self.lse, self.idx

@@ -1,0 +1,128 @@
+"""The C-ABI library loads, exports what include/dsa.h declares, and rejects
+bad arguments before touching a device (these run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_long_03_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+FAKE = ctypes.c_void_p(1 << 20)  # non-null, 256-byte aligned; never dereferenced on a failing path
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(dsa_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libdsa.so not built")
+    return B.lib()
+
+
+def test_header_declares_the_entry_points():
+    d = _declared()
+    for name in B.EXPORTS:
+        assert name in d, name
+    assert set(d) == set(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert B.dsa_abi_version() == 1
+    for code in (0, -1, -2, -3, -4):
+        assert B.dsa_status_str(code) != "unknown status"
+    assert B.dsa_status_str(-99) == "unknown status"
+
+
+def _q(T=4, Bn=1, max_len=100, seq=FAKE, pos=FAKE):
+    return B.dsa_queries(T, Bn, seq, pos, max_len)
+
+
+def _lay(cap=100):
+    return B.contiguous_layout(cap)
+
+
+def test_topk_validation(lib):
+    f = lib.dsa_topk
+    assert f(FAKE, 100, FAKE, 4, 100, 0, FAKE, FAKE, 1 << 30, None) == B.DSA_ERR_INVALID_ARG   # k = 0
+    assert f(FAKE, 100, FAKE, 4, 100, 4096, FAKE, FAKE, 1 << 30, None) == B.DSA_ERR_UNSUPPORTED  # k > 2048
+    assert f(FAKE, 100, FAKE, 4, 100, 64, FAKE, None, 0, None) == B.DSA_ERR_WORKSPACE
+    assert f(FAKE, 100, FAKE, 4, 100, 64, FAKE, FAKE, 16, None) == B.DSA_ERR_WORKSPACE
+    assert f(FAKE, 99, FAKE, 4, 100, 64, FAKE, FAKE, 1 << 30, None) == B.DSA_ERR_INVALID_ARG   # ld < max_len
+    assert f(FAKE, 102, FAKE, 4, 100, 64, FAKE, FAKE, 1 << 30, None) == B.DSA_ERR_INVALID_ARG  # ld % 4
+    assert f(None, 100, FAKE, 4, 100, 64, FAKE, FAKE, 1 << 30, None) == B.DSA_ERR_INVALID_ARG
+    assert f(None, 100, None, 0, 100, 64, None, None, 0, None) == B.DSA_OK                    # T = 0: nothing to do
+
+
+def test_indexer_validation(lib):
+    f = lib.dsa_indexer_logits
+    ok = dict(H_I=64, D_I=128)
+
+    def call(q=None, lay=None, H_I=64, D_I=128, ptrs=(FAKE,) * 5, logits=FAKE, ld=100):
+        q = q or _q()
+        lay = lay or _lay()
+        return f(ctypes.byref(q), ctypes.byref(lay), H_I, D_I, *ptrs, logits, ld, None)
+
+    del ok
+    assert call(H_I=8) == B.DSA_ERR_UNSUPPORTED
+    assert call(D_I=96) == B.DSA_ERR_UNSUPPORTED
+    assert call(H_I=0) == B.DSA_ERR_INVALID_ARG
+    assert call(ld=98) == B.DSA_ERR_INVALID_ARG
+    assert call(logits=None) == B.DSA_ERR_INVALID_ARG
+    assert call(logits=ctypes.c_void_p((1 << 20) + 4)) == B.DSA_ERR_INVALID_ARG            # misaligned
+    assert call(lay=_lay(cap=50)) == B.DSA_ERR_INVALID_ARG                                   # capacity < max_len
+    assert call(q=_q(Bn=0)) == B.DSA_ERR_INVALID_ARG
+    assert call(q=_q(seq=None)) == B.DSA_ERR_INVALID_ARG
+    paged = B.dsa_kv_layout(1, 32, FAKE, 4, 10, 0)
+    assert call(lay=paged) == B.DSA_ERR_UNSUPPORTED                                          # page size 32
+    paged = B.dsa_kv_layout(1, 64, FAKE, 1, 10, 0)
+    assert call(lay=paged) == B.DSA_ERR_INVALID_ARG                                          # 1 page < 100 tokens
+    paged = B.dsa_kv_layout(1, 64, None, 4, 10, 0)
+    assert call(lay=paged) == B.DSA_ERR_INVALID_ARG
+    assert call(q=_q(T=0, seq=None, pos=None)) == B.DSA_OK
+
+
+def test_attention_and_forward_validation(lib):
+    q, lay = _q(), _lay()
+    a = lib.dsa_sparse_mla_attn
+    assert a(ctypes.byref(q), ctypes.byref(lay), 48, FAKE, FAKE, FAKE, 64, 0.1, FAKE, None, FAKE, 1 << 30, None) == B.DSA_ERR_UNSUPPORTED
+    assert a(ctypes.byref(q), ctypes.byref(lay), 128, FAKE, FAKE, FAKE, 4096, 0.1, FAKE, None, FAKE, 1 << 30, None) == B.DSA_ERR_UNSUPPORTED
+    assert a(ctypes.byref(q), ctypes.byref(lay), 128, FAKE, FAKE, FAKE, 64, 0.0, FAKE, None, FAKE, 1 << 30, None) == B.DSA_ERR_INVALID_ARG
+    assert a(ctypes.byref(q), ctypes.byref(lay), 128, FAKE, FAKE, FAKE, 64, float("nan"), FAKE, None, FAKE, 1 << 30, None) == B.DSA_ERR_INVALID_ARG
+    assert a(ctypes.byref(q), ctypes.byref(lay), 128, None, FAKE, FAKE, 64, 0.1, FAKE, None, FAKE, 1 << 30, None) == B.DSA_ERR_INVALID_ARG
+    # a split-K shape needs a workspace
+    qq = _q(T=2)
+    need = B.dsa_workspace_bytes(B.DSA_OP_ATTN, 2, 100, 128, 2048)
+    assert need > 0
+    assert a(ctypes.byref(qq), ctypes.byref(lay), 128, FAKE, FAKE, FAKE, 2048, 0.1, FAKE, None, None, 0, None) == B.DSA_ERR_WORKSPACE
+    assert a(ctypes.byref(qq), ctypes.byref(lay), 128, FAKE, FAKE, FAKE, 2048, 0.1, FAKE, None, FAKE, need - 1, None) == B.DSA_ERR_WORKSPACE
+    fw = lib.dsa_forward
+    args = [64, 128, FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 2048, 0.1, FAKE, None, None]
+    need_f = B.dsa_workspace_bytes(B.DSA_OP_FORWARD, 4, 100, 128, 2048)
+    assert fw(ctypes.byref(q), ctypes.byref(lay), *args, FAKE, need_f - 1, None) == B.DSA_ERR_WORKSPACE
+    assert fw(ctypes.byref(q), ctypes.byref(lay), *args, None, 0, None) == B.DSA_ERR_WORKSPACE
+    bad = list(args)
+    bad[0] = 5
+    assert fw(ctypes.byref(q), ctypes.byref(lay), *bad, FAKE, need_f, None) == B.DSA_ERR_UNSUPPORTED
+
+
+def test_workspace_sizes_are_monotone(lib):
+    a = B.dsa_workspace_bytes(B.DSA_OP_FORWARD, 16, 131072, 128, 2048)
+    b = B.dsa_workspace_bytes(B.DSA_OP_FORWARD, 16, 65536, 128, 2048)
+    assert a > b > 0
+    assert B.dsa_workspace_bytes(B.DSA_OP_TOPK, 16, 131072, 0, 2048) >= 2 * 16 * 131072 * 4
+    assert B.dsa_workspace_bytes(99, 16, 131072, 128, 2048) == 0
+    assert B.dsa_workspace_bytes(B.DSA_OP_ATTN, -1, 10, 128, 2048) == 0

@@ -1,0 +1,288 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_attention_long_03_amd import binding as B
+from sparse_attention_long_03_amd import inputs as I
+from sparse_attention_long_03_amd.path import DSAPath
+
+from parity_util import (bf16_to_np, check_attn, check_logits, check_selection_valid, host_inputs,
+                         indexer_magnitude, np_)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+SMALL = {
+    # tiny step as specified: 4x64 indexer, 16 heads, k=256, 16 trailing queries
+    "tiny": I.CONFIGS["tiny"],
+    # 64x128 indexer, 128 heads, ragged tail (5000 = 4*1024 + 904), 2 queries per sequence
+    "decode_ragged": I.scaled(I.CONFIGS["decode32k"], B=3, L=5000, queries_per_seq=2),
+    # 64x64 and 4x128 indexer variants
+    "idx64x64": I.scaled(I.CONFIGS["decode32k"], B=2, L=3000, D_I=64, H=16, k=256),
+    "idx4x128": I.scaled(I.CONFIGS["decode32k"], B=2, L=3000, H_I=4, H=32, k=512),
+    # paged, lengths in [100, 3000], shuffled pages, 1-2 queries per sequence
+    "paged_small": I.scaled(I.CONFIGS["ragged_paged"], B=5, L=3000, min_len=100, H=64, k=1024),
+}
+
+
+def _inputs(name):
+    return I.make_inputs(SMALL[name], DEV)
+
+
+def _oracle_logits(h):
+    return O.indexer_logits(h["iq8"], h["iqs"], h["iw"], h["ik8"], h["iks"], h["seq_id"], h["pos"], h["bt"])
+
+
+def _magnitudes(h):
+    """Per-query term magnitudes M (tolerance floor of the indexer)."""
+    mags = []
+    for t in range(len(h["pos"])):
+        n = int(h["pos"][t]) + 1
+        b = int(h["seq_id"][t])
+        k8 = O.logical_rows(h["ik8"], b, n, h["bt"])
+        ks = O.logical_rows(h["iks"], b, n, h["bt"])
+        mags.append(indexer_magnitude(h["iq8"][t], h["iqs"][t], h["iw"][t], k8, ks))
+    return mags
+
+
+# ----------------------------------------------------------------- indexer
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_indexer_matches_oracle(name):
+    x = _inputs(name)
+    p = DSAPath(x)
+    lg = np_(p.indexer())
+    torch.cuda.synchronize()
+    h = host_inputs(x)
+    ref = _oracle_logits(h)
+    mags = _magnitudes(h)
+    for t in range(x.T):
+        n = int(h["pos"][t]) + 1
+        check_logits(lg[t, :n], ref[t, :n], mags[t], f"{name} row {t}")
+
+
+# ----------------------------------------------------------------- top-k
+
+def _topk_case(logits_np, valid, k):
+    T, n = logits_np.shape
+    ld = (n + 3) // 4 * 4
+    lg = torch.zeros((T, ld), dtype=torch.float32)
+    lg[:, :n] = torch.from_numpy(logits_np)
+    lg = lg.to(DEV)
+    vl = torch.tensor(valid, dtype=torch.int32, device=DEV)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    ws = B.workspace(B.dsa_workspace_bytes(B.DSA_OP_TOPK, T, ld, 0, k))
+    B.dsa_topk(lg, vl, ld, k, idx, ws)
+    got = np_(idx)
+    for t in range(T):
+        ref = O.topk_select(logits_np[t], int(valid[t]), k)
+        assert np.array_equal(np.sort(got[t]), np.sort(ref)), f"row {t} (n={valid[t]}, k={k})"
+    return got
+
+
+def test_topk_tie_heavy_256_levels():
+    # ragged-batch selection test: logits on 256 levels, many ties at the k-th value
+    v = I.tie_heavy_logits(6, 40000, seed=11).numpy()
+    _topk_case(v, [40000, 2049, 2048, 2047, 31111, 1], 2048)
+
+
+def test_topk_long_rows_128k_tie_heavy():
+    v = I.tie_heavy_logits(3, 131072, seed=12).numpy()
+    _topk_case(v, [131072, 131071, 65537], 2048)
+
+
+def test_topk_signed_zero_and_negatives():
+    g = np.random.default_rng(3)
+    v = g.choice(np.array([0.0, -0.0, -1.5, 2.0, -3.0, 1e-30], dtype=np.float32), size=(3, 9000))
+    _topk_case(v, [9000, 5000, 3000], 2048)
+    _topk_case(v, [9000, 8999, 100], 7)
+
+
+def test_topk_oracle_logits_and_small_k():
+    x = _inputs("decode_ragged")
+    h = host_inputs(x)
+    ref = _oracle_logits(h).astype(np.float32)
+    n = ref.shape[1]
+    valid = [int(p) + 1 for p in h["pos"]]
+    ref = np.nan_to_num(ref, nan=0.0)
+    for k in (1, 33, 2048):
+        _topk_case(ref[:, :n], valid, k)
+
+
+def test_topk_degenerate_lengths():
+    v = I.tie_heavy_logits(4, 3000, seed=13).numpy()
+    got = _topk_case(v, [0, 1, 2048, 3000], 2048)
+    assert np.all(got[0] == -1)
+    assert got[1][0] == 0 and np.all(got[1][1:] == -1)
+
+
+# ----------------------------------------------------------------- attention
+
+def _oracle_idx(h, k):
+    ref = _oracle_logits(h)
+    T = len(h["pos"])
+    idx = np.full((T, k), -1, dtype=np.int32)
+    for t in range(T):
+        n = int(h["pos"][t]) + 1
+        idx[t] = O.topk_select(ref[t, :n].astype(np.float32), n, k)
+    return idx
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode_ragged", "paged_small", "idx4x128"])
+def test_attention_matches_oracle_on_oracle_indices(name):
+    x = _inputs(name)
+    h = host_inputs(x)
+    idx = _oracle_idx(h, x.cfg.k)
+    p = DSAPath(x)
+    out, lse = p.attn(torch.from_numpy(idx).to(DEV))
+    ro, rl = O.sparse_mla_attention(h["q"], h["kv"], idx, h["seq_id"], x.cfg.scale, 512, h["bt"])
+    check_attn(bf16_to_np(out), ro, name)
+    np.testing.assert_allclose(np_(lse), rl, rtol=1e-4, atol=1e-4)
+
+
+def test_attention_padding_and_empty_rows():
+    x = I.make_inputs(I.scaled(I.CONFIGS["decode32k"], B=4, L=700, queries_per_seq=1), DEV)
+    h = host_inputs(x)
+    k = 2048
+    g = np.random.default_rng(5)
+    idx = np.full((x.T, k), -1, dtype=np.int32)
+    idx[0, :700] = g.permutation(700)                      # n < k: padded
+    idx[1, g.permutation(k)[:300]] = g.permutation(700)[:300]  # pads interleaved
+    idx[2, :1] = 699                                        # single row
+    # row 3 stays all padding: empty selection
+    p = DSAPath(x)
+    out, lse = p.attn(torch.from_numpy(idx).to(DEV))
+    ro, rl = O.sparse_mla_attention(h["q"], h["kv"], idx, h["seq_id"], x.cfg.scale)
+    check_attn(bf16_to_np(out)[:3], ro[:3], "padded")
+    assert np.all(bf16_to_np(out)[3] == 0) and np.all(np.isneginf(np_(lse)[3]))
+    np.testing.assert_allclose(np_(lse)[:3], rl[:3], rtol=1e-4, atol=1e-4)
+
+
+# ----------------------------------------------------------------- whole path
+
+@pytest.mark.parametrize("name", ["tiny", "decode_ragged", "paged_small"])
+def test_forward_end_to_end(name):
+    x = _inputs(name)
+    h = host_inputs(x)
+    p = DSAPath(x)
+    out, lse, idx = p.forward()
+    out, idx = bf16_to_np(out), np_(idx)
+    ref = _oracle_logits(h)
+    mags = _magnitudes(h)
+    for t in range(x.T):
+        n = int(h["pos"][t]) + 1
+        check_selection_valid(idx[t], ref[t], n, x.cfg.k, mags[t])
+    ro, _ = O.sparse_mla_attention(h["q"], h["kv"], idx, h["seq_id"], x.cfg.scale, 512, h["bt"])
+    check_attn(out, ro, name)
+
+
+def test_forward_is_deterministic():
+    x = _inputs("decode_ragged")
+    p = DSAPath(x)
+    o1, l1, i1 = [t.clone() for t in p.forward()]
+    o2, l2, i2 = [t.clone() for t in p.forward()]
+    assert torch.equal(i1, i2) and torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_paged_equals_contiguous_bitwise():
+    cfg = I.scaled(I.CONFIGS["decode32k"], B=3, L=2500, queries_per_seq=2, k=1024)
+    x = I.make_inputs(cfg, DEV)
+    # scatter the same logical rows into shuffled 64-token pages
+    ps = 64
+    npg = -(-cfg.L // ps)
+    perm = torch.randperm(cfg.B * npg, generator=torch.Generator().manual_seed(4)).to(torch.int32)
+    bt = perm.view(cfg.B, npg)
+    P = cfg.B * npg
+    pad = npg * ps - cfg.L
+
+    def to_pages(t):
+        tp = torch.nn.functional.pad(t, (0, 0) * (t.dim() - 2) + (0, pad)) if t.dim() > 2 else \
+            torch.nn.functional.pad(t, (0, pad))
+        flat = tp.reshape(cfg.B * npg, ps, *t.shape[2:])
+        out = torch.empty_like(flat)
+        out[bt.reshape(-1).long().to(DEV)] = flat
+        return out
+
+    xp = I.DSAInputs(cfg=I.scaled(cfg, paged=True), seq_id=x.seq_id, pos=x.pos, iq8=x.iq8, iqs=x.iqs, iw=x.iw, q=x.q,
+                     ik8=to_pages(x.ik8), iks=to_pages(x.iks), kv=to_pages(x.kv), block_table=bt.to(DEV),
+                     seq_lens=x.seq_lens, max_len=x.max_len)
+    assert xp.kv.shape[0] == P
+    pc, pp = DSAPath(x), DSAPath(xp)
+    lc, lp = pc.indexer(), pp.indexer()
+    for t in range(x.T):
+        n = int(x.pos[t]) + 1
+        assert torch.equal(lc[t, :n], lp[t, :n])
+    oc, _, ic = pc.forward()
+    op, _, ip = pp.forward()
+    assert torch.equal(ic, ip)
+    assert torch.equal(oc.view(torch.int16), op.view(torch.int16))
+
+
+# ----------------------------------------------------------------- full sizes (sampled)
+
+def _gather_rows_host(x, b, positions):
+    """Logical rows of sequence b at the given positions -> host numpy (bits / codes)."""
+    pos_t = torch.as_tensor(positions, dtype=torch.int64, device=DEV)
+    if x.block_table is None:
+        kv = x.kv[b][pos_t]
+    else:
+        pages = x.block_table[b].long()[pos_t // 64]
+        kv = x.kv[pages, pos_t % 64]
+    return I.bf16_bits(kv)
+
+
+def _key_rows_host(x, b, n):
+    if x.block_table is None:
+        return np_(x.ik8[b, :n]), np_(x.iks[b, :n]).astype(np.float64)
+    npg = -(-n // 64)
+    pages = x.block_table[b, :npg].long()
+    return (np_(x.ik8[pages].reshape(-1, x.ik8.shape[-1])[:n]), np_(x.iks[pages].reshape(-1)[:n]).astype(np.float64))
+
+
+def _sampled_full_size(cfg_name, sample_t):
+    x = I.make_inputs(I.CONFIGS[cfg_name], DEV)
+    p = DSAPath(x)
+    logits = p.indexer()
+    out, lse, idx = p.forward()
+    torch.cuda.synchronize()
+    for t in sample_t:
+        b = int(x.seq_id[t])
+        n = int(x.pos[t]) + 1
+        k8, ks = _key_rows_host(x, b, n)
+        qt, qst, wt = np_(x.iq8[t]), float(x.iqs[t]), np_(x.iw[t]).astype(np.float64)
+        ref = O.indexer_logits_row(qt, qst, wt, k8, ks)
+        mag = indexer_magnitude(qt, qst, wt, k8, ks)
+        check_logits(np_(logits[t, :n]), ref, mag, f"{cfg_name} row {t}")
+        sel = np_(idx[t])
+        check_selection_valid(sel, ref, n, x.cfg.k, mag)
+        got = sel[sel >= 0]
+        rows = _gather_rows_host(x, b, got)
+        ro, rl = O.sparse_mla_attention(I.bf16_bits(x.q[t:t + 1]), rows[None], np.arange(len(got))[None],
+                                        np.zeros(1, int), x.cfg.scale)
+        check_attn(bf16_to_np(out[t:t + 1]), ro, f"{cfg_name} query {t}")
+        np.testing.assert_allclose(np_(lse[t]), rl[0], rtol=1e-4, atol=1e-4)
+    return x, idx
+
+
+def test_full_size_decode128k_sampled():
+    x, idx = _sampled_full_size("decode128k", [0, 9, 15])
+    # every selected position is a planted far key
+    for t in range(x.T):
+        b = int(x.seq_id[t])
+        planted = set(x.planted[b].tolist())
+        sel = np_(idx[t])
+        assert all(int(s) in planted for s in sel), f"query {t} selected an unplanted key"
+        assert sel.max() < x.cfg.L // 2
+
+
+def test_full_size_decode32k_sampled():
+    _sampled_full_size("decode32k", [0, 31, 63])
+
+
+def test_full_size_ragged_paged_sampled():
+    T = int(I._workload(I.CONFIGS["ragged_paged"])[2].shape[0])
+    _sampled_full_size("ragged_paged", [0, T // 2, T - 1])
