@@ -55,16 +55,18 @@ def algorithmic_bytes(x):
 
 
 class Flusher:
-    """Evicts L2 and the 256 MB MALL between timed launches by writing a
-    512 MB buffer, so no launch reads data a previous launch left in cache
-    (a serving loop interleaves many layers' caches between two uses)."""
+    """Evicts L2 and the 256 MB MALL between timed launches by reading a
+    1 GB buffer (4x the MALL), so no launch reads data that a previous launch
+    left in cache -- a serving loop interleaves many layers' caches between
+    two uses of one layer's.  A read is used, not a fill: a fill would leave
+    the MALL full of dirty lines whose write-back the next launch would pay."""
 
-    def __init__(self, nbytes=512 << 20):
+    def __init__(self, nbytes=1 << 30):
         import torch
-        self.buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        self.buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
 
     def __call__(self):
-        self.buf.zero_()
+        self.buf.sum()
 
 
 def timed_launches(fn, n, stream, flush=None):

@@ -15,6 +15,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int check_queries(const dsa_queries* q) {
   if (q == nullptr) return DSA_ERR_INVALID_ARG;
   if (q->T < 0 || q->B < 1 || q->max_len < 0) return DSA_ERR_INVALID_ARG;
+  if (q->max_len > kTopkMaxLen) return DSA_ERR_UNSUPPORTED;
   if (q->T > 0 && (q->seq_id == nullptr || q->pos == nullptr || q->max_len < 1)) return DSA_ERR_INVALID_ARG;
   return DSA_OK;
 }
@@ -42,7 +43,7 @@ size_t forward_ws(int32_t T, int32_t max_len, int32_t H, int32_t k, bool with_id
   const int64_t ld = ((int64_t)max_len + 3) & ~int64_t(3);
   size_t s = align256((size_t)T * ld * 4);              // logits
   if (with_idx) s += align256((size_t)T * k * 4);       // selection
-  s += topk_workspace_bytes(T, ld);
+  s += topk_workspace_bytes(T, ld, k);
   s += align256(attn_workspace_bytes(T, H, k));
   return s;
 }
@@ -97,7 +98,7 @@ size_t dsa_workspace_bytes(int32_t op, int32_t T, int32_t max_len, int32_t H, in
   if (T < 0 || max_len < 0 || H < 0 || k < 0) return 0;
   const int64_t ld = ((int64_t)max_len + 3) & ~int64_t(3);
   switch (op) {
-    case DSA_OP_TOPK: return topk_workspace_bytes(T, ld);
+    case DSA_OP_TOPK: return (k > 0) ? topk_workspace_bytes(T, ld, k) : 0;
     case DSA_OP_ATTN: return (H > 0 && k > 0) ? attn_workspace_bytes(T, H, k) : 0;
     case DSA_OP_FORWARD: return (H > 0 && k > 0) ? forward_ws(T, max_len, H, k, true) : 0;
     default: return 0;
@@ -111,19 +112,19 @@ int dsa_indexer_logits(const dsa_queries* q, const dsa_kv_layout* layout, int32_
   int st = validate_indexer(q, layout, H_I, D_I, q_fp8, q_scale, w, k_fp8, k_scale, logits, ld_logits, &lay);
   if (st || q->T == 0) return st;
   return hip_status(launch_indexer(q->T, q->max_len, H_I, D_I, q_fp8, q_scale, w, k_fp8, k_scale, q->seq_id, q->pos,
-                                   lay, logits, ld_logits, stream));
+                                   lay, logits, ld_logits, nullptr, stream));
 }
 
 int dsa_topk(const float* logits, int64_t ld_logits, const int32_t* valid_len, int32_t T, int32_t max_len,
              int32_t k, int32_t* idx, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (T < 0 || max_len < 0 || k < 1) return DSA_ERR_INVALID_ARG;
-  if (k > kMaxK) return DSA_ERR_UNSUPPORTED;
+  if (k > kMaxK || max_len > kTopkMaxLen) return DSA_ERR_UNSUPPORTED;
   if (T == 0) return DSA_OK;
   if (!logits || !valid_len || !idx) return DSA_ERR_INVALID_ARG;
   if (ld_logits < max_len || (ld_logits & 3) || !aligned(logits, 16)) return DSA_ERR_INVALID_ARG;
-  const size_t need = topk_workspace_bytes(T, ld_logits);
+  const size_t need = topk_workspace_bytes(T, ld_logits, k);
   if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)) return DSA_ERR_WORKSPACE;
-  return hip_status(launch_topk(logits, ld_logits, valid_len, 0, T, k, idx, workspace, stream));
+  return hip_status(launch_topk(logits, ld_logits, valid_len, 0, T, max_len, k, idx, workspace, false, stream));
 }
 
 int dsa_sparse_mla_attn(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H, const void* q_bf16,
@@ -171,13 +172,15 @@ int dsa_forward(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, 
     p += align256((size_t)q->T * k * 4);
   }
   void* ws_topk = p;
-  p += topk_workspace_bytes(q->T, ld);
+  p += topk_workspace_bytes(q->T, ld, k);
   void* ws_attn = p;
 
-  hipError_t e = launch_indexer(q->T, q->max_len, H_I, D_I, iq_fp8, iq_scale, iw, ik_fp8, ik_scale, q->seq_id,
-                                q->pos, lay, logits, ld, stream);
+  hipError_t e = launch_topk_zero_hist(ws_topk, q->T, stream);
   if (e != hipSuccess) return DSA_ERR_HIP;
-  e = launch_topk(logits, ld, q->pos, 1, q->T, k, idx, ws_topk, stream);
+  e = launch_indexer(q->T, q->max_len, H_I, D_I, iq_fp8, iq_scale, iw, ik_fp8, ik_scale, q->seq_id, q->pos, lay,
+                     logits, ld, topk_hist_buffer(ws_topk), stream);
+  if (e != hipSuccess) return DSA_ERR_HIP;
+  e = launch_topk(logits, ld, q->pos, 1, q->T, q->max_len, k, idx, ws_topk, true, stream);
   if (e != hipSuccess) return DSA_ERR_HIP;
   e = launch_attn(q->T, H, static_cast<const uint16_t*>(q_bf16), static_cast<const uint16_t*>(kv_bf16), idx, q->seq_id,
                   lay, k, sm_scale, static_cast<uint16_t*>(out_bf16), lse, ws_attn, stream);

@@ -20,6 +20,11 @@
 // Decode is bound by HBM (one 128-byte key row feeds 64 heads x 128 MACs =
 // 128 flop/byte, far under the FP8 ridge), so the kernel streams keys with
 // wide loads and keeps many 8 KB wave tiles in flight.
+//
+// When `hist` is given, the epilogue also counts the top 11 bits of each
+// stored logit's order-preserving key into a per-row 2048-bin histogram (LDS
+// per workgroup, then one global atomic per non-empty bin): the first level
+// of the top-k radix select, obtained without reading the logits again.
 #include "launch.h"
 
 namespace dsa {
@@ -75,8 +80,10 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void indexer_kernel(const uint8_t* 
                                                                  const float* __restrict__ ks,
                                                                  const int32_t* __restrict__ seq_id,
                                                                  const int32_t* __restrict__ pos, Layout lay,
-                                                                 float* __restrict__ logits, int64_t ld) {
+                                                                 float* __restrict__ logits, int64_t ld,
+                                                                 u32* __restrict__ hist) {
   constexpr int MT = (H_I + 15) / 16;  // M tiles of 16 heads
+  __shared__ u32 h_lds[2048];
   using Frag = KeyFrag<H_I, D_I>;
 
   const int t = blockIdx.y;
@@ -110,6 +117,10 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void indexer_kernel(const uint8_t* 
     }
   const float qscale = qs[t];
   float* __restrict__ out_row = logits + (int64_t)t * ld;
+  if (hist != nullptr) {
+    for (int i = threadIdx.x; i < 2048; i += IDX_WAVES * 64) h_lds[i] = 0;
+    __syncthreads();
+  }
 
 #pragma unroll
   for (int it = 0; it < IDX_ITERS; ++it) {
@@ -139,7 +150,19 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void indexer_kernel(const uint8_t* 
       part += __shfl_xor(part, 32, 64);
       if (g == j) res = part;  // lane 16j+n keeps key base+16j+n = base+lane
     }
-    if (s_me <= p) out_row[s_me] = (res * qscale) * ksv;
+    if (s_me <= p) {
+      const float v = (res * qscale) * ksv;
+      out_row[s_me] = v;
+      if (hist != nullptr) atomicAdd(&h_lds[order_key(v) >> 21], 1u);
+    }
+  }
+  if (hist != nullptr) {
+    __syncthreads();
+    u32* g = hist + (int64_t)t * 2048;
+    for (int i = threadIdx.x; i < 2048; i += IDX_WAVES * 64) {
+      const u32 c = h_lds[i];
+      if (c) atomicAdd(&g[i], c);
+    }
   }
 }
 
@@ -150,19 +173,20 @@ bool indexer_supported(int H_I, int D_I) {
 template <int H_I, int D_I>
 static hipError_t launch_t(int T, int max_len, const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8,
                            const float* ks, const int32_t* seq_id, const int32_t* pos, const Layout& lay,
-                           float* logits, int64_t ld, hipStream_t stream) {
+                           float* logits, int64_t ld, u32* hist, hipStream_t stream) {
   dim3 grid((max_len + IDX_KEYS_PER_WG - 1) / IDX_KEYS_PER_WG, T);
   hipLaunchKernelGGL((indexer_kernel<H_I, D_I>), grid, dim3(IDX_WAVES * 64), 0, stream, q8, qs, w, k8, ks, seq_id,
-                     pos, lay, logits, ld);
+                     pos, lay, logits, ld, hist);
   return hipGetLastError();
 }
 
 hipError_t launch_indexer(int T, int max_len, int H_I, int D_I, const uint8_t* q8, const float* qs, const float* w,
                           const uint8_t* k8, const float* ks, const int32_t* seq_id, const int32_t* pos,
-                          const Layout& lay, float* logits, int64_t ld, hipStream_t stream) {
+                          const Layout& lay, float* logits, int64_t ld, u32* hist, hipStream_t stream) {
   if (T == 0 || max_len == 0) return hipSuccess;
 #define DSA_IDX_CASE(HH, DD) \
-  if (H_I == HH && D_I == DD) return launch_t<HH, DD>(T, max_len, q8, qs, w, k8, ks, seq_id, pos, lay, logits, ld, stream);
+  if (H_I == HH && D_I == DD) \
+    return launch_t<HH, DD>(T, max_len, q8, qs, w, k8, ks, seq_id, pos, lay, logits, ld, hist, stream);
   DSA_IDX_CASE(64, 128)
   DSA_IDX_CASE(64, 64)
   DSA_IDX_CASE(4, 128)

@@ -10,16 +10,22 @@
 
 namespace dsa {
 
-// (1) indexer logits; returns false if (H_I, D_I) has no built kernel.
+// (1) indexer logits; `hist` (nullable) receives the per-row 2048-bin
+// histogram of the top 11 key bits (must be zeroed first).
 bool indexer_supported(int H_I, int D_I);
 hipError_t launch_indexer(int T, int max_len, int H_I, int D_I, const uint8_t* q8, const float* qs, const float* w,
                           const uint8_t* k8, const float* ks, const int32_t* seq_id, const int32_t* pos,
-                          const Layout& lay, float* logits, int64_t ld, hipStream_t stream);
+                          const Layout& lay, float* logits, int64_t ld, u32* hist, hipStream_t stream);
 
-// (2) top-k; valid length of row t is valid_len[t] + len_add.
-size_t topk_workspace_bytes(int T, int64_t ld);
-hipError_t launch_topk(const float* logits, int64_t ld, const int32_t* valid_len, int len_add, int T, int k,
-                       int32_t* idx, void* ws, hipStream_t stream);
+// (2) top-k; valid length of row t is valid_len[t] + len_add.  The histogram
+// lives at the start of the top-k workspace (topk_hist_buffer); with
+// hist_ready the caller has already filled it (fused indexer epilogue).
+constexpr int64_t kTopkMaxLen = 4 * 1024 * 1024;  // longest row the selection handles
+size_t topk_workspace_bytes(int T, int64_t ld, int k);
+u32* topk_hist_buffer(void* ws);
+hipError_t launch_topk_zero_hist(void* ws, int T, hipStream_t stream);
+hipError_t launch_topk(const float* logits, int64_t ld, const int32_t* valid_len, int len_add, int T, int max_len,
+                       int k, int32_t* idx, void* ws, bool hist_ready, hipStream_t stream);
 
 // (3) sparse MLA attention (+ split combine)
 bool attn_supported(int H);

@@ -6,20 +6,30 @@
 // shared by all query heads.  A latent row has 576 bf16 values; the key is
 // the whole row, the value its first 512 entries.
 //
-// Work split.  A workgroup takes one query token, a group of 16*NW heads and
-// one slice ("split") of the selected rows; the splits are merged afterwards
-// by a log-sum-exp combine.  Per tile of 32 selected rows:
-//   gather   the rows (1152 B each) go into LDS twice: row-major for the
-//            scores, and the 512 value columns transposed (keys contiguous)
-//            for the value product;
-//   scores   S^T = K Q^T on 16x16x32 bf16 MFMAs: keys on M, this wave's 16
+// Work split.  A workgroup takes one query token, 4 waves of 16 heads each
+// (two head groups cover 128 heads; with fewer than 64 heads the spare waves
+// only help stage rows) and one slice ("split") of the selected rows; the
+// splits are merged afterwards by a log-sum-exp combine.  The O accumulator
+// of a wave's 16 heads is 512 x 16 fp32 (128 registers per lane) and its Q
+// operand 72 registers, so one wave per SIMD holds them with room for the
+// staged next tile.
+//
+// Per tile of 32 selected rows:
+//   gather   the rows' 16-byte chunks are loaded into registers while the
+//            previous tile is computed, then written to the other of two LDS
+//            buffers (double buffering); the 512 no-rope values of a row are
+//            stored row-major with padded rows, the 64 rope values with their
+//            chunks XOR-swizzled by row, so the score reads avoid LDS bank
+//            conflicts;
+//   scores   S^T = K Q^T on 16x16x32 bf16 MFMAs: keys on M, the wave's 16
 //            heads on N, the 576 dims on K.  A lane ends up holding one head
-//            and 8 keys, so the online softmax max/sum need no shuffles
-//            except two xor steps across the four lane groups;
-//   values   O^T += V^T P^T: dims on M (32 tiles of 16), heads on N, the 32
-//            keys on K.  The probabilities already sit in the B-operand
-//            layout (one head per lane), so P never leaves registers, and the
-//            per-head rescale of O is in-lane.
+//            and 8 keys, so the online-softmax max/sum need only two xor
+//            steps across the four lane groups;
+//   values   O^T += V^T P^T: dims on M (32 tiles of 16), heads on N, keys on
+//            K.  V^T comes from the row-major tile through ds_read_b64_tr_b16
+//            (the LDS transpose read of gfx950), and P already sits in the
+//            B-operand layout, so P never leaves registers and the per-head
+//            rescale of O is in-lane.
 // The exponentials use exp2 with log2(e) folded into the scale.
 #include "launch.h"
 
@@ -28,10 +38,16 @@ namespace dsa {
 constexpr int AT_TILE = 32;
 constexpr int AT_D = 576;
 constexpr int AT_DV = 512;
-constexpr int KS_STRIDE = 1168;  // bytes per row-major row in LDS (1152 + 16: rotates banks per row)
-constexpr int VT_STRIDE = 72;    // bytes per transposed value row (32 keys * 2 + 8)
-constexpr int KS_BYTES = AT_TILE * KS_STRIDE;
-constexpr int VT_BYTES = AT_DV * VT_STRIDE;
+constexpr int AT_ROW_BYTES = AT_D * 2;              // 1152
+constexpr int NOPE_STRIDE = 1040;                   // 1024 B + 16 B: rotates LDS banks per row
+constexpr int NOPE_BYTES = AT_TILE * NOPE_STRIDE;   // 33280
+constexpr int ROPE_BYTES = AT_TILE * 128;           // 4096
+constexpr int BUF_BYTES = NOPE_BYTES + ROPE_BYTES;  // 37376
+constexpr int AT_MAX_SPLIT = 2048;                  // rows per split (k <= 2048)
+constexpr u32 ROW_INVALID = 0x80000000u;
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
 
 __device__ __forceinline__ uint16_t f2bf(float f) {
   // round to nearest even (inputs here are finite)
@@ -40,147 +56,200 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return (uint16_t)(u >> 16);
 }
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64, 2) void sparse_mla_kernel(const uint16_t* __restrict__ q,
-                                                               const uint16_t* __restrict__ kv,
-                                                               const int32_t* __restrict__ idx,
-                                                               const int32_t* __restrict__ seq_id, Layout lay,
-                                                               int H, int k, int split_len, int n_splits,
-                                                               float scale_log2, uint16_t* __restrict__ out,
-                                                               float* __restrict__ lse, float* __restrict__ ws_o,
-                                                               float* __restrict__ ws_ml) {
-  constexpr int NT = NW * 64;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[KS_BYTES + VT_BYTES];
-  __shared__ int s_valid[AT_TILE];
-  uint8_t* const Ks = smem;
-  uint8_t* const Vt = smem + KS_BYTES;
+// waits for every LDS access of this wave, and for nothing else
+#define DSA_LGKMCNT0 (0xF | (0x3 << 14) | (0x7 << 4))
 
-  const int split = blockIdx.x;
-  const int t = blockIdx.z;
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses,
+// not for its global loads, so the next tile's loads stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(DSA_LGKMCNT0);
+  __builtin_amdgcn_s_barrier();
+}
+
+// A tile is 32 rows x 72 chunks of 16 bytes.  Thread tid stages chunks
+// tid + NT*r: consecutive threads read consecutive chunks of a row.
+template <int NT>
+struct TileStage {
+  static constexpr int CHUNKS = AT_TILE * 72;
+  static constexpr int PER_THREAD = (CHUNKS + NT - 1) / NT;
+  v4i v[PER_THREAD];
+
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ kv, const u32* rows, int tid) {
+#pragma unroll
+    for (int r = 0; r < PER_THREAD; ++r) {
+      const int c = tid + NT * r;
+      if (CHUNKS % NT == 0 || c < CHUNKS) {
+        const int row = c / 72, col = c - row * 72;
+        const u32 phys = rows[row] & ~ROW_INVALID;
+        v[r] = *reinterpret_cast<const v4i*>(kv + (int64_t)phys * AT_ROW_BYTES + 16 * col);
+      }
+    }
+  }
+  // no-rope chunks row-major (padded rows); rope chunk cc of row r in slot cc^(r&7)
+  __device__ __forceinline__ void store(LDS_AS uint8_t* buf, int tid) const {
+#pragma unroll
+    for (int r = 0; r < PER_THREAD; ++r) {
+      const int c = tid + NT * r;
+      if (CHUNKS % NT == 0 || c < CHUNKS) {
+        const int row = c / 72, col = c - row * 72;
+        LDS_AS uint8_t* dst = (col < 64) ? buf + row * NOPE_STRIDE + 16 * col
+                                         : buf + NOPE_BYTES + row * 128 + 16 * ((col - 64) ^ (row & 7));
+        *reinterpret_cast<LDS_AS v4i*>(dst) = v[r];
+      }
+    }
+  }
+};
+
+// Scores, online softmax and value product for one tile held in `buf`.
+__device__ __forceinline__ void attend_tile(const LDS_AS uint8_t* __restrict__ buf, const u32* rows, const v8bf* qf,
+                                           float scale_log2, int n, int g, float& m_run, float& l_part, v4f* o) {
+  const LDS_AS uint8_t* nope = buf;
+  const LDS_AS uint8_t* rope = buf + NOPE_BYTES;
+  // ---- scores S^T (keys x heads)
+  v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) {
+    const v8bf a0 = *reinterpret_cast<const LDS_AS v8bf*>(nope + n * NOPE_STRIDE + 64 * ks + 16 * g);
+    const v8bf a1 = *reinterpret_cast<const LDS_AS v8bf*>(nope + (16 + n) * NOPE_STRIDE + 64 * ks + 16 * g);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s1, 0, 0, 0);
+    if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int ks = 16; ks < 18; ++ks) {
+    const int c = 4 * (ks - 16) + g;  // rope chunk
+    const int r0 = n, r1 = 16 + n;
+    const v8bf a0 = *reinterpret_cast<const LDS_AS v8bf*>(rope + r0 * 128 + 16 * (c ^ (r0 & 7)));
+    const v8bf a1 = *reinterpret_cast<const LDS_AS v8bf*>(rope + r1 * 128 + 16 * (c ^ (r1 & 7)));
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s1, 0, 0, 0);
+  }
+  // lane holds head n: s0[i] -> key 4g+i, s1[i] -> key 16+4g+i
+  float z[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    z[i] = (rows[4 * g + i] & ROW_INVALID) ? -INFINITY : s0[i] * scale_log2;
+    z[4 + i] = (rows[16 + 4 * g + i] & ROW_INVALID) ? -INFINITY : s1[i] * scale_log2;
+  }
+  float mx = z[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float m_new = fmaxf(m_run, mx);
+  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+  const float corr = exp2f(m_run - m_use);
+  float psum = 0.f;
+  float pz[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    pz[i] = exp2f(z[i] - m_use);
+    psum += pz[i];
+  }
+  l_part = l_part * corr + psum;
+  m_run = m_new;
+  v8bf pb;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pb[i] = __builtin_bit_cast(__bf16, f2bf(pz[i]));
+
+  // ---- values O^T += V^T P^T; V^T rows through the LDS transpose read:
+  // source lane s of group g points at keys kb + s/4, dims 16mt + 4(s%4)..+3
+  const LDS_AS uint8_t* vsrc0 = nope + (4 * g + (n >> 2)) * NOPE_STRIDE + 8 * (n & 3);
+  const LDS_AS uint8_t* vsrc1 = vsrc0 + 16 * NOPE_STRIDE;
+#pragma unroll
+  for (int mt = 0; mt < AT_DV / 16; ++mt) {
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(vsrc0 + 32 * mt));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(vsrc1 + 32 * mt));
+    const v8bf av = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    v4f acc = o[mt] * corr;
+    o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, acc, 0, 0, 0);
+    // bound the read-ahead of the transpose reads (register pressure)
+    if ((mt & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(const uint16_t* __restrict__ q,
+                                                             const uint8_t* __restrict__ kv,
+                                                             const int32_t* __restrict__ idx,
+                                                             const int32_t* __restrict__ seq_id, Layout lay, int H,
+                                                             int k, int split_len, int n_splits, float scale_log2,
+                                                             uint16_t* __restrict__ out, float* __restrict__ lse,
+                                                             float* __restrict__ ws_o, float* __restrict__ ws_ml,
+                                                             int n_tokens) {
+  constexpr int NT = NW * 64;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF_BYTES];
+  __shared__ u32 s_row[AT_MAX_SPLIT];
+
+  // Workgroup -> (token, split, head group).  Workgroups are dealt to the 8
+  // XCDs round-robin by linear id; the head groups of one (token, split)
+  // take consecutive slots of one XCD, so the second gathers its rows from
+  // that XCD's L2 right after the first brought them from HBM.
+  const int n_hg = H / (16 * NW) > 0 ? H / (16 * NW) : 1;
+  const int lin = blockIdx.x;
+  const int xcd = lin & 7;
+  const int slot = lin >> 3;
+  const int pair = xcd + 8 * (slot / n_hg);  // (token, split) index
+  const int hg = slot - (slot / n_hg) * n_hg;
+  const int t = pair / n_splits;
+  const int split = pair - t * n_splits;
+  if (t >= n_tokens) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int n = lane & 15;
   const int g = lane >> 4;
-  const int h0 = blockIdx.y * (16 * NW) + wid * 16;  // first head of this wave
+  const int h0 = hg * (16 * NW) + wid * 16;  // first head of this wave
+  const bool has_heads = h0 < H;             // waves past H only help stage rows
   const int b = seq_id[t];
   const int32_t* __restrict__ idx_row = idx + (int64_t)t * k;
+
+  const int j_begin = split * split_len;
+  const int j_end = min(k, j_begin + split_len);
+  const int nrows = max(0, j_end - j_begin);
+  const int ntiles = (nrows + AT_TILE - 1) / AT_TILE;
+
+  // physical rows of this split (padding and the ragged tail load a valid
+  // row of the sequence and are masked)
+  const int64_t safe_row = token_row(lay, b, 0);
+  for (int i = tid; i < ntiles * AT_TILE; i += NT) {
+    const int j = j_begin + i;
+    const int s = (i < nrows) ? idx_row[j] : -1;
+    s_row[i] = (s >= 0) ? (u32)token_row(lay, b, s) : ((u32)safe_row | ROW_INVALID);
+  }
 
   // Q^T operand: head h0+n, dims 32*ks + 8g .. +8
   v8bf qf[AT_D / 32];
   {
-    const uint16_t* qrow = q + ((int64_t)t * H + h0 + n) * AT_D + 8 * g;
+    const uint16_t* qrow = q + ((int64_t)t * H + (has_heads ? h0 : 0) + n) * AT_D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < AT_D / 32; ++ks) qf[ks] = *reinterpret_cast<const v8bf*>(qrow + 32 * ks);
   }
-
   float m_run = -INFINITY;  // running max (log2 units) of head h0+n
   float l_part = 0.f;       // partial sum over this lane's keys
   v4f o[AT_DV / 16];
 #pragma unroll
   for (int mt = 0; mt < AT_DV / 16; ++mt) o[mt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const int j_begin = split * split_len;
-  const int j_end = min(k, j_begin + split_len);
-
-  for (int j0 = j_begin; j0 < j_end; j0 += AT_TILE) {
-    __syncthreads();  // previous tile fully consumed
-    // ---- gather 32 rows: value part as (4 keys x 8 dims) groups, rope part row-major only
-#pragma unroll
-    for (int r = 0; r < (8 * 64) / NT; ++r) {
-      const int gi = tid + NT * r;
-      const int kq = gi & 7;   // key quad
-      const int oc = gi >> 3;  // dim octet 0..63
-      v4i c[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int j = j0 + 4 * kq + rr;
-        int s = (j < j_end) ? idx_row[j] : -1;
-        s = (s < 0) ? 0 : s;
-        const int64_t row = token_row(lay, b, s);
-        c[rr] = *reinterpret_cast<const v4i*>(kv + row * AT_D + 8 * oc);
-        *reinterpret_cast<v4i*>(Ks + (4 * kq + rr) * KS_STRIDE + 16 * oc) = c[rr];
-      }
-      // transpose: dim 8*oc + d gets keys 4kq..4kq+3 (8 bytes)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const u32 a0 = (u32)c[0][m], a1 = (u32)c[1][m], a2 = (u32)c[2][m], a3 = (u32)c[3][m];
-        v2i lo, hi;
-        lo[0] = (int)((a0 & 0xFFFFu) | (a1 << 16));
-        lo[1] = (int)((a2 & 0xFFFFu) | (a3 << 16));
-        hi[0] = (int)((a0 >> 16) | (a1 & 0xFFFF0000u));
-        hi[1] = (int)((a2 >> 16) | (a3 & 0xFFFF0000u));
-        *reinterpret_cast<v2i*>(Vt + (8 * oc + 2 * m) * VT_STRIDE + 8 * kq) = lo;
-        *reinterpret_cast<v2i*>(Vt + (8 * oc + 2 * m + 1) * VT_STRIDE + 8 * kq) = hi;
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < (AT_TILE * 8) / NT; ++r) {
-      const int gi = tid + NT * r;
-      const int rowi = gi >> 3;
-      const int oc = 64 + (gi & 7);
-      const int j = j0 + rowi;
-      int s = (j < j_end) ? idx_row[j] : -1;
-      s = (s < 0) ? 0 : s;
-      const int64_t row = token_row(lay, b, s);
-      *reinterpret_cast<v4i*>(Ks + rowi * KS_STRIDE + 16 * oc) =
-          *reinterpret_cast<const v4i*>(kv + row * AT_D + 8 * oc);
-    }
-    if (tid < AT_TILE) {
-      const int j = j0 + tid;
-      s_valid[tid] = (j < j_end) && (idx_row[j] >= 0);
-    }
-    __syncthreads();
-
-    // ---- scores S^T (keys x heads)
-    v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < AT_D / 32; ++ks) {
-      const v8bf a0 = *reinterpret_cast<const v8bf*>(Ks + n * KS_STRIDE + 64 * ks + 16 * g);
-      const v8bf a1 = *reinterpret_cast<const v8bf*>(Ks + (16 + n) * KS_STRIDE + 64 * ks + 16 * g);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s1, 0, 0, 0);
-    }
-    // lane holds head n: s0[i] -> key 4g+i, s1[i] -> key 16+4g+i
-    float z[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[i] = s_valid[4 * g + i] ? s0[i] * scale_log2 : -INFINITY;
-      z[4 + i] = s_valid[16 + 4 * g + i] ? s1[i] * scale_log2 : -INFINITY;
-    }
-    float mx = z[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float corr = exp2f(m_run - m_use);
-    float psum = 0.f;
-    float pz[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pz[i] = exp2f(z[i] - m_use);
-      psum += pz[i];
-    }
-    l_part = l_part * corr + psum;
-    m_run = m_new;
-    v8bf pb;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pb[i] = __builtin_bit_cast(__bf16, f2bf(pz[i]));
-
-    // ---- values O^T += V^T P^T
-#pragma unroll
-    for (int mt = 0; mt < AT_DV / 16; ++mt) {
-      const uint8_t* vrow = Vt + (mt * 16 + n) * VT_STRIDE;
-      const v2i lo = *reinterpret_cast<const v2i*>(vrow + 8 * g);
-      const v2i hi = *reinterpret_cast<const v2i*>(vrow + 32 + 8 * g);
-      const v4i av = v4i{lo[0], lo[1], hi[0], hi[1]};
-      v4f acc = o[mt] * corr;
-      o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av), pb, acc, 0, 0, 0);
-    }
+  LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
+  __syncthreads();  // s_row visible
+  TileStage<NT> stage;
+  if (ntiles > 0) {
+    stage.load(kv, s_row, tid);
+    stage.store(lds, tid);
+  }
+  for (int it = 0; it < ntiles; ++it) {
+    LDS_AS uint8_t* cur = lds + (it & 1) * BUF_BYTES;
+    const bool more = it + 1 < ntiles;
+    if (more) stage.load(kv, s_row + (it + 1) * AT_TILE, tid);  // in flight during this tile
+    lds_barrier();  // tile `it` is in `cur`; the other buffer is free
+    // waves without heads compute on head 0's query and discard the result:
+    // uniform control flow keeps the accumulators in registers
+    attend_tile(cur, s_row + it * AT_TILE, qf, scale_log2, n, g, m_run, l_part, o);
+    if (more) stage.store(lds + ((it + 1) & 1) * BUF_BYTES, tid);
   }
 
+  if (!has_heads) return;
   // ---- finish: sum l over the four lane groups
   float l = l_part;
   l += __shfl_xor(l, 16, 64);
@@ -253,14 +322,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 bool attn_supported(int H) { return H == 16 || H == 32 || H == 64 || H == 128; }
 
-static int heads_per_wg(int H) { return H >= 64 ? 64 : H; }
+constexpr int AT_NW = 4;  // 4 waves x 16 heads per workgroup
+
+static int head_groups(int H) { return H > 16 * AT_NW ? H / (16 * AT_NW) : 1; }
 
 int attn_splits(int T, int H, int k) {
-  const int base = T * (H / heads_per_wg(H));
+  const int base = T * head_groups(H);
   const int tiles = (k + AT_TILE - 1) / AT_TILE;
   int s = 1;
-  // each split keeps >= 8 tiles; stop once the grid reaches 256 workgroups
-  while (base * s < 256 && tiles / (2 * s) >= 8) s *= 2;
+  // keep >= 4 tiles per split; stop once the grid reaches 256 workgroups
+  while (base * s < 256 && tiles / (2 * s) >= 4) s *= 2;
   return s;
 }
 
@@ -271,20 +342,11 @@ size_t attn_workspace_bytes(int T, int H, int k) {
   return align256(slots * AT_DV * 4) + align256(slots * 2 * 4);
 }
 
-template <int NW>
-static void launch_main(dim3 grid, hipStream_t stream, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
-                        const int32_t* seq_id, const Layout& lay, int H, int k, int split_len, int n_splits,
-                        float scale_log2, uint16_t* out, float* lse, float* ws_o, float* ws_ml) {
-  hipLaunchKernelGGL((sparse_mla_kernel<NW>), grid, dim3(NW * 64), 0, stream, q, kv, idx, seq_id, lay, H, k,
-                     split_len, n_splits, scale_log2, out, lse, ws_o, ws_ml);
-}
-
 hipError_t launch_attn(int T, int H, const uint16_t* q, const uint16_t* kv, const int32_t* idx, const int32_t* seq_id,
                        const Layout& lay, int k, float sm_scale, uint16_t* out, float* lse, void* ws,
                        hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  const int hpw = heads_per_wg(H);
-  const int nw = hpw / 16;
+  const int n_hg = head_groups(H);
   const int n_splits = attn_splits(T, H, k);
   const int tiles = (k + AT_TILE - 1) / AT_TILE;
   const int split_len = ((tiles + n_splits - 1) / n_splits) * AT_TILE;
@@ -296,13 +358,12 @@ hipError_t launch_attn(int T, int H, const uint16_t* q, const uint16_t* kv, cons
     ws_o = reinterpret_cast<float*>(ws);
     ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256(slots * AT_DV * 4));
   }
-  dim3 grid(n_splits, H / hpw, T);
-  switch (nw) {
-    case 1: launch_main<1>(grid, stream, q, kv, idx, seq_id, lay, H, k, split_len, n_splits, scale_log2, out, lse, ws_o, ws_ml); break;
-    case 2: launch_main<2>(grid, stream, q, kv, idx, seq_id, lay, H, k, split_len, n_splits, scale_log2, out, lse, ws_o, ws_ml); break;
-    case 4: launch_main<4>(grid, stream, q, kv, idx, seq_id, lay, H, k, split_len, n_splits, scale_log2, out, lse, ws_o, ws_ml); break;
-    default: return hipErrorInvalidValue;
-  }
+  // (token, split) pairs rounded up to a multiple of 8 (one per XCD per slot)
+  const int pairs = T * n_splits;
+  const int blocks = ((pairs + 7) / 8) * 8 * n_hg;
+  hipLaunchKernelGGL((sparse_mla_kernel<AT_NW>), dim3(blocks), dim3(AT_NW * 64), 0, stream, q,
+                     reinterpret_cast<const uint8_t*>(kv), idx, seq_id, lay, H, k, split_len, n_splits, scale_log2,
+                     out, lse, ws_o, ws_ml, T);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_splits == 1) return e;
   const int TH = T * H;

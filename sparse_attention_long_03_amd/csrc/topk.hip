@@ -5,44 +5,53 @@
 // key-value entries.  Result: the positions of the k largest logits of the
 // row; equal logits are taken lowest position first; -0 equals +0.
 //
-// One 1024-thread workgroup per row:
-//   pass 1  histogram of the top 11 key bits (2048 bins, LDS atomics);
-//           the bin holding the k-th largest value is found by a block scan;
-//   pass 2  one ordered sweep of the row: positions whose bin is above the
-//           threshold bin are written to the output at once, positions inside
-//           it are appended, in position order, to a candidate list;
-//   pass 3  two more histogram rounds over the candidates (bits 20..10, then
-//           9..0) give the exact k-th key v* and how many ties at v* to keep;
-//   pass 4  an ordered sweep of the candidates writes keys above v* and the
-//           first ties at v*.
-// Ordered compaction uses wave prefix sums and one block scan per 4096
-// elements, so the output is deterministic: the positions above the
-// threshold bin in ascending order, then the selected candidates ascending.
+// A 128K-long row is 512 KB, so one workgroup per row would leave most of the
+// chip idle.  The selection is split over three launches:
+//   histogram  a per-row count of the top 11 key bits (2048 bins); in
+//              dsa_forward the indexer builds it in its epilogue, so the
+//              logits are not read for it;
+//   chunk      many workgroups per row (4096 positions each) find the bin
+//              that holds the k-th largest key from the histogram, and sweep
+//              their chunk once: positions in higher bins go to a per-chunk
+//              "above" list, positions in the threshold bin to a per-chunk
+//              candidate list, both in position order;
+//   resolve    one workgroup per row concatenates the above lists, finds the
+//              exact k-th key among the candidates with two more histogram
+//              rounds (bits 20..10, 9..0), and appends the candidates above it
+//              plus the first ties at it.
+// Everything is written at positions derived from counts, never from atomics,
+// so the output is deterministic: above-threshold-bin positions ascending,
+// then the selected candidates ascending.
 #include "launch.h"
 
 namespace dsa {
 
-constexpr int TK_NT = 1024;
-constexpr int TK_E = 4;
-constexpr int TK_CHUNK = TK_NT * TK_E;
+constexpr int TK_CH = 4096;  // positions per chunk
+constexpr int TK_CHUNK_NT = 256;
+constexpr int TK_RES_NT = 1024;
+constexpr int TK_BINS = 2048;
+constexpr int TK_MAX_CHUNKS = TK_RES_NT;  // rows up to 4M positions
+constexpr int TK_RES_STAGE = 12288;       // candidates staged in LDS (96 KB)
 
-// Threshold search: bins are visited from the top; returns the bin holding
-// the `need`-th largest element and the count of elements in higher bins.
-template <int NB>
+__device__ __forceinline__ int row_len(const int32_t* valid_len, int len_add, int t) { return valid_len[t] + len_add; }
+
+// Threshold search over NB bins visited from the top with NT threads: the bin
+// holding the `need`-th largest element and the count in higher bins.
+template <int NB, int NT>
 __device__ __forceinline__ void find_threshold(const u32* hist, u32 need, u32* scratch, u32* out_bin,
                                                u32* out_above) {
-  constexpr int BPT = NB / TK_NT;  // bins per thread: 2 or 1
+  constexpr int BPT = NB / NT;
   const int tid = threadIdx.x;
   u32 c[BPT];
-  u32 tot_mine = 0;
+  u32 mine = 0;
 #pragma unroll
   for (int i = 0; i < BPT; ++i) {
     c[i] = hist[NB - 1 - (tid * BPT + i)];
-    tot_mine += c[i];
+    mine += c[i];
   }
   u32 total;
-  const u32 incl = block_incl_scan<TK_NT>(tot_mine, scratch, &total);
-  u32 excl = incl - tot_mine;
+  const u32 incl = block_incl_scan<NT>(mine, scratch, &total);
+  u32 excl = incl - mine;
   if (excl < need && incl >= need) {
 #pragma unroll
     for (int i = 0; i < BPT; ++i) {
@@ -57,169 +66,281 @@ __device__ __forceinline__ void find_threshold(const u32* hist, u32 need, u32* s
   __syncthreads();
 }
 
-__global__ __launch_bounds__(TK_NT) void topk_kernel(const float* __restrict__ logits, int64_t ld,
-                                                     const int32_t* __restrict__ valid_len, int len_add, int k,
-                                                     int32_t* __restrict__ idx, u32* __restrict__ cand_key,
-                                                     int32_t* __restrict__ cand_pos) {
-  __shared__ u32 hist[2048];
-  __shared__ u32 scratch[TK_NT / 64 + 1];
-  __shared__ u32 sh_bin, sh_above;
+__global__ void zero_u32_kernel(u32* __restrict__ p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
+}
 
+// Histogram of the top 11 key bits of each row (standalone selection).
+__global__ __launch_bounds__(TK_CHUNK_NT) void topk_hist_kernel(const float* __restrict__ logits, int64_t ld,
+                                                                const int32_t* __restrict__ valid_len, int len_add,
+                                                                int k, u32* __restrict__ hist) {
+  __shared__ u32 h[TK_BINS];
+  const int t = blockIdx.y;
+  const int n = row_len(valid_len, len_add, t);
+  const int c0 = blockIdx.x * TK_CH;
+  if (n <= k || c0 >= n) return;
+  for (int i = threadIdx.x; i < TK_BINS; i += TK_CHUNK_NT) h[i] = 0;
+  __syncthreads();
+  const float* row = logits + (int64_t)t * ld;
+  const int c1 = min(n, c0 + TK_CH);
+  for (int i = c0 + threadIdx.x; i < c1; i += TK_CHUNK_NT) atomicAdd(&h[order_key(row[i]) >> 21], 1u);
+  __syncthreads();
+  u32* g = hist + (int64_t)t * TK_BINS;
+  for (int i = threadIdx.x; i < TK_BINS; i += TK_CHUNK_NT)
+    if (h[i]) atomicAdd(&g[i], h[i]);
+}
+
+struct TopkWs {
+  u32* hist;      // [T, 2048]
+  u32* counts;    // [T, nch, 2]   (above, candidates) per chunk
+  int32_t* above; // [T, nch, cap_above]
+  u32* ckey;      // [T, nch, TK_CH]
+  int32_t* cpos;  // [T, nch, TK_CH]
+  int nch;
+  int cap_above;
+};
+
+__global__ __launch_bounds__(TK_CHUNK_NT) void topk_chunk_kernel(const float* __restrict__ logits, int64_t ld,
+                                                                 const int32_t* __restrict__ valid_len, int len_add,
+                                                                 int k, TopkWs ws) {
+  constexpr int NT = TK_CHUNK_NT;
+  constexpr int E = TK_CH / NT;  // 16 positions per thread
+  __shared__ u32 scratch[NT / 64 + 1];
+  __shared__ u32 sh_bin, sh_above;
+  const int t = blockIdx.y;
+  const int c = blockIdx.x;
+  const int n = row_len(valid_len, len_add, t);
+  const int c0 = c * TK_CH;
+  if (n <= k || c0 >= n) return;
+  find_threshold<TK_BINS, NT>(ws.hist + (int64_t)t * TK_BINS, (u32)k, scratch, &sh_bin, &sh_above);
+  const u32 b1 = sh_bin;
+
+  const float* row = logits + (int64_t)t * ld;
+  const int i0 = c0 + threadIdx.x * E;
+  u32 kk[E];
+#pragma unroll
+  for (int q = 0; q < E / 4; ++q) {
+    const int i = i0 + 4 * q;
+    if (i + 4 <= n) {
+      const float4 v = *reinterpret_cast<const float4*>(row + i);
+      kk[4 * q + 0] = order_key(v.x);
+      kk[4 * q + 1] = order_key(v.y);
+      kk[4 * q + 2] = order_key(v.z);
+      kk[4 * q + 3] = order_key(v.w);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kk[4 * q + e] = (i + e < n) ? order_key(row[i + e]) : 0u;
+    }
+  }
+  u32 na = 0, nc = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool ok = (i0 + e) < n;
+    const u32 bin = kk[e] >> 21;
+    na += (ok && bin > b1) ? 1u : 0u;
+    nc += (ok && bin == b1) ? 1u : 0u;
+  }
+  const u32 packed = (nc << 16) | na;
+  u32 tot;
+  const u32 incl = block_incl_scan<NT>(packed, scratch, &tot);
+  const u32 excl = incl - packed;
+  const int64_t slot = (int64_t)t * ws.nch + c;
+  int32_t* abv = ws.above + slot * ws.cap_above;
+  u32* ck = ws.ckey + slot * TK_CH;
+  int32_t* cp = ws.cpos + slot * TK_CH;
+  u32 ao = excl & 0xFFFFu, co = excl >> 16;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (i0 + e >= n) continue;
+    const u32 bin = kk[e] >> 21;
+    if (bin > b1) {
+      abv[ao++] = i0 + e;
+    } else if (bin == b1) {
+      ck[co] = kk[e];
+      cp[co] = i0 + e;
+      ++co;
+    }
+  }
+  if (threadIdx.x == 0) {
+    ws.counts[slot * 2 + 0] = tot & 0xFFFFu;
+    ws.counts[slot * 2 + 1] = tot >> 16;
+  }
+}
+
+// Largest c in [0, n) with off[c] <= j (off ascending, off[0] = 0).
+__device__ __forceinline__ int chunk_of(const u32* off, int n, u32 j) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= j) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(TK_RES_NT) void topk_resolve_kernel(const int32_t* __restrict__ valid_len, int len_add,
+                                                                 int k, int32_t* __restrict__ idx, TopkWs ws) {
+  constexpr int NT = TK_RES_NT;
+  __shared__ u32 hist[TK_BINS];
+  __shared__ u32 scratch[NT / 64 + 1];
+  __shared__ u32 sh_bin, sh_above;
+  __shared__ u32 s_aoff[TK_MAX_CHUNKS], s_coff[TK_MAX_CHUNKS];
+  __shared__ u32 s_ckey[TK_RES_STAGE];
+  __shared__ int32_t s_cpos[TK_RES_STAGE];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
-  const int n = valid_len[t] + len_add;
+  const int n = row_len(valid_len, len_add, t);
   int32_t* __restrict__ out = idx + (int64_t)t * k;
   if (n <= k) {
-    for (int i = tid; i < k; i += TK_NT) out[i] = (i < n) ? i : -1;
+    for (int i = tid; i < k; i += NT) out[i] = (i < n) ? i : -1;
     return;
   }
-  const float* __restrict__ row = logits + (int64_t)t * ld;
-  u32* __restrict__ ckey = cand_key + (int64_t)t * ld;
-  int32_t* __restrict__ cpos = cand_pos + (int64_t)t * ld;
+  const int nch = (n + TK_CH - 1) / TK_CH;  // <= TK_MAX_CHUNKS (checked on the host)
+  const int64_t slot0 = (int64_t)t * ws.nch;
 
-  // ---- pass 1: histogram of bits 31..21
-  for (int i = tid; i < 2048; i += TK_NT) hist[i] = 0;
-  __syncthreads();
-  for (int i0 = tid * TK_E; i0 < n; i0 += TK_CHUNK) {
-    if (i0 + TK_E <= n) {
-      const float4 v = *reinterpret_cast<const float4*>(row + i0);
-      atomicAdd(&hist[order_key(v.x) >> 21], 1u);
-      atomicAdd(&hist[order_key(v.y) >> 21], 1u);
-      atomicAdd(&hist[order_key(v.z) >> 21], 1u);
-      atomicAdd(&hist[order_key(v.w) >> 21], 1u);
-    } else {
-      for (int i = i0; i < n; ++i) atomicAdd(&hist[order_key(row[i]) >> 21], 1u);
-    }
+  // ---- per-chunk counts -> exclusive offsets (one chunk per thread)
+  const u32 my_a = (tid < nch) ? ws.counts[(slot0 + tid) * 2 + 0] : 0u;
+  const u32 my_c = (tid < nch) ? ws.counts[(slot0 + tid) * 2 + 1] : 0u;
+  u32 tot;
+  const u32 incl = block_incl_scan<NT>((my_c << 16) | my_a, scratch, &tot);
+  // counts per chunk are <= 4096, but totals may exceed 16 bits: rescan separately if needed
+  u32 a_excl, c_excl, A, C;
+  if (nch * TK_CH < 65536) {
+    a_excl = (incl - ((my_c << 16) | my_a)) & 0xFFFFu;
+    c_excl = (incl - ((my_c << 16) | my_a)) >> 16;
+    A = tot & 0xFFFFu;
+    C = tot >> 16;
+  } else {
+    const u32 ia = block_incl_scan<NT>(my_a, scratch, &A);
+    const u32 ic = block_incl_scan<NT>(my_c, scratch, &C);
+    a_excl = ia - my_a;
+    c_excl = ic - my_c;
+  }
+  if (tid < nch) {
+    s_aoff[tid] = a_excl;
+    s_coff[tid] = c_excl;
   }
   __syncthreads();
-  find_threshold<2048>(hist, (u32)k, scratch, &sh_bin, &sh_above);
-  const u32 b1 = sh_bin;
-  const u32 above1 = sh_above;
-  const u32 n_cand = hist[b1];
-  __syncthreads();
 
-  // ---- pass 2: ordered sweep; emit bins above b1, collect bin b1
-  u32 emit_base = 0, cand_base = 0;
-  for (int c0 = 0; c0 < n; c0 += TK_CHUNK) {
-    const int i0 = c0 + tid * TK_E;
-    u32 kk[TK_E];
-    bool ok[TK_E];
-    if (i0 + TK_E <= n) {
-      const float4 v = *reinterpret_cast<const float4*>(row + i0);
-      kk[0] = order_key(v.x);
-      kk[1] = order_key(v.y);
-      kk[2] = order_key(v.z);
-      kk[3] = order_key(v.w);
-#pragma unroll
-      for (int e = 0; e < TK_E; ++e) ok[e] = true;
-    } else {
-#pragma unroll
-      for (int e = 0; e < TK_E; ++e) {
-        ok[e] = (i0 + e) < n;
-        kk[e] = ok[e] ? order_key(row[i0 + e]) : 0u;
-      }
-    }
-    u32 ne = 0, nc = 0;
-#pragma unroll
-    for (int e = 0; e < TK_E; ++e) {
-      const u32 bin = kk[e] >> 21;
-      ne += (ok[e] && bin > b1) ? 1u : 0u;
-      nc += (ok[e] && bin == b1) ? 1u : 0u;
-    }
-    const u32 packed = (nc << 16) | ne;
-    u32 tot;
-    const u32 incl = block_incl_scan<TK_NT>(packed, scratch, &tot);
-    const u32 excl = incl - packed;
-    u32 eo = emit_base + (excl & 0xFFFFu);
-    u32 co = cand_base + (excl >> 16);
-#pragma unroll
-    for (int e = 0; e < TK_E; ++e) {
-      if (!ok[e]) continue;
-      const u32 bin = kk[e] >> 21;
-      if (bin > b1) {
-        out[eo++] = i0 + e;
-      } else if (bin == b1) {
-        ckey[co] = kk[e];
-        cpos[co] = i0 + e;
-        ++co;
-      }
-    }
-    emit_base += tot & 0xFFFFu;
-    cand_base += tot >> 16;
+  // ---- above lists, concatenated in chunk order
+  for (u32 j = tid; j < A; j += NT) {
+    const int c = chunk_of(s_aoff, nch, j);
+    out[j] = ws.above[(slot0 + c) * ws.cap_above + (j - s_aoff[c])];
   }
-  // candidates written by other threads of this workgroup are re-read below
-  __threadfence();
-  __syncthreads();
+  const u32 need1 = (u32)k - A;
 
-  // ---- pass 3: resolve the exact k-th key among the candidates
-  const u32 need1 = (u32)k - above1;
-  for (int i = tid; i < 2048; i += TK_NT) hist[i] = 0;
+  // ---- candidates: stage (key bits 20..0, position) in LDS when they fit
+  const bool staged = C <= TK_RES_STAGE;
+  if (staged) {
+    for (u32 j = tid; j < C; j += NT) {
+      const int c = chunk_of(s_coff, nch, j);
+      const int64_t g = (slot0 + c) * TK_CH + (j - s_coff[c]);
+      s_ckey[j] = ws.ckey[g] & 0x1FFFFFu;
+      s_cpos[j] = ws.cpos[g];
+    }
+  }
+  for (int i = tid; i < TK_BINS; i += NT) hist[i] = 0;
   __syncthreads();
-  for (u32 j = tid; j < n_cand; j += TK_NT) atomicAdd(&hist[(ckey[j] >> 10) & 0x7FFu], 1u);
+  auto cand_key = [&](u32 j) -> u32 {
+    if (staged) return s_ckey[j];
+    const int c = chunk_of(s_coff, nch, j);
+    return ws.ckey[(slot0 + c) * TK_CH + (j - s_coff[c])] & 0x1FFFFFu;
+  };
+  auto cand_pos = [&](u32 j) -> int32_t {
+    if (staged) return s_cpos[j];
+    const int c = chunk_of(s_coff, nch, j);
+    return ws.cpos[(slot0 + c) * TK_CH + (j - s_coff[c])];
+  };
+
+  // ---- exact k-th key among the candidates: bits 20..10, then 9..0
+  for (u32 j = tid; j < C; j += NT) atomicAdd(&hist[cand_key(j) >> 10], 1u);
   __syncthreads();
-  find_threshold<2048>(hist, need1, scratch, &sh_bin, &sh_above);
+  find_threshold<TK_BINS, NT>(hist, need1, scratch, &sh_bin, &sh_above);
   const u32 b2 = sh_bin;
   const u32 need2 = need1 - sh_above;
   __syncthreads();
-  for (int i = tid; i < 1024; i += TK_NT) hist[i] = 0;
+  for (int i = tid; i < 1024; i += NT) hist[i] = 0;
   __syncthreads();
-  const u32 hi2 = (b1 << 11) | b2;  // bits 31..10 of the keys still in play
-  for (u32 j = tid; j < n_cand; j += TK_NT) {
-    const u32 key = ckey[j];
-    if ((key >> 10) == hi2) atomicAdd(&hist[key & 0x3FFu], 1u);
+  for (u32 j = tid; j < C; j += NT) {
+    const u32 key = cand_key(j);
+    if ((key >> 10) == b2) atomicAdd(&hist[key & 0x3FFu], 1u);
   }
   __syncthreads();
-  find_threshold<1024>(hist, need2, scratch, &sh_bin, &sh_above);
-  const u32 vstar = (hi2 << 10) | sh_bin;
-  const u32 ties = need2 - sh_above;  // how many keys equal to vstar to keep (>= 1)
+  find_threshold<1024, NT>(hist, need2, scratch, &sh_bin, &sh_above);
+  const u32 low = (b2 << 10) | sh_bin;  // bits 20..0 of the k-th key
+  const u32 ties = need2 - sh_above;    // keys equal to it that are kept (>= 1)
 
-  // ---- pass 4: ordered sweep of the candidates
+  // ---- ordered sweep of the candidates (flattened order = position order)
   u32 gt_base = 0, eq_base = 0;
-  for (u32 c0 = 0; c0 < n_cand; c0 += TK_CHUNK) {
-    const u32 j0 = c0 + tid * TK_E;
-    u32 kk[TK_E];
-    u32 ngt = 0, neq = 0;
-#pragma unroll
-    for (int e = 0; e < TK_E; ++e) {
-      kk[e] = (j0 + e < n_cand) ? ckey[j0 + e] : 0u;
-      const bool ok = (j0 + e) < n_cand;
-      ngt += (ok && kk[e] > vstar) ? 1u : 0u;
-      neq += (ok && kk[e] == vstar) ? 1u : 0u;
-    }
-    const u32 packed = (neq << 16) | ngt;
-    u32 tot;
-    const u32 incl = block_incl_scan<TK_NT>(packed, scratch, &tot);
-    const u32 excl = incl - packed;
-    u32 gt_before = gt_base + (excl & 0xFFFFu);
-    u32 eq_before = eq_base + (excl >> 16);
-#pragma unroll
-    for (int e = 0; e < TK_E; ++e) {
-      if (j0 + e >= n_cand) continue;
-      const u32 key = kk[e];
-      if (key > vstar) {
-        out[above1 + gt_before + min(eq_before, ties)] = cpos[j0 + e];
-        ++gt_before;
-      } else if (key == vstar) {
-        if (eq_before < ties) out[above1 + gt_before + eq_before] = cpos[j0 + e];
-        ++eq_before;
-      }
-    }
-    gt_base += tot & 0xFFFFu;
-    eq_base += tot >> 16;
+  for (u32 j0 = 0; j0 < C; j0 += NT) {
+    const u32 j = j0 + tid;
+    const bool ok = j < C;
+    const u32 key = ok ? cand_key(j) : 0u;
+    const u32 gt = (ok && key > low) ? 1u : 0u;
+    const u32 eq = (ok && key == low) ? 1u : 0u;
+    const u32 packed = (eq << 16) | gt;
+    u32 bt;
+    const u32 bincl = block_incl_scan<NT>(packed, scratch, &bt);
+    const u32 excl = bincl - packed;
+    const u32 gt_before = gt_base + (excl & 0xFFFFu);
+    const u32 eq_before = eq_base + (excl >> 16);
+    if (gt) out[A + gt_before + min(eq_before, ties)] = cand_pos(j);
+    else if (eq && eq_before < ties) out[A + gt_before + eq_before] = cand_pos(j);
+    gt_base += bt & 0xFFFFu;
+    eq_base += bt >> 16;
   }
 }
 
-size_t topk_workspace_bytes(int T, int64_t ld) {
-  return 2 * align256((size_t)T * (size_t)ld * 4);
+static int topk_nch(int64_t ld) { return (int)((ld + TK_CH - 1) / TK_CH); }
+
+static TopkWs carve(void* ws, int T, int64_t ld, int k) {
+  TopkWs w;
+  w.nch = topk_nch(ld);
+  w.cap_above = k < TK_CH ? k : TK_CH;
+  char* p = static_cast<char*>(ws);
+  const size_t slots = (size_t)T * w.nch;
+  w.hist = reinterpret_cast<u32*>(p);
+  p += align256((size_t)T * TK_BINS * 4);
+  w.counts = reinterpret_cast<u32*>(p);
+  p += align256(slots * 2 * 4);
+  w.above = reinterpret_cast<int32_t*>(p);
+  p += align256(slots * w.cap_above * 4);
+  w.ckey = reinterpret_cast<u32*>(p);
+  p += align256(slots * TK_CH * 4);
+  w.cpos = reinterpret_cast<int32_t*>(p);
+  return w;
 }
 
-hipError_t launch_topk(const float* logits, int64_t ld, const int32_t* valid_len, int len_add, int T, int k,
-                       int32_t* idx, void* ws, hipStream_t stream) {
+size_t topk_workspace_bytes(int T, int64_t ld, int k) {
+  const size_t slots = (size_t)T * topk_nch(ld);
+  return align256((size_t)T * TK_BINS * 4) + align256(slots * 2 * 4) + align256(slots * (size_t)(k < TK_CH ? k : TK_CH) * 4) +
+         2 * align256(slots * TK_CH * 4);
+}
+
+u32* topk_hist_buffer(void* ws) { return static_cast<u32*>(ws); }
+
+hipError_t launch_topk_zero_hist(void* ws, int T, hipStream_t stream) {
+  const int64_t n = (int64_t)T * TK_BINS;
+  const int64_t want = (n + 255) / 256;
+  const int blocks = (int)(want < 1024 ? want : 1024);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(blocks), dim3(256), 0, stream, topk_hist_buffer(ws), n);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* logits, int64_t ld, const int32_t* valid_len, int len_add, int T, int max_len,
+                       int k, int32_t* idx, void* ws, bool hist_ready, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  u32* cand_key = reinterpret_cast<u32*>(ws);
-  int32_t* cand_pos = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + align256((size_t)T * ld * 4));
-  hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(TK_NT), 0, stream, logits, ld, valid_len, len_add, k, idx, cand_key,
-                     cand_pos);
+  TopkWs w = carve(ws, T, ld, k);
+  const int nch_need = (max_len + TK_CH - 1) / TK_CH;
+  const int nch = nch_need > 0 ? nch_need : 1;
+  if (!hist_ready) {
+    hipError_t e = launch_topk_zero_hist(ws, T, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_hist_kernel, dim3(nch, T), dim3(TK_CHUNK_NT), 0, stream, logits, ld, valid_len, len_add, k,
+                       w.hist);
+  }
+  hipLaunchKernelGGL(topk_chunk_kernel, dim3(nch, T), dim3(TK_CHUNK_NT), 0, stream, logits, ld, valid_len, len_add, k,
+                     w);
+  hipLaunchKernelGGL(topk_resolve_kernel, dim3(T), dim3(TK_RES_NT), 0, stream, valid_len, len_add, k, idx, w);
   return hipGetLastError();
 }
 
