@@ -38,9 +38,14 @@ def _flags():
     ]
 
 
+# Per-file code-generation options.  The indexer reads its MFMA results with
+# VALU code, so it asks for the VGPR form of the MFMAs (no AGPR round trips).
+EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *_flags(), *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -33,6 +33,11 @@ constexpr int IDX_WAVES = 4;
 constexpr int IDX_ITERS = 4;                                    // 64-key groups per wave
 constexpr int IDX_KEYS_PER_WG = IDX_WAVES * IDX_ITERS * 64;     // 1024 keys per workgroup
 
+// ReLU as one integer max on the float's bits: a set sign bit (negative
+// values and -0) makes the word negative, so max(bits, 0) gives +0; any other
+// value is returned unchanged.  Unlike fmaxf it needs no NaN canonicalisation.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 template <int H_I, int D_I>
 struct KeyFrag;
 
@@ -92,7 +97,7 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void indexer_kernel(const uint8_t* 
   if (wg_base > p) return;
   const int b = seq_id[t];
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int n = lane & 15;
   const int g = lane >> 4;
 
@@ -122,30 +127,44 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void indexer_kernel(const uint8_t* 
     __syncthreads();
   }
 
-#pragma unroll
-  for (int it = 0; it < IDX_ITERS; ++it) {
-    const int base = wg_base + (it * IDX_WAVES + wid) * 64;  // 64-aligned: one page when paged
-    if (base > p) break;
-    const int64_t row0 = token_row(lay, b, base);
-    // keys of the four N tiles; positions past p are clamped to p (not stored)
-    Frag kb[4];
+  // Groups of 64 keys this wave handles: base(it) = first + it*WAVES*64.
+  // Every group is loaded (groups past p re-read the group holding p, and
+  // store nothing), so the number of loads in flight is the same on every
+  // path and the next group's keys stay in flight while this one is reduced.
+  const int first = wg_base + wid * 64;
+  const int last_group = p & ~63;  // 64-aligned group holding position p
+  Frag kb[2][4];
+  int64_t row0[2];
+  auto issue = [&](int it, int slot) {
+    const int base = min(first + it * IDX_WAVES * 64, last_group);  // one page when paged
+    row0[slot] = token_row(lay, b, base);
+    const uint8_t* grp = k8 + row0[slot] * D_I;  // wave-uniform base of the 64 rows
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int s = min(base + 16 * j + n, p);
-      kb[j].load(k8 + (row0 + (s - base)) * D_I, g);
+      const int s = min(base + 16 * j + n, p);  // positions past p read p
+      kb[slot][j].load(grp + (u32)(s - base) * D_I, g);
     }
+  };
+  issue(0, 0);
+#pragma unroll
+  for (int it = 0; it < IDX_ITERS; ++it) {
+    const int cur = it & 1;
+    if (it + 1 < IDX_ITERS) issue(it + 1, cur ^ 1);
+    const int base = first + it * IDX_WAVES * 64;
+    const int base_c = min(base, last_group);
     const int s_me = base + lane;
-    const float ksv = ks[row0 + (min(s_me, p) - base)];
+    const float ksv = ks[row0[cur] + (min(base_c + lane, p) - base_c)];
     float res = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      v4f acc[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = Frag::mma(qa[mt], kb[cur][j]);
       float part = 0.f;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const v4f acc = Frag::mma(qa[mt], kb[j]);
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) part += wv[mt][i] * fmaxf(acc[i], 0.f);
-      }
+        for (int i = 0; i < 4; ++i) part += wv[mt][i] * relu(acc[mt][i]);
       part += __shfl_xor(part, 16, 64);
       part += __shfl_xor(part, 32, 64);
       if (g == j) res = part;  // lane 16j+n keeps key base+16j+n = base+lane
