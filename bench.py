@@ -6,6 +6,13 @@ of 131072 tokens, one query token each, 64x128 FP8 indexer, 128 heads over
 576-wide latent rows, 2% planted far keys.  Inputs are synthetic, seeded and
 resident in HBM before timing starts.
 
+Cache state.  A decoding model runs this step once per layer, each layer over
+its own caches, so a layer's keys are never in L2 or the 256 MB MALL when its
+step starts.  The benchmark reproduces that with REPLICAS copies of the
+per-layer tensors (index keys, latent KV, queries) used in rotation: between
+two uses of one copy, the others stream several GB through the caches.  The
+steps run back to back on one stream, as a model's layers do.
+
 Prints one JSON line.  `roofline` covers the dominant kernel (the indexer,
 bound by HBM), timed with HIP events on the stream it runs on; `cpu_baseline`
 times the float64 CPU oracle on a bounded sample of the same workload.
@@ -14,6 +21,8 @@ times the float64 CPU oracle on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +35,30 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5033.0
 BF16_PEAK_TFLOPS = 2517.0
+REPLICAS = 4
+
+# HBM traffic of one indexer launch on the 128K decode batch, from two
+# rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) over this script with
+# --copy-calibration, each scaled by counter/true bytes of a plain 256 MiB
+# device copy in the same pass.  Valid only for the kernel sources they were
+# taken on (hash below); otherwise the field is reported as null.
+TRAFFIC = {
+    "sources_sha256": "f42f4ef51a1620814c3a99f29b1f2cdebe30b31ed4e15cf7cd7db7ace65fabb0",
+    # FETCH_SIZE 135758.0 KiB/launch x 1.99982 (copy: 131083.9 KiB counted for 262144 KiB read)
+    "fetch_bytes": 278007103,
+    # WRITE_SIZE 8192.0 KiB/launch x 1.0 (copy: 262144 KiB counted for 262144 KiB written)
+    "write_bytes": 8388608,
+}
+TRAFFIC_SOURCES = ("sparse_attention_long_03_amd/csrc/indexer.hip", "sparse_attention_long_03_amd/csrc/common.h",
+                   "sparse_attention_long_03_amd/csrc/launch.h")
+
+
+def sources_hash():
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def parse():
@@ -36,11 +69,20 @@ def parse():
     ap.add_argument("--config", default="decode128k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run plain 256 MiB device copies (reference dispatches for HBM counters)")
     return ap.parse_args()
 
 
 def algorithmic_bytes(x):
-    """Bytes the method must move per forward, per kernel (see DESIGN)."""
+    """Bytes (and flops) the method must move per forward, per kernel.
+
+    indexer: per visible (query, key) pair the FP8 key row and its scale are
+    read and one fp32 logit is written; per query the FP8 query, its scale and
+    the head weights are read.  top-k: the logits are read and k indices
+    written.  attention: per selected row the 576 bf16 latent values and the
+    index are read; per query the 128x576 bf16 query is read and the 128x512
+    bf16 output written."""
     c = x.cfg
     n = (x.pos.long() + 1).sum().item()                      # visible (query, key) pairs
     T = x.T
@@ -54,32 +96,24 @@ def algorithmic_bytes(x):
                 indexer_flops=idx_flops, attn_flops=attn_flops)
 
 
-class Flusher:
-    """Evicts L2 and the 256 MB MALL between timed launches by reading a
-    1 GB buffer (4x the MALL), so no launch reads data that a previous launch
-    left in cache -- a serving loop interleaves many layers' caches between
-    two uses of one layer's.  A read is used, not a fill: a fill would leave
-    the MALL full of dirty lines whose write-back the next launch would pay."""
-
-    def __init__(self, nbytes=1 << 30):
-        import torch
-        self.buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
-
-    def __call__(self):
-        self.buf.sum()
+def replicas(x, n):
+    """n copies of the per-layer tensors (same values, distinct memory)."""
+    out = [x]
+    for _ in range(n - 1):
+        out.append(dataclasses.replace(x, iq8=x.iq8.clone(), iqs=x.iqs.clone(), iw=x.iw.clone(), q=x.q.clone(),
+                                       ik8=x.ik8.clone(), iks=x.iks.clone(), kv=x.kv.clone()))
+    return out
 
 
-def timed_launches(fn, n, stream, flush=None):
-    """Per-launch durations (ms) from HIP events recorded on `stream` around
-    each call; `flush` (if any) runs between launches, outside the events."""
+def timed_rotation(fns, n, stream):
+    """Runs fns[i % len(fns)] for i < n back to back on `stream`; returns the
+    per-launch durations (ms) from HIP events recorded around each call."""
     import torch
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
     torch.cuda.synchronize()
-    for a, b in evs:
-        if flush is not None:
-            flush()
+    for i, (a, b) in enumerate(evs):
         a.record(stream)
-        fn()
+        fns[i % len(fns)]()
         b.record(stream)
     torch.cuda.synchronize()
     return [a.elapsed_time(b) for a, b in evs]
@@ -89,8 +123,13 @@ def mean(xs):
     return sum(xs) / len(xs)
 
 
+def median(xs):
+    return sorted(xs)[len(xs) // 2]
+
+
 def cpu_baseline(x, budget_s):
-    """Float64 oracle on host cores, one query at a time until the budget is spent."""
+    """Float64 oracle on host cores, one query at a time (cycling over the
+    batch) until the time budget is spent."""
     import numpy as np
     import oracle as O
     from sparse_attention_long_03_amd import inputs as I
@@ -100,29 +139,37 @@ def cpu_baseline(x, budget_s):
     except Exception:
         cores = 1
     c = x.cfg
-    done = 0
-    dt = 0.0
-    for t in range(x.T):
-        # host copies of this query's inputs (not timed)
+    host = []
+    for t in range(x.T):  # host copies of every query's inputs (not timed)
         b = int(x.seq_id[t])
         n = int(x.pos[t]) + 1
-        q8, qs = x.iq8[t].cpu().numpy(), float(x.iqs[t])
-        w = x.iw[t].cpu().numpy().astype(np.float64)
-        k8 = x.ik8[b, :n].cpu().numpy()
-        ks = x.iks[b, :n].cpu().numpy().astype(np.float64)
-        kv = I.bf16_bits(x.kv[b, :n])
-        q = I.bf16_bits(x.q[t:t + 1])
+        host.append((n, x.iq8[t].cpu().numpy(), float(x.iqs[t]), x.iw[t].cpu().numpy().astype(np.float64),
+                     x.ik8[b, :n].cpu().numpy(), x.iks[b, :n].cpu().numpy().astype(np.float64),
+                     I.bf16_bits(x.kv[b, :n])[None], I.bf16_bits(x.q[t:t + 1])))
+    done = 0
+    dt = 0.0
+    while dt <= budget_s:
+        n, q8, qs, w, k8, ks, kv, q = host[done % x.T]
         ts = time.perf_counter()
         lg = O.indexer_logits_row(q8, qs, w, k8, ks)
         sel = O.topk_select(lg.astype(np.float32), n, c.k)
-        O.sparse_mla_attention(q, kv[None], sel[None], np.zeros(1, int), c.scale, c.d_v)
+        O.sparse_mla_attention(q, kv, sel[None], np.zeros(1, int), c.scale, c.d_v)
         dt += time.perf_counter() - ts
         done += 1
-        if dt > budget_s:
-            break
-    return {"value": done / dt, "unit": "queries/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} of {x.T} queries of the same workload (full 131072-key rows), float64 NumPy oracle, "
-                      f"{dt:.1f} s"}
+    return {"value": round(done / dt, 3), "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} queries of the same workload, cycling over its {x.T} full-length query rows "
+                      f"(indexer over all {x.max_len} keys, top-k, attention), float64 NumPy oracle, {dt:.1f} s"}
+
+
+def workload_name(cfg):
+    if cfg.kind == "decode":
+        return (f"{cfg.name}: decode, B={cfg.B} sequences x L={cfg.L} tokens, 1 query token each, indexer "
+                f"{cfg.H_I}x{cfg.D_I} FP8, top-k={cfg.k}, MLA-MQA {cfg.H} heads x 576 (512+64 rope)"
+                + (f", {cfg.planted_frac:.0%} planted far keys" if cfg.planted_frac > 0 else ""))
+    if cfg.kind == "ragged":
+        return (f"{cfg.name}: B={cfg.B} sequences, lengths uniform in [{cfg.min_len},{cfg.L}], paged KV "
+                f"(page {cfg.page_size}), 1-2 query tokens each, top-k={cfg.k}")
+    return cfg.name
 
 
 def main():
@@ -138,34 +185,61 @@ def main():
 
     torch.cuda.set_device(0)
     cfg = I.CONFIGS[args.config]
-    x = I.make_inputs(cfg, "cuda")
-    p = DSAPath(x)
+    if cfg.kind == "prefill":
+        print(json.dumps({"error": "the prefill configuration is not benchmarked by this script"}))
+        sys.exit(2)
+    x0 = I.make_inputs(cfg, "cuda")
+    xs = replicas(x0, REPLICAS)
+    paths = [DSAPath(x) for x in xs]
+    for p in paths[1:]:
+        p._ws = paths[0]._ws  # one workspace, as in a model's layer loop
+    for p in paths:
+        p.ws(B.DSA_OP_FORWARD)
     stream = torch.cuda.current_stream()
+    fwd = [p.forward for p in paths]
     torch.cuda.synchronize()
 
-    flush = Flusher()
-    # warmup, then the timed steps: one dsa_forward each, caches flushed before
-    # every step so that no step reads what the previous one left in L2/MALL
-    timed_launches(p.forward, args.warmup, stream, flush)
-    step_ms = timed_launches(p.forward, args.steps, stream, flush)
-    ms = mean(step_ms)
+    # warmup, then exactly `steps` dsa_forward calls back to back (wall clock
+    # between two synchronisations; per-step HIP events alongside)
+    for i in range(args.warmup):
+        fwd[i % REPLICAS]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        fwd[i % REPLICAS]()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
 
     # per-kernel launches, same launch configuration as inside dsa_forward
-    logits = p.new_logits()
-    idx = torch.empty((x.T, cfg.k), dtype=torch.int32, device="cuda")
-    topk_ws = B.workspace(B.dsa_workspace_bytes(B.DSA_OP_TOPK, x.T, logits.shape[1], 0, cfg.k))
-    timed_launches(lambda: p.indexer(logits), 1, stream, flush)
-    timed_launches(lambda: B.dsa_topk(logits, p.valid_len, logits.shape[1], cfg.k, idx, topk_ws), 1, stream, flush)
     n_launch = max(args.steps, 20)
-    idx_ts = timed_launches(lambda: p.indexer(logits), n_launch, stream, flush)
-    idx_avg, idx_med = mean(idx_ts), sorted(idx_ts)[len(idx_ts) // 2]
-    topk_avg = mean(timed_launches(lambda: B.dsa_topk(logits, p.valid_len, logits.shape[1], cfg.k, idx, topk_ws),
-                                   n_launch, stream, flush))
-    attn_avg = mean(timed_launches(lambda: p.attn(idx), n_launch, stream, flush))
+    logits = [p.new_logits() for p in paths]
+    idx = torch.empty((x0.T, cfg.k), dtype=torch.int32, device="cuda")
+    topk_ws = B.workspace(B.dsa_workspace_bytes(B.DSA_OP_TOPK, x0.T, logits[0].shape[1], 0, cfg.k))
+    idx_fns = [(lambda p=p, lg=lg: p.indexer(lg)) for p, lg in zip(paths, logits)]
+    topk_fns = [(lambda p=p, lg=lg: B.dsa_topk(lg, p.valid_len, lg.shape[1], cfg.k, idx, topk_ws))
+                for p, lg in zip(paths, logits)]
+    attn_fns = [(lambda p=p: p.attn(p.idx)) for p in paths]
+    timed_rotation(idx_fns + topk_fns + attn_fns, 3 * REPLICAS, stream)  # warm every launch path
+    idx_ts = timed_rotation(idx_fns, n_launch, stream)
+    topk_ts = timed_rotation(topk_fns, n_launch, stream)
+    attn_ts = timed_rotation(attn_fns, n_launch, stream)
+    step_ts = timed_rotation(fwd, n_launch, stream)
+    idx_avg, topk_avg, attn_avg = mean(idx_ts), mean(topk_ts), mean(attn_ts)
 
-    ab = algorithmic_bytes(x)
+    if args.copy_calibration:
+        src = torch.ones(1 << 26, dtype=torch.int32, device="cuda")  # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    ab = algorithmic_bytes(x0)
     idx_gbs = ab["indexer"] / (idx_avg * 1e-3) / 1e9
-    value = x.T / (ms * 1e-3)
+    value = x0.T / (wall_ms * 1e-3)
+    traffic = None
+    if TRAFFIC["sources_sha256"] is not None and TRAFFIC["sources_sha256"] == sources_hash() \
+            and cfg.name == "decode128k":
+        traffic = TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
     out = {
         "metric": "DSA decode queries/s @128K ctx, k=2048 (+indexer TFLOP/s, sparse-attn GB/s)",
         "value": round(value, 1),
@@ -173,21 +247,18 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": round(wall_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8-e4m3 indexer / bf16 attention, fp32 accumulate",
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: long-context decode, B={cfg.B} sequences x L={cfg.L} tokens, 1 query "
-                               f"token each, indexer {cfg.H_I}x{cfg.D_I} FP8, top-k={cfg.k}, MLA-MQA {cfg.H} heads "
-                               f"x 576 (512+64 rope), 2% planted far keys" if cfg.name == "decode128k" else cfg.name,
-                   "B": cfg.B, "L": cfg.L, "T": x.T, "k": cfg.k, "H_I": cfg.H_I, "D_I": cfg.D_I, "H": cfg.H,
-                   "paged": cfg.paged},
-        "roofline": {"bound": "hbm", "kernel": "indexer_kernel<64,128>", "achieved": round(idx_gbs, 1),
+        "config": {"workload": workload_name(cfg), "B": cfg.B, "L": cfg.L, "T": x0.T, "k": cfg.k, "H_I": cfg.H_I,
+                   "D_I": cfg.D_I, "H": cfg.H, "paged": cfg.paged},
+        "roofline": {"bound": "hbm", "kernel": f"indexer_kernel<{cfg.H_I},{cfg.D_I}>", "achieved": round(idx_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(idx_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": ab["indexer"], "avg_launch_us": round(idx_avg * 1e3, 2),
-                     "median_launch_us": round(idx_med * 1e3, 2)},
+                     "traffic": traffic, "bytes_per_launch": ab["indexer"],
+                     "avg_launch_us": round(idx_avg * 1e3, 2), "median_launch_us": round(median(idx_ts) * 1e3, 2)},
         "kernels": {
             "indexer_us": round(idx_avg * 1e3, 2),
             "indexer_tflops": round(ab["indexer_flops"] / (idx_avg * 1e-3) / 1e12, 2),
@@ -196,11 +267,11 @@ def main():
             "attn_us": round(attn_avg * 1e3, 2),
             "attn_gbs": round(ab["attn"] / (attn_avg * 1e-3) / 1e9, 1),
             "attn_tflops": round(ab["attn_flops"] / (attn_avg * 1e-3) / 1e12, 2),
-            "sum_of_kernels_us": round((idx_avg + topk_avg + attn_avg) * 1e3, 2),
+            "forward_event_us": round(mean(step_ts) * 1e3, 2),
         },
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(x0, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
