@@ -120,6 +120,33 @@ int dsa_topk(const float* logits, int64_t ld_logits, const int32_t* valid_len, i
              int32_t k, int32_t* idx, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * (1) + (2) fused, for batches with many query tokens (prefill): idx[t, :]
+ * receives exactly what dsa_indexer_logits followed by dsa_topk (valid length
+ * pos[t] + 1) would give, but the logits are consumed as they are produced
+ * and never stored.  Query tokens are taken 8 at a time; consecutive tokens
+ * of one sequence share their key reads, so the call suits prefill-like
+ * batches (a few thousand tokens or more); a decode batch is better served by
+ * the two separate calls.
+ *
+ *   arguments : as for dsa_indexer_logits; k as for dsa_topk;
+ *   idx       : device int32[T, k], positions in a deterministic order that
+ *               is not sorted by value (rows with pos[t] + 1 <= k: all
+ *               positions ascending, then -1)
+ *   workspace : device, 256-byte aligned; it holds a candidate list of `cap`
+ *               slots (8 bytes each) per query token, with cap = the largest
+ *               multiple of 64 not above 8192 that fits workspace_bytes / T;
+ *               cap >= k + 128 is required (DSA_ERR_WORKSPACE otherwise).
+ *               A smaller cap gives the same result with more work;
+ *               dsa_workspace_bytes(DSA_OP_INDEXER_TOPK, T, max_len, 0, k) is
+ *               the size at which no list ever needs compacting for rows up
+ *               to about 8K positions.
+ * ------------------------------------------------------------------------- */
+int dsa_indexer_topk(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,
+                     const uint8_t* q_fp8, const float* q_scale, const float* w, const uint8_t* k_fp8,
+                     const float* k_scale, int32_t k, int32_t* idx, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * (3) Sparse attention under MLA in MQA mode ("... Sparse Consideration
  * (DSA)", parts (2) and "Instantiation").  For query t, head h and the
  * selected positions i = idx[t, j] != -1 of sequence seq_id[t]:
@@ -144,7 +171,10 @@ int dsa_sparse_mla_attn(const dsa_queries* q, const dsa_kv_layout* layout, int32
 /* ---------------------------------------------------------------------------
  * (1) -> (2) -> (3) on one stream ("FP8 index -> top-k selection -> sparse
  * core attention").  Arguments as above; idx_out (device int32[T, k]) receives
- * the selection, or may be NULL to keep it inside the workspace.
+ * the selection, or may be NULL to keep it inside the workspace.  With
+ * T >= 2048 query tokens, (1) and (2) run fused as in dsa_indexer_topk (no
+ * logits in memory); below that they run as dsa_indexer_logits + dsa_topk.
+ * The selection is the same either way.
  *   workspace : device, >= dsa_workspace_bytes(DSA_OP_FORWARD, T, max_len, H, k)
  * ------------------------------------------------------------------------- */
 int dsa_forward(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,
@@ -157,6 +187,7 @@ int dsa_forward(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, 
 #define DSA_OP_TOPK 1
 #define DSA_OP_ATTN 2
 #define DSA_OP_FORWARD 3
+#define DSA_OP_INDEXER_TOPK 4
 size_t dsa_workspace_bytes(int32_t op, int32_t T, int32_t max_len, int32_t H, int32_t k);
 
 /* Static string for a status code (never NULL). */

@@ -22,7 +22,7 @@ DSA_ERR_INVALID_ARG = -1
 DSA_ERR_UNSUPPORTED = -2
 DSA_ERR_WORKSPACE = -3
 DSA_ERR_HIP = -4
-DSA_OP_TOPK, DSA_OP_ATTN, DSA_OP_FORWARD = 1, 2, 3
+DSA_OP_TOPK, DSA_OP_ATTN, DSA_OP_FORWARD, DSA_OP_INDEXER_TOPK = 1, 2, 3, 4
 
 
 class DSAError(RuntimeError):
@@ -41,8 +41,8 @@ class dsa_kv_layout(ctypes.Structure):
                 ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("seq_capacity", ctypes.c_int64)]
 
 
-EXPORTS = ("dsa_indexer_logits", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward", "dsa_workspace_bytes",
-           "dsa_status_str", "dsa_abi_version")
+EXPORTS = ("dsa_indexer_logits", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward",
+           "dsa_workspace_bytes", "dsa_status_str", "dsa_abi_version")
 
 _lib = None
 
@@ -58,6 +58,7 @@ def lib() -> ctypes.CDLL:
     vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
     Q, KV = ctypes.POINTER(dsa_queries), ctypes.POINTER(dsa_kv_layout)
     L.dsa_indexer_logits.argtypes = [Q, KV, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp]
+    L.dsa_indexer_topk.argtypes = [Q, KV, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
     L.dsa_topk.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp, sz, vp]
     L.dsa_sparse_mla_attn.argtypes = [Q, KV, i32, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
     L.dsa_forward.argtypes = [Q, KV, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]
@@ -66,7 +67,7 @@ def lib() -> ctypes.CDLL:
     L.dsa_status_str.argtypes = [i32]
     L.dsa_status_str.restype = ctypes.c_char_p
     L.dsa_abi_version.restype = i32
-    for name in ("dsa_indexer_logits", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward"):
+    for name in ("dsa_indexer_logits", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -140,6 +141,14 @@ def dsa_indexer_logits(q: dsa_queries, layout: dsa_kv_layout, H_I: int, D_I: int
     st = lib().dsa_indexer_logits(ctypes.byref(q), ctypes.byref(layout), H_I, D_I, _ptr(q_fp8), _ptr(q_scale), _ptr(w),
                                   _ptr(k_fp8), _ptr(k_scale), _ptr(logits), int(logits.shape[-1]), _stream(stream))
     _check(st, "dsa_indexer_logits")
+
+
+def dsa_indexer_topk(q: dsa_queries, layout: dsa_kv_layout, H_I: int, D_I: int, q_fp8, q_scale, w, k_fp8, k_scale,
+                     k: int, idx: torch.Tensor, ws: torch.Tensor, stream=None):
+    st = lib().dsa_indexer_topk(ctypes.byref(q), ctypes.byref(layout), H_I, D_I, _ptr(q_fp8), _ptr(q_scale), _ptr(w),
+                                _ptr(k_fp8), _ptr(k_scale), int(k), _ptr(idx), _ptr(ws), ws.numel() * ws.element_size(),
+                                _stream(stream))
+    _check(st, "dsa_indexer_topk")
 
 
 def dsa_topk(logits: torch.Tensor, valid_len: torch.Tensor, max_len: int, k: int, idx: torch.Tensor,

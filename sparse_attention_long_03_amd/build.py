@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
-SOURCES = ["abi.hip", "indexer.hip", "topk.hip", "sparse_mla.hip"]
+SOURCES = ["abi.hip", "indexer.hip", "indexer_topk.hip", "topk.hip", "sparse_mla.hip"]
 ARCH = "gfx950"
 
 
@@ -40,7 +40,7 @@ def _flags():
 
 # Per-file code-generation options.  The indexer reads its MFMA results with
 # VALU code, so it asks for the VGPR form of the MFMAs (no AGPR round trips).
-EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "indexer_topk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

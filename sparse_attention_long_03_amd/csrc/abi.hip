@@ -39,26 +39,48 @@ int check_layout(const dsa_kv_layout* l, const dsa_queries* q, Layout* out) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
 
+// dsa_forward selects from the logits as they are produced (no logits
+// buffer) once the batch has this many query tokens: enough workgroups of 8
+// tokens to fill the chip, and the row-per-token logits would be large.
+constexpr int32_t kFusedMinT = 2048;
+
+bool forward_fused(int32_t T) { return T >= kFusedMinT; }
+
 size_t forward_ws(int32_t T, int32_t max_len, int32_t H, int32_t k, bool with_idx) {
   const int64_t ld = ((int64_t)max_len + 3) & ~int64_t(3);
-  size_t s = align256((size_t)T * ld * 4);              // logits
+  size_t s = 0;
   if (with_idx) s += align256((size_t)T * k * 4);       // selection
-  s += topk_workspace_bytes(T, ld, k);
+  if (forward_fused(T)) {
+    s += align256(fused_topk_workspace_bytes(T, fused_topk_cap(max_len, k)));
+  } else {
+    s += align256((size_t)T * ld * 4);                  // logits
+    s += topk_workspace_bytes(T, ld, k);
+  }
   s += align256(attn_workspace_bytes(T, H, k));
   return s;
 }
 
-int validate_indexer(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,
-                     const uint8_t* q_fp8, const float* q_scale, const float* w, const uint8_t* k_fp8,
-                     const float* k_scale, const float* logits, int64_t ld, Layout* lay) {
+// the indexer's inputs (shared by the logits and the fused selection calls)
+int validate_indexer_inputs(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,
+                            const uint8_t* q_fp8, const float* q_scale, const float* w, const uint8_t* k_fp8,
+                            const float* k_scale, Layout* lay) {
   int st = check_queries(q);
   if (st) return st;
   if ((st = check_layout(layout, q, lay))) return st;
   if (H_I < 1 || D_I < 1) return DSA_ERR_INVALID_ARG;
   if (!indexer_supported(H_I, D_I)) return DSA_ERR_UNSUPPORTED;
   if (q->T == 0) return DSA_OK;
-  if (!q_fp8 || !q_scale || !w || !k_fp8 || !k_scale || !logits) return DSA_ERR_INVALID_ARG;
-  if (!aligned(q_fp8, 16) || !aligned(k_fp8, 16) || !aligned(logits, 16)) return DSA_ERR_INVALID_ARG;
+  if (!q_fp8 || !q_scale || !w || !k_fp8 || !k_scale) return DSA_ERR_INVALID_ARG;
+  if (!aligned(q_fp8, 16) || !aligned(k_fp8, 16)) return DSA_ERR_INVALID_ARG;
+  return DSA_OK;
+}
+
+int validate_indexer(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,
+                     const uint8_t* q_fp8, const float* q_scale, const float* w, const uint8_t* k_fp8,
+                     const float* k_scale, const float* logits, int64_t ld, Layout* lay) {
+  int st = validate_indexer_inputs(q, layout, H_I, D_I, q_fp8, q_scale, w, k_fp8, k_scale, lay);
+  if (st || q->T == 0) return st;
+  if (!logits || !aligned(logits, 16)) return DSA_ERR_INVALID_ARG;
   if (ld < q->max_len || (ld & 3)) return DSA_ERR_INVALID_ARG;
   return DSA_OK;
 }
@@ -101,6 +123,7 @@ size_t dsa_workspace_bytes(int32_t op, int32_t T, int32_t max_len, int32_t H, in
     case DSA_OP_TOPK: return (k > 0) ? topk_workspace_bytes(T, ld, k) : 0;
     case DSA_OP_ATTN: return (H > 0 && k > 0) ? attn_workspace_bytes(T, H, k) : 0;
     case DSA_OP_FORWARD: return (H > 0 && k > 0) ? forward_ws(T, max_len, H, k, true) : 0;
+    case DSA_OP_INDEXER_TOPK: return (k > 0) ? fused_topk_workspace_bytes(T, fused_topk_cap(max_len, k)) : 0;
     default: return 0;
   }
 }
@@ -113,6 +136,23 @@ int dsa_indexer_logits(const dsa_queries* q, const dsa_kv_layout* layout, int32_
   if (st || q->T == 0) return st;
   return hip_status(launch_indexer(q->T, q->max_len, H_I, D_I, q_fp8, q_scale, w, k_fp8, k_scale, q->seq_id, q->pos,
                                    lay, logits, ld_logits, nullptr, stream));
+}
+
+int dsa_indexer_topk(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,
+                     const uint8_t* q_fp8, const float* q_scale, const float* w, const uint8_t* k_fp8,
+                     const float* k_scale, int32_t k, int32_t* idx, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  Layout lay;
+  int st = validate_indexer_inputs(q, layout, H_I, D_I, q_fp8, q_scale, w, k_fp8, k_scale, &lay);
+  if (st) return st;
+  if (k < 1) return DSA_ERR_INVALID_ARG;
+  if (k > kMaxK) return DSA_ERR_UNSUPPORTED;
+  if (q->T == 0) return DSA_OK;
+  if (idx == nullptr) return DSA_ERR_INVALID_ARG;
+  const int cap = fused_topk_cap_from_bytes(q->T, workspace_bytes);
+  if (workspace == nullptr || !aligned(workspace, 256) || !fused_topk_cap_ok(cap, k)) return DSA_ERR_WORKSPACE;
+  return hip_status(launch_indexer_topk(q->T, H_I, D_I, q_fp8, q_scale, w, k_fp8, k_scale, q->seq_id, q->pos, lay, k,
+                                        cap, idx, workspace, stream));
 }
 
 int dsa_topk(const float* logits, int64_t ld_logits, const int32_t* valid_len, int32_t T, int32_t max_len,
@@ -164,24 +204,34 @@ int dsa_forward(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, 
   if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)) return DSA_ERR_WORKSPACE;
 
   char* p = static_cast<char*>(workspace);
-  float* logits = reinterpret_cast<float*>(p);
-  p += align256((size_t)q->T * ld * 4);
   int32_t* idx = idx_out;
   if (idx == nullptr) {
     idx = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)q->T * k * 4);
   }
-  void* ws_topk = p;
-  p += topk_workspace_bytes(q->T, ld, k);
+  hipError_t e;
+  if (forward_fused(q->T)) {
+    // many query tokens: indexer and selection in one pass, no logits stored
+    const int cap = fused_topk_cap(q->max_len, k);
+    void* ws_sel = p;
+    p += align256(fused_topk_workspace_bytes(q->T, cap));
+    e = launch_indexer_topk(q->T, H_I, D_I, iq_fp8, iq_scale, iw, ik_fp8, ik_scale, q->seq_id, q->pos, lay, k, cap,
+                            idx, ws_sel, stream);
+    if (e != hipSuccess) return DSA_ERR_HIP;
+  } else {
+    float* logits = reinterpret_cast<float*>(p);
+    p += align256((size_t)q->T * ld * 4);
+    void* ws_topk = p;
+    p += topk_workspace_bytes(q->T, ld, k);
+    e = launch_topk_zero_hist(ws_topk, q->T, stream);
+    if (e != hipSuccess) return DSA_ERR_HIP;
+    e = launch_indexer(q->T, q->max_len, H_I, D_I, iq_fp8, iq_scale, iw, ik_fp8, ik_scale, q->seq_id, q->pos, lay,
+                       logits, ld, topk_hist_buffer(ws_topk), stream);
+    if (e != hipSuccess) return DSA_ERR_HIP;
+    e = launch_topk(logits, ld, q->pos, 1, q->T, q->max_len, k, idx, ws_topk, true, stream);
+    if (e != hipSuccess) return DSA_ERR_HIP;
+  }
   void* ws_attn = p;
-
-  hipError_t e = launch_topk_zero_hist(ws_topk, q->T, stream);
-  if (e != hipSuccess) return DSA_ERR_HIP;
-  e = launch_indexer(q->T, q->max_len, H_I, D_I, iq_fp8, iq_scale, iw, ik_fp8, ik_scale, q->seq_id, q->pos, lay,
-                     logits, ld, topk_hist_buffer(ws_topk), stream);
-  if (e != hipSuccess) return DSA_ERR_HIP;
-  e = launch_topk(logits, ld, q->pos, 1, q->T, q->max_len, k, idx, ws_topk, true, stream);
-  if (e != hipSuccess) return DSA_ERR_HIP;
   e = launch_attn(q->T, H, static_cast<const uint16_t*>(q_bf16), static_cast<const uint16_t*>(kv_bf16), idx, q->seq_id,
                   lay, k, sm_scale, static_cast<uint16_t*>(out_bf16), lse, ws_attn, stream);
   return hip_status(e);

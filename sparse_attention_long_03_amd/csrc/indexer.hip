@@ -1,21 +1,9 @@
 // Lightning indexer logits on gfx950 FP8 matrix cores.
 //
 // "DeepSeek V3.2-Exp Cuts Prolonged-Context Costs With DeepSeek Sparse
-// Consideration (DSA)", part (1): per query token, a few small FP8 indexer
-// heads with a ReLU score every earlier token.  Computed here:
-//   I[t,s] = qs[t] * ks[s] * sum_j w[t,j] * ReLU(q8[t,j,:] . k8[s,:])
-//
-// Mapping.  One query token's heads form the M side of the MFMA (16 heads per
-// M tile), keys form N (16 keys per N tile) and the head dim is K, so one
-// v_mfma_f32_16x16x128_f8f6f4 computes 16 heads x 16 keys of dot products
-// (D_I = 128; D_I = 64 uses two 16x16x32 fp8 MFMAs).  In the 16x16 result a
-// lane holds one key (column) and four heads (rows), so the ReLU and the
-// per-head weights are applied in registers, and the sum over heads needs
-// only two cross-lane steps (lanes n, n+16, n+32, n+48).
-//
-// Each lane group g (lanes 16g..16g+15) feeds the same byte range of the head
-// dim for both operands; the contraction is a plain sum over the K index, so
-// any consistent assignment of bytes to K slots gives the same result.
+// Consideration (DSA)", part (1).  The per-tile arithmetic (heads on the MFMA
+// M side, keys on N, ReLU and head weights in registers) lives in
+// indexer_math.h; this kernel streams the keys and writes the logits.
 //
 // Decode is bound by HBM (one 128-byte key row feeds 64 heads x 128 MACs =
 // 128 flop/byte, far under the FP8 ridge), so the kernel streams keys with
@@ -25,6 +13,7 @@
 // stored logit's order-preserving key into a per-row 2048-bin histogram (LDS
 // per workgroup, then one global atomic per non-empty bin): the first level
 // of the top-k radix select, obtained without reading the logits again.
+#include "indexer_math.h"
 #include "launch.h"
 
 namespace dsa {
@@ -32,50 +21,6 @@ namespace dsa {
 constexpr int IDX_WAVES = 4;
 constexpr int IDX_ITERS = 4;                                    // 64-key groups per wave
 constexpr int IDX_KEYS_PER_WG = IDX_WAVES * IDX_ITERS * 64;     // 1024 keys per workgroup
-
-// ReLU as one integer max on the float's bits: a set sign bit (negative
-// values and -0) makes the word negative, so max(bits, 0) gives +0; any other
-// value is returned unchanged.  Unlike fmaxf it needs no NaN canonicalisation.
-__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
-
-template <int H_I, int D_I>
-struct KeyFrag;
-
-// D_I = 128: 32 bytes per lane (one f8f6f4 MFMA)
-template <int H_I>
-struct KeyFrag<H_I, 128> {
-  v8i v;
-  __device__ __forceinline__ void load(const uint8_t* row_base, int g) {
-    const v4i* p = reinterpret_cast<const v4i*>(row_base + 32 * g);
-    v4i a = p[0], b = p[1];
-    v = v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  }
-  __device__ __forceinline__ void zero() { v = v8i{0, 0, 0, 0, 0, 0, 0, 0}; }
-  __device__ __forceinline__ static v4f mma(const KeyFrag& a, const KeyFrag& b) {
-    v4f c = {0.f, 0.f, 0.f, 0.f};
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a.v, b.v, c, 0, 0, 0, 0, 0, 0);
-  }
-};
-
-// D_I = 64: 16 bytes per lane (two 16x16x32 fp8 MFMAs)
-template <int H_I>
-struct KeyFrag<H_I, 64> {
-  v4i v;
-  __device__ __forceinline__ void load(const uint8_t* row_base, int g) {
-    v = *reinterpret_cast<const v4i*>(row_base + 16 * g);
-  }
-  __device__ __forceinline__ void zero() { v = v4i{0, 0, 0, 0}; }
-  __device__ __forceinline__ static v4f mma(const KeyFrag& a, const KeyFrag& b) {
-    v4f c = {0.f, 0.f, 0.f, 0.f};
-    long a0 = (long)(((unsigned long)(u32)a.v[1] << 32) | (u32)a.v[0]);
-    long a1 = (long)(((unsigned long)(u32)a.v[3] << 32) | (u32)a.v[2]);
-    long b0 = (long)(((unsigned long)(u32)b.v[1] << 32) | (u32)b.v[0]);
-    long b1 = (long)(((unsigned long)(u32)b.v[3] << 32) | (u32)b.v[2]);
-    c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a0, b0, c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a1, b1, c, 0, 0, 0);
-    return c;
-  }
-};
 
 template <int H_I, int D_I>
 __global__ __launch_bounds__(IDX_WAVES * 64) void indexer_kernel(const uint8_t* __restrict__ q8,
@@ -87,7 +32,6 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void indexer_kernel(const uint8_t* 
                                                                  const int32_t* __restrict__ pos, Layout lay,
                                                                  float* __restrict__ logits, int64_t ld,
                                                                  u32* __restrict__ hist) {
-  constexpr int MT = (H_I + 15) / 16;  // M tiles of 16 heads
   __shared__ u32 h_lds[2048];
   using Frag = KeyFrag<H_I, D_I>;
 
@@ -101,26 +45,8 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void indexer_kernel(const uint8_t* 
   const int n = lane & 15;
   const int g = lane >> 4;
 
-  // query operand: row = head mt*16 + n
-  Frag qa[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int h = mt * 16 + n;
-    if (h < H_I)
-      qa[mt].load(q8 + ((int64_t)t * H_I + h) * D_I, g);
-    else
-      qa[mt].zero();
-  }
-  // weights of the heads whose results this lane holds: mt*16 + 4g + i
-  float wv[MT][4];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = mt * 16 + 4 * g + i;
-      wv[mt][i] = (h < H_I) ? w[(int64_t)t * H_I + h] : 0.f;
-    }
-  const float qscale = qs[t];
+  IndexerQuery<H_I, D_I> qq;
+  qq.load(q8, qs, w, t, n, g);
   float* __restrict__ out_row = logits + (int64_t)t * ld;
   if (hist != nullptr) {
     for (int i = threadIdx.x; i < 2048; i += IDX_WAVES * 64) h_lds[i] = 0;
@@ -154,23 +80,9 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void indexer_kernel(const uint8_t* 
     const int base_c = min(base, last_group);
     const int s_me = base + lane;
     const float ksv = ks[row0[cur] + (min(base_c + lane, p) - base_c)];
-    float res = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v4f acc[MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = Frag::mma(qa[mt], kb[cur][j]);
-      float part = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) part += wv[mt][i] * relu(acc[mt][i]);
-      part += __shfl_xor(part, 16, 64);
-      part += __shfl_xor(part, 32, 64);
-      if (g == j) res = part;  // lane 16j+n keeps key base+16j+n = base+lane
-    }
+    const float res = group_scores<H_I, D_I>(qq, kb[cur], g);
     if (s_me <= p) {
-      const float v = (res * qscale) * ksv;
+      const float v = scaled_logit(res, qq.qscale, ksv);
       out_row[s_me] = v;
       if (hist != nullptr) atomicAdd(&h_lds[order_key(v) >> 21], 1u);
     }

@@ -1,0 +1,140 @@
+// Arithmetic of the lightning indexer on gfx950 FP8 matrix cores, shared by
+// the kernel that writes the logits and the kernel that selects from them on
+// the fly, so that both compute every logit with the same operations in the
+// same order (and therefore the same fp32 value).
+//
+// "DeepSeek V3.2-Exp Cuts Prolonged-Context Costs With DeepSeek Sparse
+// Consideration (DSA)", part (1): per query token, a few small FP8 indexer
+// heads with a ReLU score every earlier token:
+//   I[t,s] = qs[t] * ks[s] * sum_j w[t,j] * ReLU(q8[t,j,:] . k8[s,:])
+//
+// Mapping.  One query token's heads form the M side of the MFMA (16 heads per
+// M tile), keys form N (16 keys per N tile) and the head dim is K, so one
+// v_mfma_f32_16x16x128_f8f6f4 computes 16 heads x 16 keys of dot products
+// (D_I = 64 uses two 16x16x32 fp8 MFMAs).  In the 16x16 result a lane holds
+// one key (column) and four heads (rows), so the ReLU and the per-head
+// weights are applied in registers and the sum over heads needs only two
+// cross-lane steps (lanes n, n+16, n+32, n+48).
+//
+// Each lane group g (lanes 16g..16g+15) feeds the same byte range of the head
+// dim for both operands; the contraction is a plain sum over the K index, so
+// any consistent assignment of bytes to K slots gives the same result.
+#pragma once
+
+#include "common.h"
+
+namespace dsa {
+
+// ReLU as one integer max on the float's bits: a set sign bit (negative
+// values and -0) makes the word negative, so max(bits, 0) gives +0; any other
+// value is returned unchanged.  Unlike fmaxf it needs no NaN canonicalisation.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+template <int H_I, int D_I>
+struct KeyFrag;
+
+// D_I = 128: 32 bytes per lane (one f8f6f4 MFMA)
+template <int H_I>
+struct KeyFrag<H_I, 128> {
+  v8i v;
+  __device__ __forceinline__ void load(const uint8_t* row_base, int g) {
+    const v4i* p = reinterpret_cast<const v4i*>(row_base + 32 * g);
+    v4i a = p[0], b = p[1];
+    v = v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+  __device__ __forceinline__ void zero() { v = v8i{0, 0, 0, 0, 0, 0, 0, 0}; }
+  __device__ __forceinline__ static v4f mma(const KeyFrag& a, const KeyFrag& b) {
+    v4f c = {0.f, 0.f, 0.f, 0.f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a.v, b.v, c, 0, 0, 0, 0, 0, 0);
+  }
+};
+
+// D_I = 64: 16 bytes per lane (two 16x16x32 fp8 MFMAs)
+template <int H_I>
+struct KeyFrag<H_I, 64> {
+  v4i v;
+  __device__ __forceinline__ void load(const uint8_t* row_base, int g) {
+    v = *reinterpret_cast<const v4i*>(row_base + 16 * g);
+  }
+  __device__ __forceinline__ void zero() { v = v4i{0, 0, 0, 0}; }
+  __device__ __forceinline__ static v4f mma(const KeyFrag& a, const KeyFrag& b) {
+    v4f c = {0.f, 0.f, 0.f, 0.f};
+    long a0 = (long)(((unsigned long)(u32)a.v[1] << 32) | (u32)a.v[0]);
+    long a1 = (long)(((unsigned long)(u32)a.v[3] << 32) | (u32)a.v[2]);
+    long b0 = (long)(((unsigned long)(u32)b.v[1] << 32) | (u32)b.v[0]);
+    long b1 = (long)(((unsigned long)(u32)b.v[3] << 32) | (u32)b.v[2]);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a0, b0, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a1, b1, c, 0, 0, 0);
+    return c;
+  }
+};
+
+// The query side of one token in registers: its heads as MFMA A operands
+// (row = head mt*16 + n) and the weights of the heads whose results this lane
+// holds (mt*16 + 4g + i).  Heads past H_I are zero.
+template <int H_I, int D_I>
+struct IndexerQuery {
+  static constexpr int MT = (H_I + 15) / 16;
+  KeyFrag<H_I, D_I> qa[MT];
+  float wv[MT][4];
+  float qscale;
+
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ q8, const float* __restrict__ qs,
+                                       const float* __restrict__ w, int t, int n, int g) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int h = mt * 16 + n;
+      if (h < H_I)
+        qa[mt].load(q8 + ((int64_t)t * H_I + h) * D_I, g);
+      else
+        qa[mt].zero();
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = mt * 16 + 4 * g + i;
+        wv[mt][i] = (h < H_I) ? w[(int64_t)t * H_I + h] : 0.f;
+      }
+    qscale = qs[t];
+  }
+
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      qa[mt].zero();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[mt][i] = 0.f;
+    }
+    qscale = 0.f;
+  }
+};
+
+// Head-weighted ReLU sums of one query against 64 keys (4 N tiles of 16):
+// lane 16j + n returns the sum for key 16j + n of the group.
+template <int H_I, int D_I>
+__device__ __forceinline__ float group_scores(const IndexerQuery<H_I, D_I>& q, const KeyFrag<H_I, D_I> (&kb)[4],
+                                              int g) {
+  constexpr int MT = IndexerQuery<H_I, D_I>::MT;
+  float res = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v4f acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = KeyFrag<H_I, D_I>::mma(q.qa[mt], kb[j]);
+    float part = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part += q.wv[mt][i] * relu(acc[mt][i]);
+    part += __shfl_xor(part, 16, 64);
+    part += __shfl_xor(part, 32, 64);
+    if (g == j) res = part;
+  }
+  return res;
+}
+
+// The logit from the head sum and the two per-token scales.
+__device__ __forceinline__ float scaled_logit(float res, float qscale, float kscale) { return (res * qscale) * kscale; }
+
+}  // namespace dsa

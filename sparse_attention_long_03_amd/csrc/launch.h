@@ -17,6 +17,16 @@ hipError_t launch_indexer(int T, int max_len, int H_I, int D_I, const uint8_t* q
                           const uint8_t* k8, const float* ks, const int32_t* seq_id, const int32_t* pos,
                           const Layout& lay, float* logits, int64_t ld, u32* hist, hipStream_t stream);
 
+// (1+2) indexer fused with top-k (many query tokens): candidate lists of
+// `cap` slots per token in the workspace (8 * T * cap bytes).
+int fused_topk_cap(int max_len, int k);              // preferred capacity
+int fused_topk_cap_from_bytes(int T, size_t bytes);  // capacity a workspace holds
+size_t fused_topk_workspace_bytes(int T, int cap);
+bool fused_topk_cap_ok(int cap, int k);
+hipError_t launch_indexer_topk(int T, int H_I, int D_I, const uint8_t* q8, const float* qs, const float* w,
+                               const uint8_t* k8, const float* ks, const int32_t* seq_id, const int32_t* pos,
+                               const Layout& lay, int k, int cap, int32_t* idx, void* ws, hipStream_t stream);
+
 // (2) top-k; valid length of row t is valid_len[t] + len_add.  The histogram
 // lives at the start of the top-k workspace (topk_hist_buffer); with
 // hist_ready the caller has already filled it (fused indexer epilogue).

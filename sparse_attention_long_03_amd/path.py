@@ -64,6 +64,19 @@ class DSAPath:
         B.dsa_topk(logits, vl, logits.shape[1], k, idx, ws, stream)
         return idx
 
+    def indexer_topk(self, idx: Optional[torch.Tensor] = None, k=None, ws_bytes=None, stream=None) -> torch.Tensor:
+        """Fused indexer + selection (no logits); `ws_bytes` overrides the
+        preferred workspace size (a smaller one compacts the candidate lists
+        more often, with the same result)."""
+        x, c = self.x, self.cfg
+        k = c.k if k is None else k
+        if idx is None:
+            idx = torch.empty((self.T, k), dtype=torch.int32, device=self.dev)
+        n = B.dsa_workspace_bytes(B.DSA_OP_INDEXER_TOPK, self.T, x.max_len, 0, k) if ws_bytes is None else ws_bytes
+        ws = B.workspace(n, self.dev)
+        B.dsa_indexer_topk(self.q, self.layout, c.H_I, c.D_I, x.iq8, x.iqs, x.iw, x.ik8, x.iks, k, idx, ws, stream)
+        return idx
+
     def attn(self, idx: torch.Tensor, stream=None):
         x, c = self.x, self.cfg
         B.dsa_sparse_mla_attn(self.q, self.layout, c.H, x.q, x.kv, idx, idx.shape[1], c.scale, self.out, self.lse,

@@ -126,3 +126,35 @@ def test_workspace_sizes_are_monotone(lib):
     assert B.dsa_workspace_bytes(B.DSA_OP_TOPK, 16, 131072, 0, 2048) >= 2 * 16 * 131072 * 4
     assert B.dsa_workspace_bytes(99, 16, 131072, 128, 2048) == 0
     assert B.dsa_workspace_bytes(B.DSA_OP_ATTN, -1, 10, 128, 2048) == 0
+
+
+def test_fused_indexer_topk_validation(lib):
+    f = lib.dsa_indexer_topk
+    q, lay = _q(T=16), _lay()
+
+    def call(k=256, ws=FAKE, nbytes=None, H_I=64, q_=None, idx=FAKE):
+        nbytes = 8 * 16 * (k + 128) if nbytes is None else nbytes
+        return f(ctypes.byref(q_ or q), ctypes.byref(lay), H_I, 128, FAKE, FAKE, FAKE, FAKE, FAKE, k, idx, ws, nbytes,
+                 None)
+
+    assert call(k=0) == B.DSA_ERR_INVALID_ARG
+    assert call(k=4096) == B.DSA_ERR_UNSUPPORTED
+    assert call(H_I=8) == B.DSA_ERR_UNSUPPORTED
+    assert call(idx=None) == B.DSA_ERR_INVALID_ARG
+    assert call(ws=None) == B.DSA_ERR_WORKSPACE
+    assert call(nbytes=8 * 16 * (256 + 128) - 1) == B.DSA_ERR_WORKSPACE      # fewer than k + 128 slots
+    assert call(ws=ctypes.c_void_p((1 << 20) + 64)) == B.DSA_ERR_WORKSPACE   # misaligned
+    assert call(q_=_q(T=0, seq=None, pos=None)) == B.DSA_OK
+    # the preferred size holds a list no row of 100 keys ever overflows, and at least k + 128 slots
+    pref = B.dsa_workspace_bytes(B.DSA_OP_INDEXER_TOPK, 16, 100, 0, 256)
+    assert pref == 8 * 16 * (256 + 128)
+    assert B.dsa_workspace_bytes(B.DSA_OP_INDEXER_TOPK, 16, 5000, 0, 256) == 8 * 16 * (5056 + 64)
+    assert B.dsa_workspace_bytes(B.DSA_OP_INDEXER_TOPK, 16, 1 << 20, 0, 2048) == 8 * 16 * 8192
+
+
+def test_forward_workspace_switches_to_fused_selection(lib):
+    # below 2048 query tokens the logits are stored; from 2048 on they are not
+    small = B.dsa_workspace_bytes(B.DSA_OP_FORWARD, 2047, 65536, 128, 2048)
+    big = B.dsa_workspace_bytes(B.DSA_OP_FORWARD, 2048, 65536, 128, 2048)
+    assert small >= 2047 * 65536 * 4
+    assert big < 2048 * 65536 * 4
