@@ -104,25 +104,33 @@ __device__ __forceinline__ void attend_tile(const LDS_AS uint8_t* __restrict__ b
                                            float scale_log2, int n, int g, float& m_ref, float& l_part, v4f* o) {
   const LDS_AS uint8_t* nope = buf;
   const LDS_AS uint8_t* rope = buf + NOPE_BYTES;
-  // ---- scores S^T (keys x heads)
+  // ---- scores S^T (keys x heads): K fragments of keys n and 16+n, dims
+  // 32ks + 8g..+8 (no-rope rows for ks < 16, the swizzled rope block after).
+  // The reads run SPIPE steps ahead of the MFMAs that use them, in a ring of
+  // registers, so LDS latency overlaps the matrix work.
+  constexpr int SPIPE = 4;
+  auto frag = [&](int ks, int r) -> v8bf {
+    if (ks < 16) return *reinterpret_cast<const LDS_AS v8bf*>(nope + r * NOPE_STRIDE + 64 * ks + 16 * g);
+    const int c = 4 * (ks - 16) + g;  // rope chunk
+    return *reinterpret_cast<const LDS_AS v8bf*>(rope + r * 128 + 16 * (c ^ (r & 7)));
+  };
+  v8bf ra0[SPIPE], ra1[SPIPE];
+#pragma unroll
+  for (int j = 0; j < SPIPE; ++j) {
+    ra0[j] = frag(j, n);
+    ra1[j] = frag(j, 16 + n);
+  }
   v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks) {
-    const v8bf a0 = *reinterpret_cast<const LDS_AS v8bf*>(nope + n * NOPE_STRIDE + 64 * ks + 16 * g);
-    const v8bf a1 = *reinterpret_cast<const LDS_AS v8bf*>(nope + (16 + n) * NOPE_STRIDE + 64 * ks + 16 * g);
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s1, 0, 0, 0);
-    // bound the read-ahead (register pressure)
-    if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-  }
-#pragma unroll
-  for (int ks = 16; ks < 18; ++ks) {
-    const int c = 4 * (ks - 16) + g;  // rope chunk
-    const int r0 = n, r1 = 16 + n;
-    const v8bf a0 = *reinterpret_cast<const LDS_AS v8bf*>(rope + r0 * 128 + 16 * (c ^ (r0 & 7)));
-    const v8bf a1 = *reinterpret_cast<const LDS_AS v8bf*>(rope + r1 * 128 + 16 * (c ^ (r1 & 7)));
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s1, 0, 0, 0);
+  for (int ks = 0; ks < AT_D / 32; ++ks) {
+    const int slot = ks % SPIPE;
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra0[slot], qf[ks], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra1[slot], qf[ks], s1, 0, 0, 0);
+    if (ks + SPIPE < AT_D / 32) {
+      ra0[slot] = frag(ks + SPIPE, n);
+      ra1[slot] = frag(ks + SPIPE, 16 + n);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the ring order
   }
   // lane holds head n: s0[i] -> key 4g+i, s1[i] -> key 16+4g+i
   float z[8];
@@ -298,7 +306,11 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(const uint16_t* __r
 
 // Merge the splits: with o_s the normalised partial of split s,
 //   O = sum_s w_s o_s / sum_s w_s,   w_s = 2^(m_s - M) l_s,   M = max_s m_s.
-// One wave per (token, head); each lane owns 8 of the 512 value dims.
+// One wave per (token, head); lane s < n_splits reads split s's (m, l), the
+// weights come out of two wave reductions, and every lane then loads its 8
+// value dims of all splits at once (independent loads, one round trip).
+constexpr int AT_MAX_SPLITS = 8;
+
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ ws_o,
                                                       const float* __restrict__ ws_ml, int TH, int H, int n_splits,
                                                       uint16_t* __restrict__ out, float* __restrict__ lse) {
@@ -307,24 +319,36 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   const int lane = threadIdx.x & 63;
   const int t = item / H;
   const int h = item - t * H;
-  float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) {
-    const int64_t slot = ((int64_t)t * n_splits + s) * H + h;
-    if (ws_ml[slot * 2 + 1] > 0.f) M = fmaxf(M, ws_ml[slot * 2]);
+  const int64_t slot0 = (int64_t)t * n_splits * H + h;  // split s: slot0 + s*H
+  float m = -INFINITY, ls = 0.f;
+  if (lane < n_splits) {
+    m = ws_ml[(slot0 + (int64_t)lane * H) * 2];
+    ls = ws_ml[(slot0 + (int64_t)lane * H) * 2 + 1];
   }
+  float M = (ls > 0.f) ? m : -INFINITY;
+#pragma unroll
+  for (int d = 1; d < AT_MAX_SPLITS; d <<= 1) M = fmaxf(M, __shfl_xor(M, d, 64));
+  const float wgt = (ls > 0.f) ? exp2f(m - M) * ls : 0.f;
+  float L = wgt;
+#pragma unroll
+  for (int d = 1; d < AT_MAX_SPLITS; d <<= 1) L += __shfl_xor(L, d, 64);
+  // the reductions above ran within groups of 8 lanes: take lane 0's
+  L = __shfl(L, 0, 64);
+  M = __shfl(M, 0, 64);
+
+  v4i x[AT_MAX_SPLITS];
+#pragma unroll
+  for (int s = 0; s < AT_MAX_SPLITS; ++s)
+    if (s < n_splits) x[s] = *reinterpret_cast<const v4i*>(ws_o + (slot0 + (int64_t)s * H) * AT_DV + 8 * lane);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-  for (int s = 0; s < n_splits; ++s) {
-    const int64_t slot = ((int64_t)t * n_splits + s) * H + h;
-    const float ls = ws_ml[slot * 2 + 1];
-    if (!(ls > 0.f)) continue;
-    const float wgt = exp2f(ws_ml[slot * 2] - M) * ls;
-    L += wgt;
-    const v4i x = *reinterpret_cast<const v4i*>(ws_o + slot * AT_DV + 8 * lane);
+#pragma unroll
+  for (int s = 0; s < AT_MAX_SPLITS; ++s) {
+    if (s >= n_splits) break;
+    const float ws = __shfl(wgt, s, 64);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += wgt * __uint_as_float((u32)x[i] << 16);
-      acc[2 * i + 1] += wgt * __uint_as_float((u32)x[i] & 0xFFFF0000u);
+      acc[2 * i] += ws * __uint_as_float((u32)x[s][i] << 16);
+      acc[2 * i + 1] += ws * __uint_as_float((u32)x[s][i] & 0xFFFF0000u);
     }
   }
   const float inv = (L > 0.f) ? 1.f / L : 0.f;
@@ -350,7 +374,7 @@ int attn_splits(int T, int H, int k) {
   const int tiles = (k + AT_TILE - 1) / AT_TILE;
   int s = 1;
   // keep >= 4 tiles per split; stop once the grid reaches 256 workgroups
-  while (base * s < 256 && tiles / (2 * s) >= 4) s *= 2;
+  while (base * s < 256 && tiles / (2 * s) >= 4 && 2 * s <= AT_MAX_SPLITS) s *= 2;
   return s;
 }
 
