@@ -248,22 +248,30 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(const uint16_t* __r
 
   LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
   __syncthreads();  // s_row / s_valid visible
-  // tile it+1 is loaded into registers while tile it is computed from LDS
-  TileStage<NT> stage;
+  // Two tiles in flight: while a tile is computed from one LDS buffer, the
+  // next two load into two register stages (A: odd distance, B: even), so the
+  // loop runs over pairs of tiles.  Every path issues the same loads -- tiles
+  // past the last one re-read it (an L2 hit; a padding tile of an odd count is
+  // masked out, contributing exactly nothing) -- so the waits stay partial.
+  TileStage<NT> sa, sb;
+  auto tile_rows = [&](int i) { return s_row + min(i, ntiles - 1) * AT_TILE; };
   if (ntiles > 0) {
-    stage.load(kv, s_row, tid);
-    stage.store(lds, tid);
+    sa.load(kv, tile_rows(0), tid);
+    sa.store(lds, tid);
+    sa.load(kv, tile_rows(1), tid);
+    sb.load(kv, tile_rows(2), tid);
   }
-  // Q and the first tile are in: with nothing outstanding at loop entry, the
-  // only loads the loop waits for are the next tile's, at its LDS store
-  __builtin_amdgcn_s_waitcnt(DSA_VMCNT(0));
-  for (int it = 0; it < ntiles; ++it) {
-    LDS_AS uint8_t* cur = lds + (it & 1) * BUF_BYTES;
-    const bool more = it + 1 < ntiles;
-    if (more) stage.load(kv, s_row + (it + 1) * AT_TILE, tid);
-    lds_barrier();  // tile `it` is in `cur`; the other buffer is free
-    attend_tile(cur, s_valid[it], qf, scale_log2, n, g, m_ref, l_part, o);
-    if (more) stage.store(lds + ((it + 1) & 1) * BUF_BYTES, tid);
+  // Q and the first tile are in; only the two stages' loads stay outstanding
+  __builtin_amdgcn_s_waitcnt(DSA_VMCNT(2 * TileStage<NT>::PER));
+  for (int it = 0; it < ntiles; it += 2) {
+    lds_barrier();  // tile `it` is in buffer 0; buffer 1 is free
+    attend_tile(lds, s_valid[it], qf, scale_log2, n, g, m_ref, l_part, o);
+    sa.store(lds + BUF_BYTES, tid);
+    sa.load(kv, tile_rows(it + 3), tid);
+    lds_barrier();  // tile `it+1` is in buffer 1; buffer 0 is free
+    attend_tile(lds + BUF_BYTES, (it + 1 < ntiles) ? s_valid[it + 1] : 0u, qf, scale_log2, n, g, m_ref, l_part, o);
+    sb.store(lds, tid);
+    sb.load(kv, tile_rows(it + 4), tid);
   }
 
   if (!has_heads) return;

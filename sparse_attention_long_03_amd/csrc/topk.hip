@@ -112,9 +112,7 @@ __global__ __launch_bounds__(TK_CHUNK_NT) void topk_chunk_kernel(const float* __
   const int n = row_len(valid_len, len_add, t);
   const int c0 = c * TK_CH;
   if (n <= k || c0 >= n) return;
-  find_threshold<TK_BINS, NT>(ws.hist + (int64_t)t * TK_BINS, (u32)k, scratch, &sh_bin, &sh_above);
-  const u32 b1 = sh_bin;
-
+  // the chunk's logits are loaded first: their latency overlaps the threshold search
   const float* row = logits + (int64_t)t * ld;
   const int i0 = c0 + threadIdx.x * E;
   u32 kk[E];
@@ -132,6 +130,8 @@ __global__ __launch_bounds__(TK_CHUNK_NT) void topk_chunk_kernel(const float* __
       for (int e = 0; e < 4; ++e) kk[4 * q + e] = (i + e < n) ? order_key(row[i + e]) : 0u;
     }
   }
+  find_threshold<TK_BINS, NT>(ws.hist + (int64_t)t * TK_BINS, (u32)k, scratch, &sh_bin, &sh_above);
+  const u32 b1 = sh_bin;
   u32 na = 0, nc = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -196,6 +196,11 @@ __global__ __launch_bounds__(TK_RES_NT) void topk_resolve_kernel(const int32_t* 
   }
   const int nch = (n + TK_CH - 1) / TK_CH;  // <= TK_MAX_CHUNKS (checked on the host)
   const int64_t slot0 = (int64_t)t * ws.nch;
+  // the lists are only read here and `out` only written: no aliasing, so the
+  // list loads may run ahead of the stores
+  const int32_t* __restrict__ above = ws.above;
+  const u32* __restrict__ ckey = ws.ckey;
+  const int32_t* __restrict__ cpos = ws.cpos;
 
   // ---- per-chunk counts -> exclusive offsets (one chunk per thread)
   const u32 my_a = (tid < nch) ? ws.counts[(slot0 + tid) * 2 + 0] : 0u;
@@ -224,7 +229,7 @@ __global__ __launch_bounds__(TK_RES_NT) void topk_resolve_kernel(const int32_t* 
   // ---- above lists, concatenated in chunk order
   for (u32 j = tid; j < A; j += NT) {
     const int c = chunk_of(s_aoff, nch, j);
-    out[j] = ws.above[(slot0 + c) * ws.cap_above + (j - s_aoff[c])];
+    out[j] = above[(slot0 + c) * ws.cap_above + (j - s_aoff[c])];
   }
   const u32 need1 = (u32)k - A;
 
@@ -234,8 +239,8 @@ __global__ __launch_bounds__(TK_RES_NT) void topk_resolve_kernel(const int32_t* 
     for (u32 j = tid; j < C; j += NT) {
       const int c = chunk_of(s_coff, nch, j);
       const int64_t g = (slot0 + c) * TK_CH + (j - s_coff[c]);
-      s_ckey[j] = ws.ckey[g] & 0x1FFFFFu;
-      s_cpos[j] = ws.cpos[g];
+      s_ckey[j] = ckey[g] & 0x1FFFFFu;
+      s_cpos[j] = cpos[g];
     }
   }
   for (int i = tid; i < TK_BINS; i += NT) hist[i] = 0;
@@ -243,12 +248,12 @@ __global__ __launch_bounds__(TK_RES_NT) void topk_resolve_kernel(const int32_t* 
   auto cand_key = [&](u32 j) -> u32 {
     if (staged) return s_ckey[j];
     const int c = chunk_of(s_coff, nch, j);
-    return ws.ckey[(slot0 + c) * TK_CH + (j - s_coff[c])] & 0x1FFFFFu;
+    return ckey[(slot0 + c) * TK_CH + (j - s_coff[c])] & 0x1FFFFFu;
   };
   auto cand_pos = [&](u32 j) -> int32_t {
     if (staged) return s_cpos[j];
     const int c = chunk_of(s_coff, nch, j);
-    return ws.cpos[(slot0 + c) * TK_CH + (j - s_coff[c])];
+    return cpos[(slot0 + c) * TK_CH + (j - s_coff[c])];
   };
 
   // ---- exact k-th key among the candidates: bits 20..10, then 9..0
