@@ -49,8 +49,8 @@ TRAFFIC = {
     # WRITE_SIZE 8192.0 KiB/launch x 1.0 (copy: 262144 KiB counted for 262144 KiB written)
     "write_bytes": 8388608,
 }
-TRAFFIC_SOURCES = ("sparse_attention_long_03_amd/csrc/indexer.hip", "sparse_attention_long_03_amd/csrc/common.h",
-                   "sparse_attention_long_03_amd/csrc/launch.h")
+TRAFFIC_SOURCES = ("sparse_attention_long_03_amd/csrc/indexer.hip", "sparse_attention_long_03_amd/csrc/indexer_math.h",
+                   "sparse_attention_long_03_amd/csrc/common.h", "sparse_attention_long_03_amd/csrc/launch.h")
 
 
 def sources_hash():

@@ -111,7 +111,10 @@ struct IndexerQuery {
 };
 
 // Head-weighted ReLU sums of one query against 64 keys (4 N tiles of 16):
-// lane 16j + n returns the sum for key 16j + n of the group.
+// lane 16j + n returns the sum for key 16j + n of the group.  Within a lane,
+// each 16-head tile sums its four heads in a short chain of its own and the
+// tiles are added pairwise, so the dependent adds stay few; then the sums of
+// the four lane groups are added across lanes.
 template <int H_I, int D_I>
 __device__ __forceinline__ float group_scores(const IndexerQuery<H_I, D_I>& q, const KeyFrag<H_I, D_I> (&kb)[4],
                                               int g) {
@@ -122,11 +125,18 @@ __device__ __forceinline__ float group_scores(const IndexerQuery<H_I, D_I>& q, c
     v4f acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = KeyFrag<H_I, D_I>::mma(q.qa[mt], kb[j]);
-    float part = 0.f;
+    float pm[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt) {
+      pm[mt] = q.wv[mt][0] * relu(acc[mt][0]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part += q.wv[mt][i] * relu(acc[mt][i]);
+      for (int i = 1; i < 4; ++i) pm[mt] += q.wv[mt][i] * relu(acc[mt][i]);
+    }
+#pragma unroll
+    for (int w = 1; w < MT; w *= 2)
+#pragma unroll
+      for (int mt = 0; mt + w < MT; mt += 2 * w) pm[mt] += pm[mt + w];
+    float part = pm[0];
     part += __shfl_xor(part, 16, 64);
     part += __shfl_xor(part, 32, 64);
     if (g == j) res = part;

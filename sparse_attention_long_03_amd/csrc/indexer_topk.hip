@@ -37,6 +37,7 @@ constexpr int FT_WAVES = 4;
 constexpr int FT_QPW = 2;                 // query tokens per wave
 constexpr int FT_QB = FT_WAVES * FT_QPW;  // query tokens per workgroup
 constexpr int FT_TILE = 64;               // keys per tile
+constexpr int FT_AHEAD = 4;               // key tiles in flight (register stages)
 constexpr int FT_CAP_MAX = 8192;          // candidate slots per token
 constexpr int FT_BINS = 2048;
 
@@ -261,27 +262,39 @@ __global__ __launch_bounds__(FT_WAVES * 64) void indexer_topk_kernel(
     }
     const int ntiles = pmax / FT_TILE + 1;
 
-    // tile `it`: rows past pmax re-read row pmax (stored, never used)
-    TileRegs<D_I> st;
-    float ks_next;
-    auto stage_load = [&](int it) {
-      const int base = it * FT_TILE;
-      const int64_t row0 = token_row(lay, seq, base);  // one page when paged
-      st.load(k8 + (row0 + (min(base + sr, pmax) - base)) * D_I + sc);
-      ks_next = ks[row0 + (min(base + lane, pmax) - base)];
+    // Key tiles load FT_AHEAD tiles ahead into a ring of register stages
+    // (stage j holds the next tile of residue j), so the loop body covers
+    // FT_AHEAD tiles.  Loads past the last tile re-read it, and tiles past it
+    // are computed but never taken (their positions exceed every row's
+    // end): every path issues the same loads, so the waits stay partial.
+    struct Stage {
+      TileRegs<D_I> r;
+      float ks;
+      int pg;  // physical page of the stage's next tile (paged layout)
     };
-    stage_load(0);
-    st.store(&tile[0][sr * STRIDE + sc]);
-    float ksv = ks_next;
-    __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-      const int cur = it & 1;
-      stage_load(min(it + 1, ntiles - 1));
+    // A tile is one 64-token page when paged.  Each stage looks up the page
+    // of its next tile right after issuing its current loads, FT_AHEAD steps
+    // before it is needed: loads complete in issue order, so a lookup issued
+    // just before its use would make that wait drain every stage.  (The
+    // lookup is unconditional: with a contiguous layout it reads a scale,
+    // unused.)
+    const int32_t* pg_src = lay.paged ? lay.block_table + (int64_t)seq * lay.max_pages
+                                      : reinterpret_cast<const int32_t*>(ks);
+    auto page = [&](int i) -> int { return pg_src[lay.paged ? min(i, ntiles - 1) : 0]; };
+    auto load = [&](Stage& S, int i) {  // S.pg is the page of tile i
+      const int base = min(i, ntiles - 1) * FT_TILE;
+      const int64_t row0 = lay.paged ? (int64_t)S.pg * 64 : (int64_t)seq * lay.seq_capacity + base;
+      S.r.load(k8 + (row0 + (min(base + sr, pmax) - base)) * D_I + sc);
+      S.ks = ks[row0 + (min(base + lane, pmax) - base)];
+      S.pg = page(i + FT_AHEAD);
+    };
+    float ksv;
+    auto step = [&](int i, Stage& S) {  // S holds tile i+1
       if (wave_on) {
         KeyFrag<H_I, D_I> kb[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) kb[j].load(&tile[cur][(16 * j + n) * STRIDE], g);
-        const int s = it * FT_TILE + lane;
+        for (int j = 0; j < 4; ++j) kb[j].load(&tile[i & 1][(16 * j + n) * STRIDE], g);
+        const int s = i * FT_TILE + lane;
 #pragma unroll
         for (int qi = 0; qi < FT_QPW; ++qi) {
           if (!row_on[qi]) continue;
@@ -305,9 +318,29 @@ __global__ __launch_bounds__(FT_WAVES * 64) void indexer_topk_kernel(
           }
         }
       }
-      if (it + 1 < ntiles) st.store(&tile[cur ^ 1][sr * STRIDE + sc]);
-      ksv = ks_next;
+      S.r.store(&tile[(i + 1) & 1][sr * STRIDE + sc]);
+      ksv = S.ks;
+      load(S, i + 1 + FT_AHEAD);
       __syncthreads();
+    };
+    Stage s0, s1, s2, s3;
+    s0.pg = page(0);
+    s1.pg = page(1);
+    s2.pg = page(2);
+    s3.pg = page(3);
+    load(s0, 0);  // tile 0, then its stage's next tile 4 (page looked up by load)
+    s0.r.store(&tile[0][sr * STRIDE + sc]);
+    ksv = s0.ks;
+    load(s1, 1);
+    load(s2, 2);
+    load(s3, 3);
+    load(s0, 4);
+    __syncthreads();
+    for (int it = 0; it < ntiles; it += FT_AHEAD) {
+      step(it + 0, s1);
+      step(it + 1, s2);
+      step(it + 2, s3);
+      step(it + 3, s0);
     }
   }
 
