@@ -135,11 +135,11 @@ int dsa_topk(const float* logits, int64_t ld_logits, const int32_t* valid_len, i
  *   workspace : device, 256-byte aligned; it holds a candidate list of `cap`
  *               slots (8 bytes each) per query token, with cap = the largest
  *               multiple of 64 not above 8192 that fits workspace_bytes / T;
- *               cap >= k + 128 is required (DSA_ERR_WORKSPACE otherwise).
+ *               cap >= k + 320 is required (DSA_ERR_WORKSPACE otherwise).
  *               A smaller cap gives the same result with more work;
  *               dsa_workspace_bytes(DSA_OP_INDEXER_TOPK, T, max_len, 0, k) is
  *               the size at which no list ever needs compacting for rows up
- *               to about 8K positions.
+ *               to about 7.9K positions.
  * ------------------------------------------------------------------------- */
 int dsa_indexer_topk(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,
                      const uint8_t* q_fp8, const float* q_scale, const float* w, const uint8_t* k_fp8,

@@ -309,13 +309,6 @@ __global__ __launch_bounds__(FT_WAVES * 64) void indexer_topk_kernel(
             lpos[qi][d] = s;
           }
           cnt[qi] += __popcll(m);
-          if (cnt[qi] > cap - FT_TILE) {
-            u32 kstar, ties;
-            wave_kth(lkey[qi], cnt[qi], k, my_hist, kstar, ties);
-            wave_emit(lkey[qi], lpos[qi], cnt[qi], k, kstar, ties, lkey[qi], lpos[qi]);
-            cnt[qi] = k;
-            tau[qi] = kstar;
-          }
         }
       }
       S.r.store(&tile[(i + 1) & 1][sr * STRIDE + sc]);
@@ -341,6 +334,17 @@ __global__ __launch_bounds__(FT_WAVES * 64) void indexer_topk_kernel(
       step(it + 1, s2);
       step(it + 2, s3);
       step(it + 3, s0);
+      // a list compacts once it could not take FT_AHEAD more tiles
+#pragma unroll
+      for (int qi = 0; qi < FT_QPW; ++qi) {
+        if (cnt[qi] > cap - FT_AHEAD * FT_TILE) {
+          u32 kstar, ties;
+          wave_kth(lkey[qi], cnt[qi], k, my_hist, kstar, ties);
+          wave_emit(lkey[qi], lpos[qi], cnt[qi], k, kstar, ties, lkey[qi], lpos[qi]);
+          cnt[qi] = k;
+          tau[qi] = kstar;
+        }
+      }
     }
   }
 
@@ -362,9 +366,9 @@ __global__ __launch_bounds__(FT_WAVES * 64) void indexer_topk_kernel(
 }
 
 int fused_topk_cap(int max_len, int k) {
-  int c = ((max_len + FT_TILE - 1) / FT_TILE) * FT_TILE + FT_TILE;  // no compaction needed
+  int c = ((max_len + FT_TILE - 1) / FT_TILE) * FT_TILE + FT_AHEAD * FT_TILE;  // no compaction needed
   if (c > FT_CAP_MAX) c = FT_CAP_MAX;
-  if (c < k + 2 * FT_TILE) c = k + 2 * FT_TILE;
+  if (c < k + (FT_AHEAD + 1) * FT_TILE) c = k + (FT_AHEAD + 1) * FT_TILE;
   return c;
 }
 
@@ -378,7 +382,11 @@ int fused_topk_cap_from_bytes(int T, size_t bytes) {
 // keys then positions; T * cap * 4 is a multiple of 256 (cap is a multiple of 64)
 size_t fused_topk_workspace_bytes(int T, int cap) { return 8 * (size_t)T * cap; }
 
-bool fused_topk_cap_ok(int cap, int k) { return cap >= k + 2 * FT_TILE && cap <= FT_CAP_MAX && cap % FT_TILE == 0; }
+// a compacted list (k entries) must take FT_AHEAD more tiles before the next
+// check, plus one tile of margin
+bool fused_topk_cap_ok(int cap, int k) {
+  return cap >= k + (FT_AHEAD + 1) * FT_TILE && cap <= FT_CAP_MAX && cap % FT_TILE == 0;
+}
 
 template <int H_I, int D_I>
 static hipError_t launch_fused_t(int T, const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8,

@@ -133,7 +133,7 @@ def test_fused_indexer_topk_validation(lib):
     q, lay = _q(T=16), _lay()
 
     def call(k=256, ws=FAKE, nbytes=None, H_I=64, q_=None, idx=FAKE):
-        nbytes = 8 * 16 * (k + 128) if nbytes is None else nbytes
+        nbytes = 8 * 16 * (k + 320) if nbytes is None else nbytes
         return f(ctypes.byref(q_ or q), ctypes.byref(lay), H_I, 128, FAKE, FAKE, FAKE, FAKE, FAKE, k, idx, ws, nbytes,
                  None)
 
@@ -142,13 +142,14 @@ def test_fused_indexer_topk_validation(lib):
     assert call(H_I=8) == B.DSA_ERR_UNSUPPORTED
     assert call(idx=None) == B.DSA_ERR_INVALID_ARG
     assert call(ws=None) == B.DSA_ERR_WORKSPACE
-    assert call(nbytes=8 * 16 * (256 + 128) - 1) == B.DSA_ERR_WORKSPACE      # fewer than k + 128 slots
+    assert call(nbytes=8 * 16 * (256 + 320) - 1) == B.DSA_ERR_WORKSPACE      # fewer than k + 320 slots
     assert call(ws=ctypes.c_void_p((1 << 20) + 64)) == B.DSA_ERR_WORKSPACE   # misaligned
     assert call(q_=_q(T=0, seq=None, pos=None)) == B.DSA_OK
-    # the preferred size holds a list no row of 100 keys ever overflows, and at least k + 128 slots
+    # the preferred size holds every position of the row plus 4 tiles (no
+    # compaction), and at least k + 320 slots
     pref = B.dsa_workspace_bytes(B.DSA_OP_INDEXER_TOPK, 16, 100, 0, 256)
-    assert pref == 8 * 16 * (256 + 128)
-    assert B.dsa_workspace_bytes(B.DSA_OP_INDEXER_TOPK, 16, 5000, 0, 256) == 8 * 16 * (5056 + 64)
+    assert pref == 8 * 16 * (256 + 320)
+    assert B.dsa_workspace_bytes(B.DSA_OP_INDEXER_TOPK, 16, 5000, 0, 256) == 8 * 16 * (5056 + 256)
     assert B.dsa_workspace_bytes(B.DSA_OP_INDEXER_TOPK, 16, 1 << 20, 0, 2048) == 8 * 16 * 8192
 
 

@@ -43,8 +43,8 @@ def _sorted(idx):
 
 
 def _min_ws(x, k):
-    """The smallest workspace the call accepts: k + 128 candidate slots per token."""
-    return 8 * x.T * (k + 128)
+    """The smallest workspace the call accepts: k + 320 candidate slots per token."""
+    return 8 * x.T * (k + 320)
 
 
 @pytest.mark.parametrize("small_ws", [False, True], ids=["preferred_ws", "min_ws"])
