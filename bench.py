@@ -43,9 +43,9 @@ REPLICAS = 4
 # device copy in the same pass.  Valid only for the kernel sources they were
 # taken on (hash below); otherwise the field is reported as null.
 TRAFFIC = {
-    "sources_sha256": "f42f4ef51a1620814c3a99f29b1f2cdebe30b31ed4e15cf7cd7db7ace65fabb0",
-    # FETCH_SIZE 135758.0 KiB/launch x 1.99982 (copy: 131083.9 KiB counted for 262144 KiB read)
-    "fetch_bytes": 278007103,
+    "sources_sha256": "ff50f493e106f8e9ebeee27ecbc37506279bbbcb5f099d881d55392c2b50cdf5",
+    # FETCH_SIZE 135758.6 KiB/launch x 1.99982 (copy: 131083.9 KiB counted for 262144 KiB read)
+    "fetch_bytes": 278008363,
     # WRITE_SIZE 8192.0 KiB/launch x 1.0 (copy: 262144 KiB counted for 262144 KiB written)
     "write_bytes": 8388608,
 }
