@@ -59,17 +59,21 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void indexer_kernel(const uint8_t* 
   // path and the next group's keys stay in flight while this one is reduced.
   const int first = wg_base + wid * 64;
   const int last_group = p & ~63;  // 64-aligned group holding position p
+  // The key scales load with their keys: a load issued after a logit store
+  // cannot complete before it (the counter is in order), so nothing the math
+  // waits for may be issued after the previous group's store.
   Frag kb[2][4];
-  int64_t row0[2];
+  float ksb[2];
   auto issue = [&](int it, int slot) {
     const int base = min(first + it * IDX_WAVES * 64, last_group);  // one page when paged
-    row0[slot] = token_row(lay, b, base);
-    const uint8_t* grp = k8 + row0[slot] * D_I;  // wave-uniform base of the 64 rows
+    const int64_t row0 = token_row(lay, b, base);
+    const uint8_t* grp = k8 + row0 * D_I;  // wave-uniform base of the 64 rows
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int s = min(base + 16 * j + n, p);  // positions past p read p
       kb[slot][j].load(grp + (u32)(s - base) * D_I, g);
     }
+    ksb[slot] = ks[row0 + (min(base + lane, p) - base)];
   };
   issue(0, 0);
 #pragma unroll
@@ -77,9 +81,8 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void indexer_kernel(const uint8_t* 
     const int cur = it & 1;
     if (it + 1 < IDX_ITERS) issue(it + 1, cur ^ 1);
     const int base = first + it * IDX_WAVES * 64;
-    const int base_c = min(base, last_group);
     const int s_me = base + lane;
-    const float ksv = ks[row0[cur] + (min(base_c + lane, p) - base_c)];
+    const float ksv = ksb[cur];
     const float res = group_scores<H_I, D_I>(qq, kb[cur], g);
     if (s_me <= p) {
       const float v = scaled_logit(res, qq.qscale, ksv);
