@@ -23,4 +23,7 @@ from .dsa_oracle import (  # noqa: F401
     topk_select,
     sparse_mla_attention,
     dsa_forward,
+    encode_e4m3fn,
+    quantize_index_key,
+    cache_write,
 )

@@ -248,3 +248,76 @@ def dsa_forward(iq8, iqs, iw, ik8, iks, q_bits, kv_bits, seq_id, pos, k: int, sc
         idx[t] = topk_select(logits[t, :n].astype(np.float32), n, k)
     out, lse = sparse_mla_attention(q_bits, kv_bits, idx, seq_id, scale, d_v, block_table, page_size)
     return logits, idx, out, lse
+
+
+# ---------------------------------------------------------------------------
+# (f4) Cache write: quantise a new token's index key, store it and its latent row
+# ---------------------------------------------------------------------------
+#
+# [DSA-article] (1): the indexer runs in FP8, so each token's index key is
+# stored as FP8 before it is scored.  Reading taken (the pages give no
+# quantisation recipe): one float32 scale per token, scale = max(amax / 448,
+# 2^-126) where amax is the largest |x| of the key and 448 the largest e4m3fn
+# value; each element is x / scale (float32 division), clamped to +-448, then
+# rounded to the nearest e4m3fn value, ties to the even code.
+
+E4M3FN_MAX = 448.0
+SCALE_FLOOR = 2.0 ** -126
+
+# non-negative finite e4m3fn values: codes 0x00..0x7E, strictly increasing
+_E4M3FN_POS = _E4M3FN_TABLE[:0x7F]
+
+
+def encode_e4m3fn(y) -> np.ndarray:
+    """Nearest e4m3fn code of each value (|y| <= 448), ties to the even code.
+
+    The magnitude is rounded among the 127 non-negative finite values; the
+    sign bit is the sign of y (so -0.0, and negative values that round to
+    zero, give 0x80).
+    """
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    if np.any(a > E4M3FN_MAX) or np.any(np.isnan(a)):
+        raise ValueError("encode_e4m3fn expects finite values with |y| <= 448")
+    hi = np.searchsorted(_E4M3FN_POS, a, side="left")          # first value >= a
+    hi = np.minimum(hi, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _E4M3FN_POS[lo]
+    d_hi = _E4M3FN_POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    mag = np.where(a == _E4M3FN_POS[hi], hi, np.where(pick_hi, hi, lo)).astype(np.uint8)
+    return (mag | (np.signbit(y).astype(np.uint8) << 7)).astype(np.uint8)
+
+
+def quantize_index_key(x) -> tuple:
+    """(codes uint8[D], scale float32) of one token's float32 index key."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x)) if x.size else np.float32(0)
+    scale = np.float32(max(np.float32(amax) / np.float32(E4M3FN_MAX), np.float32(SCALE_FLOOR)))
+    y = np.clip(x / scale, np.float32(-E4M3FN_MAX), np.float32(E4M3FN_MAX)).astype(np.float32)
+    return encode_e4m3fn(y), scale
+
+
+def cache_write(k8_cache, ks_cache, kv_cache, seq_id, pos, k_new, kv_new_bits=None, block_table=None,
+                page_size: int = 64):
+    """Store new tokens into the caches (returns updated copies).
+
+    Token t goes to logical position pos[t] of sequence seq_id[t] (contiguous
+    ``[B, L, ...]`` caches, or physical page ``block_table[b, pos // 64]`` row
+    ``pos % 64``): its index key quantised by quantize_index_key, its scale,
+    and (if given) its 576-value latent row, copied bit for bit.
+    """
+    k8_cache, ks_cache = np.array(k8_cache, copy=True), np.array(ks_cache, copy=True)
+    kv_cache = None if kv_cache is None else np.array(kv_cache, copy=True)
+    for t in range(len(seq_id)):
+        b, s = int(seq_id[t]), int(pos[t])
+        if block_table is None:
+            where = (b, s)
+        else:
+            where = (int(np.asarray(block_table)[b, s // page_size]), s % page_size)
+        codes, scale = quantize_index_key(np.asarray(k_new)[t])
+        k8_cache[where] = codes
+        ks_cache[where] = scale
+        if kv_new_bits is not None:
+            kv_cache[where] = np.asarray(kv_new_bits)[t]
+    return k8_cache, ks_cache, kv_cache

@@ -337,3 +337,96 @@ def test_generator_is_deterministic():
         ha = hashlib.sha256(getattr(a, name).contiguous().view(torch.uint8).numpy().tobytes()).hexdigest()
         hb = hashlib.sha256(getattr(b, name).contiguous().view(torch.uint8).numpy().tobytes()).hexdigest()
         assert ha == hb, name
+
+
+# ----------------------------------------------------------------- cache write (FP8 quantisation)
+
+def _torch_e4m3fn_codes(y32):
+    import torch
+    return torch.from_numpy(np.asarray(y32, dtype=np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_encode_e4m3fn_matches_torch_including_ties():
+    rng = np.random.default_rng(5)
+    vals = O.decode_e4m3fn(np.arange(0x7F, dtype=np.uint8))          # 0 .. 448
+    mids = (vals[:-1] + vals[1:]) / 2                                   # exact ties (5 significant bits)
+    qtr = vals[:-1] + (vals[1:] - vals[:-1]) * 0.25                     # just off the ties
+    rnd = rng.uniform(-448, 448, 20000)
+    small = rng.normal(0, 2.0 ** -8, 5000)                              # subnormal range
+    y = np.concatenate([vals, -vals, mids, -mids, qtr, -qtr, rnd, small, [0.0, -0.0]]).astype(np.float32)
+    assert np.array_equal(O.encode_e4m3fn(y), _torch_e4m3fn_codes(y))
+
+
+def test_encode_e4m3fn_closed_forms():
+    enc = lambda v: int(O.encode_e4m3fn(np.float32(v)))
+    assert enc(1.0) == 0x38 and enc(-1.0) == 0xB8
+    assert enc(448.0) == 0x7E and enc(432.0) == 0x7E       # 416 | 448 tie -> even mantissa (448)
+    assert enc(400.0) == 0x7C                              # 384 | 416 tie -> even mantissa (384)
+    assert enc(2.0 ** -9) == 0x01                          # smallest subnormal
+    assert enc(2.0 ** -10) == 0x00 and enc(-2.0 ** -10) == 0x80   # 0 | 2^-9 tie -> 0, sign kept
+    assert enc(3 * 2.0 ** -10) == 0x02                     # 2^-9 | 2^-8 tie -> even (2^-8)
+    assert enc(0.0) == 0x00 and enc(-0.0) == 0x80
+
+
+def test_quantize_index_key_scale_and_bounds():
+    rng = np.random.default_rng(6)
+    # power-of-two ranges: the scale is exact and the largest element maps to +-448
+    for e in (-20, -3, 0, 7):
+        x = (rng.normal(size=128) * 2.0 ** e).astype(np.float32)
+        x[17] = np.float32(448 * 2.0 ** e)
+        codes, scale = O.quantize_index_key(x)
+        assert scale == np.float32(2.0 ** e)
+        assert codes[17] == 0x7E
+    # an all-zero key: the scale floor, every code zero
+    codes, scale = O.quantize_index_key(np.zeros(64, np.float32))
+    assert scale == np.float32(2.0 ** -126) and not codes.any()
+    # general keys: the largest magnitude code is 0x7E, and the error stays
+    # within half a step (relative 2^-4 for normals, absolute 2^-10 scale below)
+    for _ in range(50):
+        x = (rng.standard_t(3, size=128) * rng.uniform(1e-3, 1e3)).astype(np.float32)
+        codes, scale = O.quantize_index_key(x)
+        assert (codes & 0x7F).max() == 0x7E
+        back = O.decode_e4m3fn(codes) * np.float64(scale)
+        err = np.abs(back - x.astype(np.float64))
+        assert np.all(err <= 2.0 ** -4 * np.abs(x) + 2.0 ** -10 * np.float64(scale) * (1 + 1e-6))
+
+
+def test_quantize_index_key_matches_torch_route():
+    import torch
+    rng = np.random.default_rng(7)
+    for _ in range(30):
+        x = (rng.normal(size=128) * rng.uniform(1e-4, 1e4)).astype(np.float32)
+        codes, scale = O.quantize_index_key(x)
+        xt = torch.from_numpy(x)
+        s_t = torch.clamp(xt.abs().max() / 448.0, min=2.0 ** -126)
+        c_t = (xt / s_t).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.float32(s_t.item()) == scale
+        assert np.array_equal(codes, c_t)
+
+
+def test_cache_write_paged_equals_contiguous_and_touches_only_its_rows():
+    rng = np.random.default_rng(8)
+    B, L, D = 2, 256, 64
+    k8 = rng.integers(0, 256, (B, L, D), dtype=np.uint8)
+    ks = rng.uniform(0.1, 1, (B, L)).astype(np.float32)
+    kv = rng.integers(0, 65536, (B, L, 576), dtype=np.uint16)
+    seq_id, pos = np.array([0, 1, 1]), np.array([5, 0, 200])
+    k_new = rng.normal(size=(3, D)).astype(np.float32)
+    kv_new = rng.integers(0, 65536, (3, 576), dtype=np.uint16)
+    a8, as_, akv = O.cache_write(k8, ks, kv, seq_id, pos, k_new, kv_new)
+    for t in range(3):
+        c, s = O.quantize_index_key(k_new[t])
+        assert np.array_equal(a8[seq_id[t], pos[t]], c) and as_[seq_id[t], pos[t]] == s
+        assert np.array_equal(akv[seq_id[t], pos[t]], kv_new[t])
+    mask = np.ones((B, L), bool)
+    mask[seq_id, pos] = False
+    assert np.array_equal(a8[mask], k8[mask]) and np.array_equal(akv[mask], kv[mask])
+    # paged: 4 pages of 64 per sequence, shuffled
+    perm = rng.permutation(B * 4)
+    bt = perm.reshape(B, 4)
+    def pages(c):
+        out = np.empty((B * 4, 64) + c.shape[2:], c.dtype)
+        out[bt.reshape(-1)] = c.reshape((B * 4, 64) + c.shape[2:])
+        return out
+    p8, ps, pkv = O.cache_write(pages(k8), pages(ks), pages(kv), seq_id, pos, k_new, kv_new, block_table=bt)
+    assert np.array_equal(p8, pages(a8)) and np.array_equal(ps, pages(as_)) and np.array_equal(pkv, pages(akv))
