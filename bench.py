@@ -161,6 +161,26 @@ def cpu_baseline(x, budget_s):
                       f"(indexer over all {x.max_len} keys, top-k, attention), float64 NumPy oracle, {dt:.1f} s"}
 
 
+def cache_write_timing(x, n_launch, stream):
+    """dsa_cache_write of one new token per query (its FP8 index key and
+    latent row) at the query's position: mean time and algorithmic GB/s
+    (fp32 key + bf16 row read; FP8 key + scale + row written)."""
+    import torch
+    from sparse_attention_long_03_amd import binding as B
+    c = x.cfg
+    g = torch.Generator(device="cuda").manual_seed(99)
+    k_new = torch.randn((x.T, c.D_I), generator=g, device="cuda")
+    kv_new = torch.randn((x.T, c.D), generator=g, device="cuda").to(torch.bfloat16)
+    q = B.queries(x.seq_id, x.pos, c.B, x.max_len)
+    lay = B.paged_layout(x.block_table, x.kv.shape[0], c.page_size) if x.block_table is not None \
+        else B.contiguous_layout(x.kv.shape[1])
+    fn = lambda: B.dsa_cache_write(q, lay, c.D_I, k_new, kv_new, x.ik8, x.iks, x.kv)
+    timed_rotation([fn], 2, stream)
+    ts = mean(timed_rotation([fn], n_launch, stream))
+    nbytes = x.T * (c.D_I * 4 + c.D * 2 + c.D_I + 4 + c.D * 2)
+    return round(ts * 1e3, 2), round(nbytes / (ts * 1e-3) / 1e9, 1)
+
+
 def workload_name(cfg):
     if cfg.kind == "decode":
         return (f"{cfg.name}: decode, B={cfg.B} sequences x L={cfg.L} tokens, 1 query token each, indexer "
@@ -205,6 +225,7 @@ def bench_prefill(args, cfg):
     fused_ts = timed_rotation([fused], n_launch, stream)
     attn_ts = timed_rotation([lambda: p.attn(idx)], n_launch, stream)
     fused_avg, attn_avg = mean(fused_ts), mean(attn_ts)
+    cw_us, cw_gbs = cache_write_timing(x, n_launch, stream)  # last: it overwrites the caches
 
     pairs = (x.pos.long() + 1).sum().item()
     sel = sum(min(int(q) + 1, k) for q in x.pos.tolist())
@@ -235,7 +256,8 @@ def bench_prefill(args, cfg):
                      "flops_per_launch": idx_flops, "avg_launch_us": round(fused_avg * 1e3, 1)},
         "kernels": {"indexer_topk_ms": round(fused_avg, 3), "indexer_tflops": round(idx_tf, 1),
                     "attn_ms": round(attn_avg, 3), "attn_tflops": round(attn_tf, 1),
-                    "attn_frac_bf16": round(attn_tf / BF16_PEAK_TFLOPS, 4)},
+                    "attn_frac_bf16": round(attn_tf / BF16_PEAK_TFLOPS, 4),
+                    "cache_write_us": cw_us, "cache_write_gbs": cw_gbs},
     }
     print(json.dumps(out), flush=True)
 
@@ -293,6 +315,7 @@ def main():
     attn_ts = timed_rotation(attn_fns, n_launch, stream)
     step_ts = timed_rotation(fwd, n_launch, stream)
     idx_avg, topk_avg, attn_avg = mean(idx_ts), mean(topk_ts), mean(attn_ts)
+    cw_us, cw_gbs = cache_write_timing(xs[1], n_launch, stream)  # on a replica not used below
 
     if args.copy_calibration:
         src = torch.ones(1 << 26, dtype=torch.int32, device="cuda")  # 256 MiB
@@ -336,6 +359,8 @@ def main():
             "attn_gbs": round(ab["attn"] / (attn_avg * 1e-3) / 1e9, 1),
             "attn_tflops": round(ab["attn_flops"] / (attn_avg * 1e-3) / 1e12, 2),
             "forward_event_us": round(mean(step_ts) * 1e3, 2),
+            "cache_write_us": cw_us,
+            "cache_write_gbs": cw_gbs,
         },
     }
     if not args.no_cpu:

@@ -80,6 +80,28 @@ typedef struct dsa_kv_layout {
 } dsa_kv_layout;
 
 /* ---------------------------------------------------------------------------
+ * (0) Cache write: store new tokens into the caches that (1) and (3) read.
+ * The indexer scores in FP8 ("... Sparse Consideration (DSA)", part (1)), so
+ * each new token's float32 index key is quantised with one float32 scale per
+ * token:
+ *     scale  = max(amax / 448, 2^-126),   amax = max_i |k_new[t, i]|
+ *     code_i = e4m3fn(clamp(k_new[t, i] / scale, -448, 448))
+ * rounding to the nearest e4m3fn value, ties to the even code (float32
+ * division, exactly rounded).  Token t is written at logical position pos[t]
+ * of sequence seq_id[t]: codes to k_fp8, scale to k_scale and, when given,
+ * its 576-value latent row to kv_bf16 (copied bit for bit).  Positions must
+ * be distinct within a call; other rows are not touched.
+ *
+ *   q           : seq_id / pos of the new tokens (pos[t] < max_len)
+ *   D_I         : 64 or 128
+ *   k_new       : device float[T, D_I], finite
+ *   kv_new_bf16 : device bf16[T, 576] or NULL (then kv_bf16 must be NULL)
+ *   k_fp8, k_scale, kv_bf16 : the caches, in the layout above
+ * ------------------------------------------------------------------------- */
+int dsa_cache_write(const dsa_queries* q, const dsa_kv_layout* layout, int32_t D_I, const float* k_new,
+                    const void* kv_new_bf16, uint8_t* k_fp8, float* k_scale, void* kv_bf16, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * (1) Lightning indexer logits.
  *   logits[t * ld_logits + s] =
  *       q_scale[t] * k_scale[s] * sum_j w[t,j] * ReLU( sum_d q[t,j,d] * k[s,d] )

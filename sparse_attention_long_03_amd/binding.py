@@ -41,8 +41,8 @@ class dsa_kv_layout(ctypes.Structure):
                 ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("seq_capacity", ctypes.c_int64)]
 
 
-EXPORTS = ("dsa_indexer_logits", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward",
-           "dsa_workspace_bytes", "dsa_status_str", "dsa_abi_version")
+EXPORTS = ("dsa_cache_write", "dsa_indexer_logits", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_attn",
+           "dsa_forward", "dsa_workspace_bytes", "dsa_status_str", "dsa_abi_version")
 
 _lib = None
 
@@ -57,6 +57,7 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
     Q, KV = ctypes.POINTER(dsa_queries), ctypes.POINTER(dsa_kv_layout)
+    L.dsa_cache_write.argtypes = [Q, KV, i32, vp, vp, vp, vp, vp, vp]
     L.dsa_indexer_logits.argtypes = [Q, KV, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp]
     L.dsa_indexer_topk.argtypes = [Q, KV, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
     L.dsa_topk.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp, sz, vp]
@@ -67,7 +68,8 @@ def lib() -> ctypes.CDLL:
     L.dsa_status_str.argtypes = [i32]
     L.dsa_status_str.restype = ctypes.c_char_p
     L.dsa_abi_version.restype = i32
-    for name in ("dsa_indexer_logits", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward"):
+    for name in ("dsa_cache_write", "dsa_indexer_logits", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_attn",
+                 "dsa_forward"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -134,6 +136,13 @@ def dsa_status_str(status: int) -> str:
 
 def dsa_abi_version() -> int:
     return int(lib().dsa_abi_version())
+
+
+def dsa_cache_write(q: dsa_queries, layout: dsa_kv_layout, D_I: int, k_new, kv_new_bf16, k_fp8, k_scale, kv_bf16,
+                    stream=None):
+    st = lib().dsa_cache_write(ctypes.byref(q), ctypes.byref(layout), D_I, _ptr(k_new), _ptr(kv_new_bf16),
+                               _ptr(k_fp8), _ptr(k_scale), _ptr(kv_bf16), _stream(stream))
+    _check(st, "dsa_cache_write")
 
 
 def dsa_indexer_logits(q: dsa_queries, layout: dsa_kv_layout, H_I: int, D_I: int, q_fp8, q_scale, w, k_fp8, k_scale,

@@ -155,6 +155,24 @@ int dsa_indexer_topk(const dsa_queries* q, const dsa_kv_layout* layout, int32_t 
                                         cap, idx, workspace, stream));
 }
 
+int dsa_cache_write(const dsa_queries* q, const dsa_kv_layout* layout, int32_t D_I, const float* k_new,
+                    const void* kv_new_bf16, uint8_t* k_fp8, float* k_scale, void* kv_bf16, hipStream_t stream) {
+  Layout lay;
+  int st = check_queries(q);
+  if (st) return st;
+  if ((st = check_layout(layout, q, &lay))) return st;
+  if (D_I < 1) return DSA_ERR_INVALID_ARG;
+  if (D_I != 64 && D_I != 128) return DSA_ERR_UNSUPPORTED;
+  if ((kv_new_bf16 == nullptr) != (kv_bf16 == nullptr)) return DSA_ERR_INVALID_ARG;
+  if (q->T == 0) return DSA_OK;
+  if (!k_new || !k_fp8 || !k_scale) return DSA_ERR_INVALID_ARG;
+  if (!aligned(k_fp8, 16) || (kv_bf16 && (!aligned(kv_bf16, 16) || !aligned(kv_new_bf16, 16))))
+    return DSA_ERR_INVALID_ARG;
+  return hip_status(launch_cache_write(q->T, D_I, q->seq_id, q->pos, lay, k_new,
+                                      static_cast<const uint16_t*>(kv_new_bf16), k_fp8, k_scale,
+                                      static_cast<uint16_t*>(kv_bf16), stream));
+}
+
 int dsa_topk(const float* logits, int64_t ld_logits, const int32_t* valid_len, int32_t T, int32_t max_len,
              int32_t k, int32_t* idx, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (T < 0 || max_len < 0 || k < 1) return DSA_ERR_INVALID_ARG;

@@ -45,6 +45,11 @@ hipError_t launch_attn(int T, int H, const uint16_t* q, const uint16_t* kv, cons
                        const Layout& lay, int k, float sm_scale, uint16_t* out, float* lse, void* ws,
                        hipStream_t stream);
 
+// cache write: quantise new index keys to FP8 and store them (+ latent rows)
+hipError_t launch_cache_write(int T, int D_I, const int32_t* seq_id, const int32_t* pos, const Layout& lay,
+                              const float* k_new, const uint16_t* kv_new, uint8_t* k8, float* ks, uint16_t* kv,
+                              hipStream_t stream);
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace dsa

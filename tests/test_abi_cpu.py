@@ -159,3 +159,15 @@ def test_forward_workspace_switches_to_fused_selection(lib):
     big = B.dsa_workspace_bytes(B.DSA_OP_FORWARD, 2048, 65536, 128, 2048)
     assert small >= 2047 * 65536 * 4
     assert big < 2048 * 65536 * 4
+
+
+def test_cache_write_validation(lib):
+    f = lib.dsa_cache_write
+    q, lay = _q(), _lay()
+    assert f(ctypes.byref(q), ctypes.byref(lay), 96, FAKE, None, FAKE, FAKE, None, None) == B.DSA_ERR_UNSUPPORTED
+    assert f(ctypes.byref(q), ctypes.byref(lay), 0, FAKE, None, FAKE, FAKE, None, None) == B.DSA_ERR_INVALID_ARG
+    assert f(ctypes.byref(q), ctypes.byref(lay), 128, FAKE, FAKE, FAKE, FAKE, None, None) == B.DSA_ERR_INVALID_ARG
+    assert f(ctypes.byref(q), ctypes.byref(lay), 128, None, None, FAKE, FAKE, None, None) == B.DSA_ERR_INVALID_ARG
+    assert f(ctypes.byref(q), ctypes.byref(_lay(cap=50)), 128, FAKE, None, FAKE, FAKE, None, None) == B.DSA_ERR_INVALID_ARG
+    q0 = _q(T=0, seq=None, pos=None)
+    assert f(ctypes.byref(q0), ctypes.byref(lay), 128, None, None, None, None, None, None) == B.DSA_OK
