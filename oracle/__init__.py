@@ -26,4 +26,5 @@ from .dsa_oracle import (  # noqa: F401
     encode_e4m3fn,
     quantize_index_key,
     cache_write,
+    masked_dense_attention,
 )

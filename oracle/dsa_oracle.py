@@ -321,3 +321,43 @@ def cache_write(k8_cache, ks_cache, kv_cache, seq_id, pos, k_new, kv_new_bits=No
         if kv_new_bits is not None:
             kv_cache[where] = np.asarray(kv_new_bits)[t]
     return k8_cache, ks_cache, kv_cache
+
+
+# ---------------------------------------------------------------------------
+# (f1) Masked dense variant of the sparse attention (short prefill lengths)
+# ---------------------------------------------------------------------------
+#
+# [DSA-article] "Lets Discuss it's effectivity and accuracy", first point:
+# at short lengths the prefill is run as a masked dense attention rather than
+# as a gather of the selected rows.  Reading taken: for query t, every
+# position s <= pos[t] of its sequence is scored and the positions not in the
+# query's selection are masked out (score -inf) before the softmax -- the
+# same set, hence the same result, as sparse_mla_attention, reached over
+# contiguous rows.
+
+
+def masked_dense_attention(q_bits, kv_bits, idx, seq_id, pos, scale: float, d_v: int = 512, block_table=None,
+                           page_size: int = 64):
+    """out float64[T, H, d_v], lse float64[T, H] over all s <= pos[t] with the
+    positions absent from idx[t] masked out (empty selection: out 0, lse -inf)."""
+    q = decode_bf16(q_bits)
+    T, H, D = q.shape
+    out = np.zeros((T, H, d_v))
+    lse = np.full((T, H), -np.inf)
+    for t in range(T):
+        n = int(pos[t]) + 1
+        rows = decode_bf16(logical_rows(kv_bits, int(seq_id[t]), n, block_table, page_size))  # [n, D]
+        sel = np.asarray(idx[t])
+        sel = sel[sel >= 0]
+        mask = np.zeros(n, dtype=bool)
+        mask[sel] = True
+        if not mask.any():
+            continue
+        z = scale * (q[t] @ rows.T)                  # [H, n]
+        z = np.where(mask[None, :], z, -np.inf)
+        m = z.max(axis=1, keepdims=True)
+        p = np.exp(z - m)
+        l = p.sum(axis=1, keepdims=True)
+        out[t] = (p @ rows[:, :d_v]) / l
+        lse[t] = m[:, 0] + np.log(l[:, 0])
+    return out, lse

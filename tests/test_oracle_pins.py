@@ -430,3 +430,46 @@ def test_cache_write_paged_equals_contiguous_and_touches_only_its_rows():
         return out
     p8, ps, pkv = O.cache_write(pages(k8), pages(ks), pages(kv), seq_id, pos, k_new, kv_new, block_table=bt)
     assert np.array_equal(p8, pages(a8)) and np.array_equal(ps, pages(as_)) and np.array_equal(pkv, pages(akv))
+
+
+# ----------------------------------------------------------------- masked dense variant
+
+def test_masked_dense_equals_sparse_attention():
+    rng = np.random.default_rng(9)
+    B, L, H, D = 2, 300, 4, 576
+    kv = I.bf16_bits((torch.randn(B, L, D) / 8).to(torch.bfloat16))
+    T = 5
+    q = I.bf16_bits((torch.randn(T, H, D) / 8).to(torch.bfloat16))
+    seq_id = rng.integers(0, B, T)
+    pos = np.array([0, 17, 150, 299, 260])
+    k = 64
+    idx = np.full((T, k), -1)
+    for t in range(T):
+        n = pos[t] + 1
+        sel = rng.permutation(n)[:min(k, n)]
+        idx[t, :len(sel)] = sel
+    idx[4] = -1                                           # an empty selection
+    od, ld = O.masked_dense_attention(q, kv, idx, seq_id, pos, 1 / 24)
+    os_, ls = O.sparse_mla_attention(q, kv, idx, seq_id, 1 / 24)
+    np.testing.assert_allclose(od, os_, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(ld[:4], ls[:4], rtol=1e-12)
+    assert np.all(od[4] == 0) and np.all(np.isneginf(ld[4]))
+
+
+def test_masked_dense_full_selection_is_causal_sdpa():
+    """Every position selected: plain causal attention of the query row."""
+    B, L, H, D = 1, 64, 3, 576
+    kv = I.bf16_bits((torch.randn(B, L, D) / 8).to(torch.bfloat16))
+    q = I.bf16_bits((torch.randn(2, H, D) / 8).to(torch.bfloat16))
+    pos = np.array([40, 63])
+    idx = np.full((2, 64), -1)
+    for t in range(2):
+        idx[t, :pos[t] + 1] = np.arange(pos[t] + 1)[::-1]
+    od, _ = O.masked_dense_attention(q, kv, idx, np.zeros(2, int), pos, 0.05)
+    qf = torch.from_numpy(O.decode_bf16(q))
+    kf = torch.from_numpy(O.decode_bf16(kv)[0])
+    for t in range(2):
+        n = pos[t] + 1
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qf[t][:, None, :], kf[:n][None].expand(H, n, D), kf[:n, :512][None].expand(H, n, 512), scale=0.05)
+        np.testing.assert_allclose(od[t], ref[:, 0].numpy(), rtol=1e-10, atol=1e-12)
