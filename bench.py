@@ -69,6 +69,8 @@ def parse():
     ap.add_argument("--config", default="decode128k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--crossover", action="store_true",
+                    help="time the masked dense attention against the sparse gather over context lengths")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 256 MiB device copies (reference dispatches for HBM counters)")
     return ap.parse_args()
@@ -262,6 +264,41 @@ def bench_prefill(args, cfg):
     print(json.dumps(out), flush=True)
 
 
+def bench_crossover(args):
+    """Sparse gather vs masked dense attention on the same top-2048 selection,
+    prefill (every token a query) and 16-sequence decode, L = 1K .. 16K: the
+    context length below which the dense variant is faster."""
+    import torch
+    from sparse_attention_long_03_amd import inputs as I
+    from sparse_attention_long_03_amd.path import DSAPath
+
+    stream = torch.cuda.current_stream()
+    n = max(args.steps // 5, 5)
+    series = {}
+    for kind, base in (("prefill", I.CONFIGS["prefill64k"]), ("decode_b16", I.CONFIGS["decode128k"])):
+        pts = []
+        for L in (1024, 2048, 4096, 8192, 16384):
+            cfg = I.scaled(base, L=L, planted_frac=0.0)
+            x = I.make_inputs(cfg, "cuda")
+            p = DSAPath(x)
+            idx = p.indexer_topk() if x.T >= 2048 else p.topk(p.indexer())
+            out, lse = torch.empty_like(p.out), torch.empty_like(p.lse)
+            sparse = lambda: p.attn(idx)
+            dense = lambda: p.dense_attn(idx, out, lse)
+            timed_rotation([sparse, dense], 4, stream)
+            ts = mean(timed_rotation([sparse], n, stream))
+            td = mean(timed_rotation([dense], n, stream))
+            pts.append({"L": L, "T": x.T, "sparse_ms": round(ts, 4), "dense_ms": round(td, 4),
+                        "rows_gathered": sum(min(int(q) + 1, cfg.k) for q in x.pos.tolist()),
+                        "rows_dense": int((x.pos.long() + 1).sum().item())})
+            del x, p, idx, out, lse
+            torch.cuda.empty_cache()
+        faster = [pt["L"] for pt in pts if pt["dense_ms"] < pt["sparse_ms"]]
+        series[kind] = {"points": pts, "dense_faster_up_to_L": max(faster) if faster else None}
+    print(json.dumps({"metric": "masked dense vs sparse attention time, same top-2048 selection", "unit": "ms",
+                      "n_gpus": 1, "data": "synthetic", "series": series}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -274,6 +311,9 @@ def main():
     from sparse_attention_long_03_amd.path import DSAPath
 
     torch.cuda.set_device(0)
+    if args.crossover:
+        bench_crossover(args)
+        return
     cfg = I.CONFIGS[args.config]
     if cfg.kind == "prefill":
         bench_prefill(args, cfg)

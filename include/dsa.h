@@ -191,6 +191,23 @@ int dsa_sparse_mla_attn(const dsa_queries* q, const dsa_kv_layout* layout, int32
                         float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * (3') Masked dense variant of (3) ("... Sparse Consideration (DSA)", "Lets
+ * Discuss it's effectivity and accuracy": at short lengths the prefill runs
+ * as a masked dense attention).  For query t every position s <= pos[t] of
+ * its sequence is read in order and scored; positions absent from idx[t, :]
+ * are masked out.  The result is that of dsa_sparse_mla_attn on the same
+ * idx (up to floating-point summation order); the rows are read contiguously
+ * instead of gathered.  Entries of idx outside 0..pos[t] are ignored, and a
+ * position listed twice counts once.
+ *
+ *   arguments : as for dsa_sparse_mla_attn; max_len <= 16384
+ *   workspace : device, >= dsa_workspace_bytes(DSA_OP_DENSE_ATTN, T, max_len, H, k)
+ * ------------------------------------------------------------------------- */
+int dsa_masked_dense_attn(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H, const void* q_bf16,
+                          const void* kv_bf16, const int32_t* idx, int32_t k, float sm_scale, void* out_bf16,
+                          float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * (1) -> (2) -> (3) on one stream ("FP8 index -> top-k selection -> sparse
  * core attention").  Arguments as above; idx_out (device int32[T, k]) receives
  * the selection, or may be NULL to keep it inside the workspace.  With
@@ -210,6 +227,7 @@ int dsa_forward(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, 
 #define DSA_OP_ATTN 2
 #define DSA_OP_FORWARD 3
 #define DSA_OP_INDEXER_TOPK 4
+#define DSA_OP_DENSE_ATTN 5
 size_t dsa_workspace_bytes(int32_t op, int32_t T, int32_t max_len, int32_t H, int32_t k);
 
 /* Static string for a status code (never NULL). */

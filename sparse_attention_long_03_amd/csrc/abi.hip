@@ -124,6 +124,7 @@ size_t dsa_workspace_bytes(int32_t op, int32_t T, int32_t max_len, int32_t H, in
     case DSA_OP_ATTN: return (H > 0 && k > 0) ? attn_workspace_bytes(T, H, k) : 0;
     case DSA_OP_FORWARD: return (H > 0 && k > 0) ? forward_ws(T, max_len, H, k, true) : 0;
     case DSA_OP_INDEXER_TOPK: return (k > 0) ? fused_topk_workspace_bytes(T, fused_topk_cap(max_len, k)) : 0;
+    case DSA_OP_DENSE_ATTN: return (H > 0) ? dense_attn_workspace_bytes(T, H, max_len) : 0;
     default: return 0;
   }
 }
@@ -197,6 +198,22 @@ int dsa_sparse_mla_attn(const dsa_queries* q, const dsa_kv_layout* layout, int32
   return hip_status(launch_attn(q->T, H, static_cast<const uint16_t*>(q_bf16), static_cast<const uint16_t*>(kv_bf16),
                                 idx, q->seq_id, lay, k, sm_scale, static_cast<uint16_t*>(out_bf16), lse, workspace,
                                 stream));
+}
+
+int dsa_masked_dense_attn(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H, const void* q_bf16,
+                          const void* kv_bf16, const int32_t* idx, int32_t k, float sm_scale, void* out_bf16,
+                          float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Layout lay;
+  int st = validate_attn(q, layout, H, q_bf16, kv_bf16, idx, k, sm_scale, out_bf16, &lay);
+  if (st) return st;
+  if (!dense_attn_supported(q->max_len)) return DSA_ERR_UNSUPPORTED;
+  if (q->T == 0) return DSA_OK;
+  const size_t need = dense_attn_workspace_bytes(q->T, H, q->max_len);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)))
+    return DSA_ERR_WORKSPACE;
+  return hip_status(launch_dense_attn(q->T, H, static_cast<const uint16_t*>(q_bf16),
+                                      static_cast<const uint16_t*>(kv_bf16), idx, q->seq_id, q->pos, lay, k,
+                                      q->max_len, sm_scale, static_cast<uint16_t*>(out_bf16), lse, workspace, stream));
 }
 
 int dsa_forward(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,

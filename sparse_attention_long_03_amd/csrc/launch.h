@@ -50,6 +50,13 @@ hipError_t launch_cache_write(int T, int D_I, const int32_t* seq_id, const int32
                               const float* k_new, const uint16_t* kv_new, uint8_t* k8, float* ks, uint16_t* kv,
                               hipStream_t stream);
 
+// (3') masked dense variant of (3): all positions 0..pos[t], unselected masked
+bool dense_attn_supported(int max_len);
+size_t dense_attn_workspace_bytes(int T, int H, int max_len);
+hipError_t launch_dense_attn(int T, int H, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                             const int32_t* seq_id, const int32_t* pos, const Layout& lay, int k, int max_len,
+                             float sm_scale, uint16_t* out, float* lse, void* ws, hipStream_t stream);
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace dsa

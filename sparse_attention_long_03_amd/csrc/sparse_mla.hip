@@ -176,11 +176,17 @@ __device__ __forceinline__ void attend_tile(const LDS_AS uint8_t* __restrict__ b
   }
 }
 
-template <int NW>
+// DENSE = false: the rows are the selected positions idx[t, :], gathered.
+// DENSE = true (the masked dense variant): the rows are all positions
+// 0..pos[t] of the token's sequence, read in order, and a row counts only if
+// its position is among idx[t, :] -- the same set, reached over contiguous
+// rows.  Splits then run over positions (at most 2048 per split).
+template <int NW, bool DENSE>
 __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(const uint16_t* __restrict__ q,
                                                              const uint8_t* __restrict__ kv,
                                                              const int32_t* __restrict__ idx,
-                                                             const int32_t* __restrict__ seq_id, Layout lay, int H,
+                                                             const int32_t* __restrict__ seq_id,
+                                                             const int32_t* __restrict__ pos, Layout lay, int H,
                                                              int k, int split_len, int n_splits, float scale_log2,
                                                              uint16_t* __restrict__ out, float* __restrict__ lse,
                                                              uint16_t* __restrict__ ws_o, float* __restrict__ ws_ml,
@@ -214,21 +220,40 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(const uint16_t* __r
   const int32_t* __restrict__ idx_row = idx + (int64_t)t * k;
 
   const int j_begin = split * split_len;
-  const int j_end = min(k, j_begin + split_len);
+  const int j_end = DENSE ? min(pos[t] + 1, j_begin + split_len) : min(k, j_begin + split_len);
   const int nrows = max(0, j_end - j_begin);
-  const int ntiles = (nrows + AT_TILE - 1) / AT_TILE;
+  int ntiles = (nrows + AT_TILE - 1) / AT_TILE;
 
   // physical rows of this split (padding and the ragged tail load a valid
   // row of the sequence and are masked), and one validity bit per row
   const int64_t safe_row = token_row(lay, b, 0);
-  for (int i0 = 0; i0 < ntiles * AT_TILE; i0 += NT) {
-    const int i = i0 + tid;
-    const int s = (i < nrows) ? idx_row[j_begin + i] : -1;
-    if (i < ntiles * AT_TILE) s_row[i] = (s >= 0) ? (u32)token_row(lay, b, s) : ((u32)safe_row | ROW_INVALID);
-    const uint64_t bits = __builtin_amdgcn_ballot_w64(s >= 0);
-    if (lane == 0 && i < ntiles * AT_TILE) {
-      s_valid[i >> 5] = (u32)bits;
-      if (i + 32 < ntiles * AT_TILE) s_valid[(i >> 5) + 1] = (u32)(bits >> 32);
+  if (!DENSE) {
+    // selected positions, compacted in order (padding entries -1 dropped:
+    // rows shorter than k carry many), then the tail of the last tile masked
+    __shared__ u32 scan_scratch[NT / 64 + 1];
+    int nvalid = 0;
+    for (int i0 = 0; i0 < nrows; i0 += NT) {
+      const int i = i0 + tid;
+      const int s = (i < nrows) ? idx_row[j_begin + i] : -1;
+      u32 tot;
+      const u32 incl = block_incl_scan<NT>(s >= 0 ? 1u : 0u, scan_scratch, &tot);
+      if (s >= 0) s_row[nvalid + (int)incl - 1] = (u32)token_row(lay, b, s);
+      nvalid += (int)tot;
+    }
+    ntiles = (nvalid + AT_TILE - 1) / AT_TILE;
+    for (int i = nvalid + tid; i < ntiles * AT_TILE; i += NT) s_row[i] = (u32)safe_row | ROW_INVALID;
+    for (int it = tid; it < ntiles; it += NT) {
+      const int left = nvalid - it * AT_TILE;
+      s_valid[it] = left >= AT_TILE ? 0xFFFFFFFFu : ((1u << left) - 1u);
+    }
+  } else {
+    for (int i = tid; i < ntiles * AT_TILE; i += NT)
+      s_row[i] = (i < nrows) ? (u32)token_row(lay, b, j_begin + i) : ((u32)safe_row | ROW_INVALID);
+    for (int i = tid; i < AT_MAX_SPLIT / AT_TILE; i += NT) s_valid[i] = 0;
+    __syncthreads();
+    for (int j = tid; j < k; j += NT) {
+      const int s = idx_row[j];
+      if (s >= j_begin && s < j_end) atomicOr(&s_valid[(s - j_begin) >> 5], 1u << ((s - j_begin) & 31));
     }
   }
 
@@ -386,21 +411,38 @@ int attn_splits(int T, int H, int k) {
   return s;
 }
 
-size_t attn_workspace_bytes(int T, int H, int k) {
-  const int s = attn_splits(T, H, k);
+// masked dense variant: splits over positions, at most AT_MAX_SPLIT each
+static int dense_splits(int T, int H, int max_len) {
+  const int tiles = (max_len + AT_TILE - 1) / AT_TILE;
+  int s = 1;
+  while (s * AT_MAX_SPLIT < max_len) s *= 2;
+  while (T * head_groups(H) * s < 256 && tiles / (2 * s) >= 4 && 2 * s <= AT_MAX_SPLITS) s *= 2;
+  return s;
+}
+
+bool dense_attn_supported(int max_len) { return max_len <= AT_MAX_SPLITS * AT_MAX_SPLIT; }
+
+static size_t split_workspace(int T, int H, int s) {
   if (s == 1) return 0;
   const size_t slots = (size_t)T * s * H;
   return align256(slots * AT_DV * 2) + align256(slots * 2 * 4);
 }
 
-hipError_t launch_attn(int T, int H, const uint16_t* q, const uint16_t* kv, const int32_t* idx, const int32_t* seq_id,
-                       const Layout& lay, int k, float sm_scale, uint16_t* out, float* lse, void* ws,
-                       hipStream_t stream) {
+size_t attn_workspace_bytes(int T, int H, int k) { return split_workspace(T, H, attn_splits(T, H, k)); }
+
+size_t dense_attn_workspace_bytes(int T, int H, int max_len) {
+  return split_workspace(T, H, dense_splits(T, H, max_len));
+}
+
+template <bool DENSE>
+static hipError_t launch_attn_t(int T, int H, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                                const int32_t* seq_id, const int32_t* pos, const Layout& lay, int k, int max_len,
+                                float sm_scale, uint16_t* out, float* lse, void* ws, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  const int nw = attn_waves(H);
   const int n_hg = head_groups(H);
-  const int n_splits = attn_splits(T, H, k);
-  const int tiles = (k + AT_TILE - 1) / AT_TILE;
+  const int n_splits = DENSE ? dense_splits(T, H, max_len) : attn_splits(T, H, k);
+  const int span = DENSE ? max_len : k;
+  const int tiles = (span + AT_TILE - 1) / AT_TILE;
   const int split_len = ((tiles + n_splits - 1) / n_splits) * AT_TILE;
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   uint16_t* ws_o = nullptr;
@@ -414,14 +456,25 @@ hipError_t launch_attn(int T, int H, const uint16_t* q, const uint16_t* kv, cons
   const int pairs = T * n_splits;
   const int blocks = ((pairs + 7) / 8) * 8 * n_hg;
   const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv);
-  (void)nw;
-  hipLaunchKernelGGL((sparse_mla_kernel<4>), dim3(blocks), dim3(4 * 64), 0, stream, q, kvb, idx, seq_id, lay, H, k,
-                     split_len, n_splits, scale_log2, out, lse, ws_o, ws_ml, T);
+  hipLaunchKernelGGL((sparse_mla_kernel<4, DENSE>), dim3(blocks), dim3(4 * 64), 0, stream, q, kvb, idx, seq_id, pos,
+                     lay, H, k, split_len, n_splits, scale_log2, out, lse, ws_o, ws_ml, T);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_splits == 1) return e;
   const int TH = T * H;
   hipLaunchKernelGGL(combine_kernel, dim3((TH + 3) / 4), dim3(256), 0, stream, ws_o, ws_ml, TH, H, n_splits, out, lse);
   return hipGetLastError();
+}
+
+hipError_t launch_attn(int T, int H, const uint16_t* q, const uint16_t* kv, const int32_t* idx, const int32_t* seq_id,
+                       const Layout& lay, int k, float sm_scale, uint16_t* out, float* lse, void* ws,
+                       hipStream_t stream) {
+  return launch_attn_t<false>(T, H, q, kv, idx, seq_id, nullptr, lay, k, 0, sm_scale, out, lse, ws, stream);
+}
+
+hipError_t launch_dense_attn(int T, int H, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                             const int32_t* seq_id, const int32_t* pos, const Layout& lay, int k, int max_len,
+                             float sm_scale, uint16_t* out, float* lse, void* ws, hipStream_t stream) {
+  return launch_attn_t<true>(T, H, q, kv, idx, seq_id, pos, lay, k, max_len, sm_scale, out, lse, ws, stream);
 }
 
 }  // namespace dsa

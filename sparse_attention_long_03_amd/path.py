@@ -83,6 +83,18 @@ class DSAPath:
                               self.ws(B.DSA_OP_ATTN), stream)
         return self.out, self.lse
 
+    def dense_attn(self, idx: torch.Tensor, out=None, lse=None, stream=None):
+        """The masked dense variant over the same selection (contiguous rows)."""
+        x, c = self.x, self.cfg
+        out = torch.empty_like(self.out) if out is None else out
+        lse = torch.empty_like(self.lse) if lse is None else lse
+        n = B.dsa_workspace_bytes(B.DSA_OP_DENSE_ATTN, self.T, x.max_len, c.H, idx.shape[1])
+        if ("dense", n) not in self._ws:
+            self._ws[("dense", n)] = B.workspace(n, self.dev)
+        B.dsa_masked_dense_attn(self.q, self.layout, c.H, x.q, x.kv, idx, idx.shape[1], c.scale, out, lse,
+                                self._ws[("dense", n)], stream)
+        return out, lse
+
     def forward(self, stream=None):
         x, c = self.x, self.cfg
         B.dsa_forward(self.q, self.layout, c.H_I, c.D_I, x.iq8, x.iqs, x.iw, x.ik8, x.iks, c.H, x.q, x.kv, c.k,

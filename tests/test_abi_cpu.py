@@ -171,3 +171,15 @@ def test_cache_write_validation(lib):
     assert f(ctypes.byref(q), ctypes.byref(_lay(cap=50)), 128, FAKE, None, FAKE, FAKE, None, None) == B.DSA_ERR_INVALID_ARG
     q0 = _q(T=0, seq=None, pos=None)
     assert f(ctypes.byref(q0), ctypes.byref(lay), 128, None, None, None, None, None, None) == B.DSA_OK
+
+
+def test_masked_dense_validation(lib):
+    f = lib.dsa_masked_dense_attn
+    q, lay = _q(max_len=100), _lay()
+    assert f(ctypes.byref(q), ctypes.byref(lay), 48, FAKE, FAKE, FAKE, 64, 0.1, FAKE, None, FAKE, 1 << 30, None) == B.DSA_ERR_UNSUPPORTED
+    big = _q(max_len=20000)
+    assert f(ctypes.byref(big), ctypes.byref(_lay(cap=20000)), 128, FAKE, FAKE, FAKE, 64, 0.1, FAKE, None, FAKE, 1 << 30, None) == B.DSA_ERR_UNSUPPORTED
+    need = B.dsa_workspace_bytes(B.DSA_OP_DENSE_ATTN, 4, 16384, 128, 2048)
+    assert need > 0
+    q16 = _q(max_len=16384)
+    assert f(ctypes.byref(q16), ctypes.byref(_lay(cap=16384)), 128, FAKE, FAKE, FAKE, 2048, 0.1, FAKE, None, FAKE, need - 1, None) == B.DSA_ERR_WORKSPACE

@@ -1,0 +1,70 @@
+"""GPU parity of the masked dense variant (dsa_masked_dense_attn): the same
+selection as the sparse gather, read over contiguous rows."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_attention_long_03_amd import binding as B
+from sparse_attention_long_03_amd import inputs as I
+from sparse_attention_long_03_amd.path import DSAPath
+
+from parity_util import bf16_to_np, check_attn, host_inputs, np_
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+CASES = {
+    # decode-like: 3 sequences of 5000 tokens, 2 queries each (several position splits)
+    "decode_5000": I.scaled(I.CONFIGS["decode32k"], B=3, L=5000, queries_per_seq=2),
+    # short prefill: every token a query, rows below k keep every position
+    "prefill_1500": I.scaled(I.CONFIGS["prefill64k"], L=1500, H=64, k=512),
+    # paged, ragged lengths
+    "paged": I.scaled(I.CONFIGS["ragged_paged"], B=4, L=3000, min_len=100, H=64, k=1024),
+    # the longest rows the variant takes
+    "decode_16k": I.scaled(I.CONFIGS["decode32k"], B=2, L=16384),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_dense_matches_sparse_and_oracle(name):
+    x = I.make_inputs(CASES[name], DEV)
+    p = DSAPath(x)
+    idx = p.topk(p.indexer())
+    o_s, l_s = (t.clone() for t in p.attn(idx))
+    o_d, l_d = p.dense_attn(idx)
+    torch.cuda.synchronize()
+    # against the sparse kernel on the same selection (summation order differs)
+    check_attn(bf16_to_np(o_d), bf16_to_np(o_s).astype(np.float64), f"{name} dense vs sparse")
+    np.testing.assert_allclose(np_(l_d), np_(l_s), rtol=1e-4, atol=1e-4)
+    # against the oracle's masked dense definition on a sample of queries
+    h = host_inputs(x)
+    rows = sorted({0, x.T // 2, x.T - 1})
+    ro, rl = O.masked_dense_attention(h["q"][rows], h["kv"], np_(idx)[rows], h["seq_id"][rows], h["pos"][rows],
+                                      x.cfg.scale, block_table=h["bt"])
+    check_attn(bf16_to_np(o_d[rows]), ro, f"{name} dense vs oracle")
+    np.testing.assert_allclose(np_(l_d)[rows], rl, rtol=1e-4, atol=1e-4)
+
+
+def test_dense_ignores_padding_and_out_of_range_entries():
+    cfg = I.scaled(I.CONFIGS["decode32k"], B=2, L=2000, H=32, k=300)
+    x = I.make_inputs(cfg, DEV)
+    p = DSAPath(x)
+    rng = np.random.default_rng(4)
+    idx = np.full((x.T, cfg.k), -1, np.int32)
+    for t in range(x.T):
+        n = int(x.pos[t]) + 1
+        sel = rng.permutation(n)[:200]
+        idx[t, :200] = sel
+        idx[t, 200] = n + 5          # past the query: ignored
+        idx[t, 201] = sel[0]         # a duplicate: counts once
+    o_d, l_d = p.dense_attn(torch.from_numpy(idx).to(DEV))
+    torch.cuda.synchronize()
+    clean = idx.copy()
+    clean[:, 200:] = -1
+    h = host_inputs(x)
+    ro, rl = O.sparse_mla_attention(h["q"], h["kv"], clean, h["seq_id"], cfg.scale)
+    check_attn(bf16_to_np(o_d), ro, "dense with padding")
+    np.testing.assert_allclose(np_(l_d), rl, rtol=1e-4, atol=1e-4)
