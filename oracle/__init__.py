@@ -27,4 +27,5 @@ from .dsa_oracle import (  # noqa: F401
     quantize_index_key,
     cache_write,
     masked_dense_attention,
+    sparse_mla_attention_backward,
 )

@@ -361,3 +361,64 @@ def masked_dense_attention(q_bits, kv_bits, idx, seq_id, pos, scale: float, d_v:
         out[t] = (p @ rows[:, :d_v]) / l
         lse[t] = m[:, 0] + np.log(l[:, 0])
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# (f3) Backward of the sparse MLA-MQA attention
+# ---------------------------------------------------------------------------
+#
+# [DSA-article] opening paragraph and "Teaching signal": DSA is a trainable
+# sparsification, the sparse stage training the main model through the
+# selected set.  With o = softmax(z) V over the selected rows i, z_i =
+# scale <q, kv_i>, V = kv[:, :512], and an output gradient dO, the gradients
+# follow from the chain rule:
+#   P_i = exp(z_i - lse),  dP_i = <dO, kv_i[:512]>,  D = <dO, o>,
+#   dZ_i = P_i (dP_i - D),
+#   dq = scale sum_i dZ_i kv_i[:576],
+#   dkv_i[:576] += scale sum_h dZ_hi q_h,   dkv_i[:512] += sum_h P_hi dO_h.
+# Several queries may select one row; their contributions add up.
+
+
+def sparse_mla_attention_backward(q_bits, kv_bits, idx, seq_id, scale: float, d_out, d_v: int = 512,
+                                  block_table=None, page_size: int = 64):
+    """(dq float64[T, H, D], dkv_sel float64[T, k, D], dkv float64[cache shape]).
+
+    dkv_sel[t, j] is the gradient reaching the row idx[t, j] from query t
+    (zero for padding); dkv adds them up per cache row.
+    """
+    q = decode_bf16(q_bits)
+    kv = decode_bf16(kv_bits)
+    d_out = np.asarray(d_out, dtype=np.float64)
+    T, H, D = q.shape
+    k = np.asarray(idx).shape[1]
+    dq = np.zeros((T, H, D))
+    dkv_sel = np.zeros((T, k, D))
+    dkv = np.zeros(kv.shape)
+    bt = None if block_table is None else np.asarray(block_table)
+    for t in range(T):
+        b = int(seq_id[t])
+        sel = np.asarray(idx[t])
+        js = np.nonzero(sel >= 0)[0]
+        if len(js) == 0:
+            continue
+        pos = sel[js]
+        if bt is None:
+            where = [(b, int(s)) for s in pos]
+        else:
+            where = [(int(bt[b, int(s) // page_size]), int(s) % page_size) for s in pos]
+        rows = np.stack([kv[w] for w in where])              # [n, D]
+        z = scale * (q[t] @ rows.T)                           # [H, n]
+        m = z.max(axis=1, keepdims=True)
+        p = np.exp(z - m)
+        p /= p.sum(axis=1, keepdims=True)                     # P_i = exp(z_i - lse)
+        o = p @ rows[:, :d_v]                                 # [H, d_v]
+        dP = d_out[t] @ rows[:, :d_v].T                       # [H, n]
+        Dh = np.sum(d_out[t] * o, axis=1, keepdims=True)      # [H, 1]
+        dZ = p * (dP - Dh)                                    # [H, n]
+        dq[t] = scale * (dZ @ rows)
+        g = scale * (dZ.T @ q[t])                             # [n, D]
+        g[:, :d_v] += p.T @ d_out[t]
+        dkv_sel[t, js] = g
+        for r, w in enumerate(where):
+            dkv[w] += g[r]
+    return dq, dkv_sel, dkv

@@ -473,3 +473,74 @@ def test_masked_dense_full_selection_is_causal_sdpa():
         ref = torch.nn.functional.scaled_dot_product_attention(
             qf[t][:, None, :], kf[:n][None].expand(H, n, D), kf[:n, :512][None].expand(H, n, 512), scale=0.05)
         np.testing.assert_allclose(od[t], ref[:, 0].numpy(), rtol=1e-10, atol=1e-12)
+
+
+# ----------------------------------------------------------------- attention backward
+
+def _bwd_case(rng, T=3, H=4, B=2, L=80, k=24, D=576):
+    kv = I.bf16_bits((torch.randn(B, L, D) / 6).to(torch.bfloat16))
+    q = I.bf16_bits((torch.randn(T, H, D) / 6).to(torch.bfloat16))
+    seq_id = np.array([0, 1, 1])[:T]
+    idx = np.full((T, k), -1)
+    for t in range(T):
+        n = rng.integers(5, k + 1)
+        idx[t, :n] = rng.choice(L, n, replace=False)
+    idx[2, :3] = idx[1, :3]          # two queries of one sequence share rows
+    dO = rng.normal(size=(T, H, 512))
+    return q, kv, idx, seq_id, dO
+
+
+def test_attention_backward_finite_differences():
+    rng = np.random.default_rng(10)
+    q, kv, idx, seq_id, dO = _bwd_case(rng)
+    scale = 1 / 24
+    dq, dkv_sel, dkv = O.sparse_mla_attention_backward(q, kv, idx, seq_id, scale, dO)
+    qf, kvf = O.decode_bf16(q), O.decode_bf16(kv)
+
+    def loss(qv, kvv):
+        # the forward on float64 values (the oracle decodes bf16 bits itself,
+        # so this wraps it through bits-free arithmetic of the same definition)
+        tot = 0.0
+        for t in range(qv.shape[0]):
+            sel = idx[t][idx[t] >= 0]
+            rows = kvv[seq_id[t], sel]
+            z = scale * qv[t] @ rows.T
+            p = np.exp(z - z.max(1, keepdims=True))
+            p /= p.sum(1, keepdims=True)
+            tot += np.sum(dO[t] * (p @ rows[:, :512]))
+        return tot
+    eps = 1e-6
+    for (t, h, d) in [(0, 1, 3), (1, 2, 500), (2, 0, 570)]:
+        e = np.zeros_like(qf); e[t, h, d] = eps
+        fd = (loss(qf + e, kvf) - loss(qf - e, kvf)) / (2 * eps)
+        assert abs(fd - dq[t, h, d]) <= 1e-6 * max(1.0, abs(fd))
+    for (b, s, d) in [(int(seq_id[0]), int(idx[0, 0]), 7), (1, int(idx[1, 0]), 511), (1, int(idx[1, 1]), 575)]:
+        e = np.zeros_like(kvf); e[b, s, d] = eps
+        fd = (loss(qf, kvf + e) - loss(qf, kvf - e)) / (2 * eps)
+        assert abs(fd - dkv[b, s, d]) <= 1e-6 * max(1.0, abs(fd))
+
+
+def test_attention_backward_matches_autograd():
+    rng = np.random.default_rng(11)
+    q, kv, idx, seq_id, dO = _bwd_case(rng)
+    scale = 1 / 24
+    dq, dkv_sel, dkv = O.sparse_mla_attention_backward(q, kv, idx, seq_id, scale, dO)
+    qt = torch.tensor(O.decode_bf16(q), requires_grad=True)
+    kvt = torch.tensor(O.decode_bf16(kv), requires_grad=True)
+    outs = []
+    for t in range(qt.shape[0]):
+        sel = torch.tensor(idx[t][idx[t] >= 0])
+        rows = kvt[int(seq_id[t])][sel]
+        outs.append(torch.nn.functional.scaled_dot_product_attention(
+            qt[t][:, None, :], rows[None].expand(qt.shape[1], -1, -1),
+            rows[:, :512][None].expand(qt.shape[1], -1, -1), scale=scale)[:, 0])
+    torch.autograd.backward(torch.stack(outs), torch.tensor(dO))
+    np.testing.assert_allclose(dq, qt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dkv, kvt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    # per-slot gradients add up to the per-row ones
+    acc = np.zeros_like(dkv)
+    for t in range(3):
+        for j in range(idx.shape[1]):
+            if idx[t, j] >= 0:
+                acc[seq_id[t], idx[t, j]] += dkv_sel[t, j]
+    np.testing.assert_allclose(acc, dkv, rtol=1e-12, atol=1e-14)
