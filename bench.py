@@ -43,9 +43,9 @@ REPLICAS = 4
 # device copy in the same pass.  Valid only for the kernel sources they were
 # taken on (hash below); otherwise the field is reported as null.
 TRAFFIC = {
-    "sources_sha256": "ff50f493e106f8e9ebeee27ecbc37506279bbbcb5f099d881d55392c2b50cdf5",
-    # FETCH_SIZE 135758.6 KiB/launch x 1.99982 (copy: 131083.9 KiB counted for 262144 KiB read)
-    "fetch_bytes": 278008363,
+    "sources_sha256": "ce18cf7f112a8375f525873aadd7c78331236a63fccad0841ab8a8e711e1ce2b",
+    # FETCH_SIZE 135759.4 KiB/launch x 1.99982 (copy: 131084.0 KiB counted for 262144 KiB read)
+    "fetch_bytes": 278009696,
     # WRITE_SIZE 8192.0 KiB/launch x 1.0 (copy: 262144 KiB counted for 262144 KiB written)
     "write_bytes": 8388608,
 }
