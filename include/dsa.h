@@ -191,6 +191,39 @@ int dsa_sparse_mla_attn(const dsa_queries* q, const dsa_kv_layout* layout, int32
                         float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * (3b) Backward of (3) ("... Sparse Consideration (DSA)", opening paragraph
+ * and "Teaching signal": the sparse path is trained).  Given the forward's
+ * out and lse for the same q, kv and idx, and the output gradient d_out, with
+ * P_i = exp(z_i - lse), dP_i = <d_out[t,h], kv_row_i[0:512]>,
+ * D = <d_out[t,h], out[t,h]> and dS_i = P_i (dP_i - D):
+ *     dq[t,h,:]       = sm_scale * sum_i dS_i * kv_row_i[0:576]
+ *     dkv[row_i, :]  += sm_scale * sum_h dS_hi * q[t,h,:]
+ *     dkv[row_i, c]  += sum_h P_hi * d_out[t,h,c],   c < 512
+ * summed over every query t and selected entry i (a row selected twice by one
+ * query, or by several queries, receives every contribution).  P and dS are
+ * rounded to bf16 for the products, as are the per-entry row gradients before
+ * they are summed in fp32; the order of the fp32 sums into dkv is not fixed.
+ *
+ *   arguments : q, layout, H, q_bf16, kv_bf16, idx, k, sm_scale as for
+ *               dsa_sparse_mla_attn (the same values as the forward call)
+ *   out_bf16  : device bf16[T, H, 512]  the forward's output (16-byte aligned)
+ *   lse       : device float[T, H]      the forward's log-sum-exp
+ *   d_out_bf16: device bf16[T, H, 512]  gradient of the output (16-byte aligned)
+ *   dq        : device float[T, H, 576] written (16-byte aligned)
+ *   dkv       : device float cache, 576 per token in the layout of kv_bf16
+ *               (B * seq_capacity rows, or num_pages * 64); the gradients are
+ *               ADDED to it (zero it first for a plain gradient); rows no
+ *               query selected are not touched.  16-byte aligned.
+ *   workspace : device, >= dsa_workspace_bytes(DSA_OP_ATTN_BWD, T, 0, H, k),
+ *               256-byte aligned; about k * (4H + 1168) bytes per query token.
+ *   limits    : T * roundup(k, 32) < 2^31; fewer than 2^31 cache rows.
+ * ------------------------------------------------------------------------- */
+int dsa_sparse_mla_attn_bwd(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H, const void* q_bf16,
+                            const void* kv_bf16, const int32_t* idx, int32_t k, float sm_scale, const void* out_bf16,
+                            const float* lse, const void* d_out_bf16, float* dq, float* dkv, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * (3') Masked dense variant of (3) ("... Sparse Consideration (DSA)", "Lets
  * Discuss it's effectivity and accuracy": at short lengths the prefill runs
  * as a masked dense attention).  For query t every position s <= pos[t] of
@@ -228,6 +261,7 @@ int dsa_forward(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, 
 #define DSA_OP_FORWARD 3
 #define DSA_OP_INDEXER_TOPK 4
 #define DSA_OP_DENSE_ATTN 5
+#define DSA_OP_ATTN_BWD 6
 size_t dsa_workspace_bytes(int32_t op, int32_t T, int32_t max_len, int32_t H, int32_t k);
 
 /* Static string for a status code (never NULL). */

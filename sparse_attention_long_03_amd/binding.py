@@ -22,7 +22,7 @@ DSA_ERR_INVALID_ARG = -1
 DSA_ERR_UNSUPPORTED = -2
 DSA_ERR_WORKSPACE = -3
 DSA_ERR_HIP = -4
-DSA_OP_TOPK, DSA_OP_ATTN, DSA_OP_FORWARD, DSA_OP_INDEXER_TOPK, DSA_OP_DENSE_ATTN = 1, 2, 3, 4, 5
+DSA_OP_TOPK, DSA_OP_ATTN, DSA_OP_FORWARD, DSA_OP_INDEXER_TOPK, DSA_OP_DENSE_ATTN, DSA_OP_ATTN_BWD = 1, 2, 3, 4, 5, 6
 
 
 class DSAError(RuntimeError):
@@ -42,7 +42,8 @@ class dsa_kv_layout(ctypes.Structure):
 
 
 EXPORTS = ("dsa_cache_write", "dsa_indexer_logits", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_attn",
-           "dsa_masked_dense_attn", "dsa_forward", "dsa_workspace_bytes", "dsa_status_str", "dsa_abi_version")
+           "dsa_sparse_mla_attn_bwd", "dsa_masked_dense_attn", "dsa_forward", "dsa_workspace_bytes",
+           "dsa_status_str", "dsa_abi_version")
 
 _lib = None
 
@@ -62,6 +63,7 @@ def lib() -> ctypes.CDLL:
     L.dsa_indexer_topk.argtypes = [Q, KV, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
     L.dsa_topk.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp, sz, vp]
     L.dsa_sparse_mla_attn.argtypes = [Q, KV, i32, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
+    L.dsa_sparse_mla_attn_bwd.argtypes = [Q, KV, i32, vp, vp, vp, i32, f32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_masked_dense_attn.argtypes = [Q, KV, i32, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
     L.dsa_forward.argtypes = [Q, KV, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]
     L.dsa_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
@@ -70,7 +72,7 @@ def lib() -> ctypes.CDLL:
     L.dsa_status_str.restype = ctypes.c_char_p
     L.dsa_abi_version.restype = i32
     for name in ("dsa_cache_write", "dsa_indexer_logits", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_attn",
-                 "dsa_masked_dense_attn", "dsa_forward"):
+                 "dsa_sparse_mla_attn_bwd", "dsa_masked_dense_attn", "dsa_forward"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -175,6 +177,16 @@ def dsa_sparse_mla_attn(q: dsa_queries, layout: dsa_kv_layout, H: int, q_bf16, k
                                    int(k), float(sm_scale), _ptr(out_bf16), _ptr(lse), _ptr(ws), nbytes,
                                    _stream(stream))
     _check(st, "dsa_sparse_mla_attn")
+
+
+def dsa_sparse_mla_attn_bwd(q: dsa_queries, layout: dsa_kv_layout, H: int, q_bf16, kv_bf16, idx: torch.Tensor, k: int,
+                            sm_scale: float, out_bf16, lse, d_out_bf16, dq, dkv, ws: Optional[torch.Tensor] = None,
+                            stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib().dsa_sparse_mla_attn_bwd(ctypes.byref(q), ctypes.byref(layout), H, _ptr(q_bf16), _ptr(kv_bf16),
+                                       _ptr(idx), int(k), float(sm_scale), _ptr(out_bf16), _ptr(lse),
+                                       _ptr(d_out_bf16), _ptr(dq), _ptr(dkv), _ptr(ws), nbytes, _stream(stream))
+    _check(st, "dsa_sparse_mla_attn_bwd")
 
 
 def dsa_masked_dense_attn(q: dsa_queries, layout: dsa_kv_layout, H: int, q_bf16, kv_bf16, idx: torch.Tensor, k: int,

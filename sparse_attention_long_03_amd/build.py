@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
-SOURCES = ["abi.hip", "cache_write.hip", "indexer.hip", "indexer_topk.hip", "topk.hip", "sparse_mla.hip"]
+SOURCES = ["abi.hip", "cache_write.hip", "indexer.hip", "indexer_topk.hip", "topk.hip", "sparse_mla.hip",
+           "sparse_mla_bwd.hip"]
 ARCH = "gfx950"
 
 

@@ -125,6 +125,7 @@ size_t dsa_workspace_bytes(int32_t op, int32_t T, int32_t max_len, int32_t H, in
     case DSA_OP_FORWARD: return (H > 0 && k > 0) ? forward_ws(T, max_len, H, k, true) : 0;
     case DSA_OP_INDEXER_TOPK: return (k > 0) ? fused_topk_workspace_bytes(T, fused_topk_cap(max_len, k)) : 0;
     case DSA_OP_DENSE_ATTN: return (H > 0) ? dense_attn_workspace_bytes(T, H, max_len) : 0;
+    case DSA_OP_ATTN_BWD: return (H > 0 && k > 0 && attn_bwd_size_ok(T, k)) ? attn_bwd_workspace_bytes(T, H, k) : 0;
     default: return 0;
   }
 }
@@ -214,6 +215,27 @@ int dsa_masked_dense_attn(const dsa_queries* q, const dsa_kv_layout* layout, int
   return hip_status(launch_dense_attn(q->T, H, static_cast<const uint16_t*>(q_bf16),
                                       static_cast<const uint16_t*>(kv_bf16), idx, q->seq_id, q->pos, lay, k,
                                       q->max_len, sm_scale, static_cast<uint16_t*>(out_bf16), lse, workspace, stream));
+}
+
+int dsa_sparse_mla_attn_bwd(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H, const void* q_bf16,
+                            const void* kv_bf16, const int32_t* idx, int32_t k, float sm_scale, const void* out_bf16,
+                            const float* lse, const void* d_out_bf16, float* dq, float* dkv, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  Layout lay;
+  int st = validate_attn(q, layout, H, q_bf16, kv_bf16, idx, k, sm_scale, out_bf16, &lay);
+  if (st) return st;
+  if (!attn_bwd_supported(H)) return DSA_ERR_UNSUPPORTED;
+  const int64_t num_rows = layout->paged ? (int64_t)layout->num_pages * 64 : (int64_t)q->B * layout->seq_capacity;
+  if (num_rows >= (int64_t(1) << 31) || !attn_bwd_size_ok(q->T, k)) return DSA_ERR_UNSUPPORTED;
+  if (q->T == 0) return DSA_OK;
+  if (!lse || !d_out_bf16 || !dq || !dkv) return DSA_ERR_INVALID_ARG;
+  if (!aligned(d_out_bf16, 16) || !aligned(dq, 16) || !aligned(dkv, 16)) return DSA_ERR_INVALID_ARG;
+  const size_t need = attn_bwd_workspace_bytes(q->T, H, k);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)) return DSA_ERR_WORKSPACE;
+  return hip_status(launch_attn_bwd(q->T, H, static_cast<const uint16_t*>(q_bf16),
+                                    static_cast<const uint16_t*>(kv_bf16), idx, q->seq_id, lay, num_rows, k, sm_scale,
+                                    static_cast<const uint16_t*>(out_bf16), lse,
+                                    static_cast<const uint16_t*>(d_out_bf16), dq, dkv, workspace, stream));
 }
 
 int dsa_forward(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,

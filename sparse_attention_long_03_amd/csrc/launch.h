@@ -57,6 +57,16 @@ hipError_t launch_dense_attn(int T, int H, const uint16_t* q, const uint16_t* kv
                              const int32_t* seq_id, const int32_t* pos, const Layout& lay, int k, int max_len,
                              float sm_scale, uint16_t* out, float* lse, void* ws, hipStream_t stream);
 
+// (3) backward: dq, and the gradients of the selected rows added into dkv
+// (fp32, 576 per cache row; num_rows = rows of the cache)
+bool attn_bwd_supported(int H);
+bool attn_bwd_size_ok(int T, int k);
+size_t attn_bwd_workspace_bytes(int T, int H, int k);
+hipError_t launch_attn_bwd(int T, int H, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                           const int32_t* seq_id, const Layout& lay, int64_t num_rows, int k, float sm_scale,
+                           const uint16_t* out, const float* lse, const uint16_t* dout, float* dq, float* dkv,
+                           void* ws, hipStream_t stream);
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace dsa

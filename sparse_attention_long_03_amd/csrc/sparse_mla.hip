@@ -26,20 +26,10 @@
 //            (the LDS transpose read of gfx950), and P already sits in the
 //            B-operand layout, so P never leaves registers.
 // The exponentials use exp2 with log2(e) folded into the scale.
+#include "attn_tile.h"
 #include "launch.h"
 
 namespace dsa {
-
-constexpr int AT_TILE = 32;
-constexpr int AT_D = 576;
-constexpr int AT_DV = 512;
-constexpr int AT_ROW_BYTES = AT_D * 2;              // 1152
-constexpr int NOPE_STRIDE = 1040;                   // 1024 B + 16 B: rotates LDS banks per row
-constexpr int NOPE_BYTES = AT_TILE * NOPE_STRIDE;   // 33280
-constexpr int ROPE_BYTES = AT_TILE * 128;           // 4096
-constexpr int BUF_BYTES = NOPE_BYTES + ROPE_BYTES;  // 37376
-constexpr int AT_MAX_SPLIT = 2048;                  // rows per split (k <= 2048)
-constexpr u32 ROW_INVALID = 0x80000000u;
 
 // Online-softmax reference maximum: P = exp2(z - m_ref) may grow to
 // 2^RESCALE_SLACK before O and l are rescaled to a new reference, so the
@@ -47,56 +37,6 @@ constexpr u32 ROW_INVALID = 0x80000000u;
 // -- a few times per split instead of every tile.  The result is exact: the
 // normalisation divides by l accumulated against the same reference.
 constexpr float RESCALE_SLACK = 8.f;
-
-typedef short v4s __attribute__((ext_vector_type(4)));
-#define LDS_AS __attribute__((address_space(3)))
-
-// s_waitcnt immediates (gfx9 encoding): at most N vector-memory loads of
-// this wave outstanding / every LDS access of this wave done; nothing else
-#define DSA_VMCNT(N) (((N) & 0xF) | (((N) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
-#define DSA_LGKMCNT0 (0xF | (0x3 << 14) | (0x7 << 4))
-
-// float -> bf16 bits, round to nearest even (gfx950 converts natively)
-__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
-
-// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses,
-// not for its global loads, so the next tile's loads stay in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(DSA_LGKMCNT0);
-  __builtin_amdgcn_s_barrier();
-}
-
-// A tile is 32 rows x 72 chunks of 16 bytes.  With NT threads, TPR = NT/32
-// threads share a row: thread tid takes row tid/TPR and chunks tid%TPR + TPR*r.
-// Every address is one row base plus an immediate offset; a wave reads whole
-// 128-byte lines of 64/TPR rows per load.
-template <int NT>
-struct TileStage {
-  static constexpr int TPR = NT / AT_TILE;
-  static constexpr int PER = (72 + TPR - 1) / TPR;
-  v4i v[PER];
-
-  __device__ __forceinline__ void load(const uint8_t* __restrict__ kv, const u32* rows, int tid) {
-    const int c0 = tid % TPR;
-    const u32 phys = rows[tid / TPR] & ~ROW_INVALID;
-    const uint8_t* src = kv + (int64_t)phys * AT_ROW_BYTES + 16 * c0;
-#pragma unroll
-    for (int r = 0; r < PER; ++r)
-      if (72 % TPR == 0 || c0 + TPR * r < 72) v[r] = *reinterpret_cast<const v4i*>(src + 16 * TPR * r);
-  }
-  // no-rope chunks row-major (padded rows); rope chunk cc of row r in slot cc^(r&7)
-  __device__ __forceinline__ void store(LDS_AS uint8_t* buf, int tid) const {
-    const int row = tid / TPR, c0 = tid % TPR;
-#pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const int c = c0 + TPR * r;
-      if (c < 64)
-        *reinterpret_cast<LDS_AS v4i*>(buf + row * NOPE_STRIDE + 16 * c) = v[r];
-      else if (c < 72)
-        *reinterpret_cast<LDS_AS v4i*>(buf + NOPE_BYTES + row * 128 + 16 * ((c - 64) ^ (row & 7))) = v[r];
-    }
-  }
-};
 
 // Scores, online softmax and value product for one tile held in `buf`.
 // `valid` has bit j set when row j of the tile is a selected row.
@@ -231,21 +171,8 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(const uint16_t* __r
     // selected positions, compacted in order (padding entries -1 dropped:
     // rows shorter than k carry many), then the tail of the last tile masked
     __shared__ u32 scan_scratch[NT / 64 + 1];
-    int nvalid = 0;
-    for (int i0 = 0; i0 < nrows; i0 += NT) {
-      const int i = i0 + tid;
-      const int s = (i < nrows) ? idx_row[j_begin + i] : -1;
-      u32 tot;
-      const u32 incl = block_incl_scan<NT>(s >= 0 ? 1u : 0u, scan_scratch, &tot);
-      if (s >= 0) s_row[nvalid + (int)incl - 1] = (u32)token_row(lay, b, s);
-      nvalid += (int)tot;
-    }
+    const int nvalid = compact_selection<NT>(idx_row + j_begin, nrows, lay, b, s_row, s_valid, scan_scratch, tid);
     ntiles = (nvalid + AT_TILE - 1) / AT_TILE;
-    for (int i = nvalid + tid; i < ntiles * AT_TILE; i += NT) s_row[i] = (u32)safe_row | ROW_INVALID;
-    for (int it = tid; it < ntiles; it += NT) {
-      const int left = nvalid - it * AT_TILE;
-      s_valid[it] = left >= AT_TILE ? 0xFFFFFFFFu : ((1u << left) - 1u);
-    }
   } else {
     for (int i = tid; i < ntiles * AT_TILE; i += NT)
       s_row[i] = (i < nrows) ? (u32)token_row(lay, b, j_begin + i) : ((u32)safe_row | ROW_INVALID);

@@ -1,0 +1,659 @@
+// Backward of the sparse attention under MLA in MQA mode, on gfx950.
+//
+// "DeepSeek V3.2-Exp Cuts Prolonged-Context Costs With DeepSeek Sparse
+// Consideration (DSA)", opening paragraph and "Teaching signal": the sparse
+// path is trained, so gradients flow through the selected rows.  For query t,
+// head h and its selected rows i (z = scale q.kv_i, P = softmax(z) restored
+// from the forward's log-sum-exp, V = kv[:, :512], dO the output gradient):
+//   dP_i = dO . V_i,  D = dO . O,  dS_i = P_i (dP_i - D)
+//   dq   = scale sum_i dS_i kv_i
+//   dkv_i += scale sum_h dS_hi q_h   (+ sum_h P_hi dO_h on the first 512)
+// Every query's heads share its rows (MQA), so a row's gradient is a
+// contraction over heads, and a cache row selected by several queries
+// collects all their contributions.
+//
+// Four steps, chosen for the memory system of the MI355X:
+//   1. dq kernel, per (token, 64 heads): the forward's row gather and tile
+//      pipeline; per tile it rebuilds S and dP (the no-rope K fragments feed
+//      both), then P and dS in registers, accumulates dq^T += K^T dS^T with
+//      K^T read through the LDS transpose read, and stores P and scale*dS as
+//      bf16 per (token, head, slot).
+//   2. stable LSD radix sort of the selected cache rows of all (token, slot)
+//      pairs (8-bit digits).
+//   3. slot kernel, per token, all heads: the gradient of each selected slot,
+//      [scale dS; P]^T [q; dO] -- a contraction over 2H stacked rows -- on
+//      bf16 MFMAs.  q and dO are constant per token, so each wave keeps its
+//      slice of [q; dO]^T in registers (read once through the LDS transpose
+//      read) and streams the P / dS tiles; one bf16 row of 576 per slot.
+//   4. segmented reduction: the sorted (row, slot) list is cut into chunks of
+//      256; a wave sums each run of equal rows of its chunk in fp32 and adds
+//      it to the fp32 dkv row with one atomic per value.
+// fp32 atomics reach only about a fifth of the store bandwidth on this GPU,
+// so adding every slot's gradient straight into dkv (T * k * 576 atomics)
+// would cost several times steps 3 and 4 together; the sort reduces the
+// atomics to one per (run, value).
+#include "attn_tile.h"
+#include "launch.h"
+
+namespace dsa {
+
+constexpr u32 SLOT_NONE = 0xFFFFFFFFu;  // row list entry past a token's selected slots
+constexpr float LOG2E = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// 1. dq, P and dS
+// ---------------------------------------------------------------------------
+
+// One tile in `buf`: rebuild S and dP, form P and dS, store them, and add
+// K^T dS^T to the dq accumulator.  Lane (n, g) holds head n; its score
+// registers cover keys 4g..4g+3 and 16+4g..16+4g+3 of the tile.
+__device__ __forceinline__ void dq_tile(const LDS_AS uint8_t* __restrict__ buf, u32 valid, const v8bf* qf,
+                                        const v8bf* dof, float scale_log2, float lse2, float dsum, float sm_scale,
+                                        int n, int g, v4f* acc, uint16_t* __restrict__ ds_row,
+                                        uint16_t* __restrict__ p_row, bool store) {
+  const LDS_AS uint8_t* nope = buf;
+  const LDS_AS uint8_t* rope = buf + NOPE_BYTES;
+  constexpr int SPIPE = 4;
+  auto frag = [&](int ks, int r) -> v8bf {
+    if (ks < 16) return *reinterpret_cast<const LDS_AS v8bf*>(nope + r * NOPE_STRIDE + 64 * ks + 16 * g);
+    const int c = 4 * (ks - 16) + g;
+    return *reinterpret_cast<const LDS_AS v8bf*>(rope + r * 128 + 16 * (c ^ (r & 7)));
+  };
+  v8bf ra0[SPIPE], ra1[SPIPE];
+#pragma unroll
+  for (int j = 0; j < SPIPE; ++j) {
+    ra0[j] = frag(j, n);
+    ra1[j] = frag(j, 16 + n);
+  }
+  // S^T = K Q^T and dP^T = V dO^T; the no-rope fragments (V) serve both
+  v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, d0 = s0, d1 = s0;
+#pragma unroll
+  for (int ks = 0; ks < AT_D / 32; ++ks) {
+    const int slot = ks % SPIPE;
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra0[slot], qf[ks], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra1[slot], qf[ks], s1, 0, 0, 0);
+    if (ks < AT_DV / 32) {
+      d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra0[slot], dof[ks], d0, 0, 0, 0);
+      d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra1[slot], dof[ks], d1, 0, 0, 0);
+    }
+    if (ks + SPIPE < AT_D / 32) {
+      ra0[slot] = frag(ks + SPIPE, n);
+      ra1[slot] = frag(ks + SPIPE, 16 + n);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // P = exp(z - lse) (0 for masked rows) and scale * dS = scale * P (dP - D)
+  v8bf pb, db;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float p0 = ((valid >> (4 * g + i)) & 1u) ? exp2f(s0[i] * scale_log2 - lse2) : 0.f;
+    const float p1 = ((valid >> (16 + 4 * g + i)) & 1u) ? exp2f(s1[i] * scale_log2 - lse2) : 0.f;
+    pb[i] = (__bf16)p0;
+    pb[4 + i] = (__bf16)p1;
+    db[i] = (__bf16)(p0 * (d0[i] - dsum) * sm_scale);
+    db[4 + i] = (__bf16)(p1 * (d1[i] - dsum) * sm_scale);
+  }
+  if (store) {
+    const v4i pv = __builtin_bit_cast(v4i, pb), dv = __builtin_bit_cast(v4i, db);
+    *reinterpret_cast<v2i*>(p_row + 4 * g) = v2i{pv[0], pv[1]};
+    *reinterpret_cast<v2i*>(p_row + 16 + 4 * g) = v2i{pv[2], pv[3]};
+    *reinterpret_cast<v2i*>(ds_row + 4 * g) = v2i{dv[0], dv[1]};
+    *reinterpret_cast<v2i*>(ds_row + 16 + 4 * g) = v2i{dv[2], dv[3]};
+  }
+  // dq^T += K^T (scale dS)^T: K^T through the LDS transpose read.  Source
+  // lane n of group g points at rows 4g + n/4 (and 16 rows on), dims
+  // 16mt + 4(n%4)..+3, so the fragment's K order is the keys' order in db.
+  const LDS_AS uint8_t* vsrc0 = nope + (4 * g + (n >> 2)) * NOPE_STRIDE + 8 * (n & 3);
+  const LDS_AS uint8_t* vsrc1 = vsrc0 + 16 * NOPE_STRIDE;
+#pragma unroll
+  for (int mt = 0; mt < AT_DV / 16; ++mt) {
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(vsrc0 + 32 * mt));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(vsrc1 + 32 * mt));
+    const v8bf av = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, db, acc[mt], 0, 0, 0);
+    if ((mt & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+  }
+  // rope dims: the same rows, with the chunk swizzle of the rope block
+  {
+    const int r = 4 * g + (n >> 2);
+#pragma unroll
+    for (int mr = 0; mr < 4; ++mr) {
+      const int c = 2 * mr + ((n & 3) >> 1);
+      const LDS_AS uint8_t* src = rope + r * 128 + 16 * (c ^ (r & 7)) + 8 * (n & 1);
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)src);
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(src + 16 * 128));
+      const v8bf av = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[32 + mr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, db, acc[32 + mr], 0, 0, 0);
+    }
+  }
+}
+
+// Workgroup = (token, 16*NW heads); 16 heads per wave.  Outputs: dq, the
+// P / scale*dS rows of the token (dsp: [T][2H][kp], rows h: scale*dS of head
+// h, rows H+h: P), and, from head group 0, the token's compacted row list
+// (rows_out[t*kp + c], SLOT_NONE past the selected slots) and count.
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void sparse_mla_bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ seq_id, Layout lay, int H, int k, int kp, float sm_scale,
+    const uint16_t* __restrict__ out, const float* __restrict__ lse, const uint16_t* __restrict__ dout,
+    float* __restrict__ dq, uint16_t* __restrict__ dsp, u32* __restrict__ rows_out, int32_t* __restrict__ cnt_out,
+    int n_tokens) {
+  constexpr int NT = NW * 64;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF_BYTES];
+  __shared__ u32 s_row[AT_MAX_SPLIT];
+  __shared__ u32 s_valid[AT_MAX_SPLIT / AT_TILE];
+  __shared__ u32 scan_scratch[NW + 1];
+
+  // head groups of one token on one XCD, in consecutive slots (shared rows
+  // come from that XCD's L2 for the second)
+  const int n_hg = H / (16 * NW) > 0 ? H / (16 * NW) : 1;
+  const int lin = blockIdx.x;
+  const int slot = lin >> 3;
+  const int t = (lin & 7) + 8 * (slot / n_hg);
+  const int hg = slot - (slot / n_hg) * n_hg;
+  if (t >= n_tokens) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int h0 = hg * (16 * NW) + wid * 16;
+  const bool has_heads = h0 < H;
+  const int b = seq_id[t];
+
+  const int nvalid = compact_selection<NT>(idx + (int64_t)t * k, k, lay, b, s_row, s_valid, scan_scratch, tid);
+  const int ntiles = (nvalid + AT_TILE - 1) / AT_TILE;
+
+  // Q^T and dO^T operands of head h0+n (dims 32ks + 8g..+8), and D = dO . O
+  const int hq = (has_heads ? h0 : 0) + n;
+  const int64_t th = (int64_t)t * H + hq;
+  v8bf qf[AT_D / 32], dof[AT_DV / 32];
+#pragma unroll
+  for (int ks = 0; ks < AT_D / 32; ++ks) qf[ks] = *reinterpret_cast<const v8bf*>(q + th * AT_D + 32 * ks + 8 * g);
+  float dsum = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < AT_DV / 32; ++ks) {
+    dof[ks] = *reinterpret_cast<const v8bf*>(dout + th * AT_DV + 32 * ks + 8 * g);
+    const v8bf o = *reinterpret_cast<const v8bf*>(out + th * AT_DV + 32 * ks + 8 * g);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dsum += (float)dof[ks][i] * (float)o[i];
+  }
+  dsum += __shfl_xor(dsum, 16, 64);
+  dsum += __shfl_xor(dsum, 32, 64);
+  const float lse2 = lse[th] * LOG2E;
+  const float scale_log2 = sm_scale * LOG2E;
+  uint16_t* ds_base = dsp + ((int64_t)t * 2 * H + hq) * kp;
+  uint16_t* p_base = ds_base + (int64_t)H * kp;
+
+  v4f acc[AT_D / 16];
+#pragma unroll
+  for (int mt = 0; mt < AT_D / 16; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
+  __syncthreads();  // s_row / s_valid visible
+  if (hg == 0) {
+    for (int c = tid; c < kp; c += NT) rows_out[(int64_t)t * kp + c] = (c < nvalid) ? s_row[c] : SLOT_NONE;
+    if (tid == 0) cnt_out[t] = nvalid;
+  }
+  // the forward's two-stage gather pipeline (tiles past the last re-read it
+  // and are masked out)
+  TileStage<NT> sa, sb;
+  auto tile_rows = [&](int i) { return s_row + min(i, ntiles - 1) * AT_TILE; };
+  if (ntiles > 0) {
+    sa.load(kv, tile_rows(0), tid);
+    sa.store(lds, tid);
+    sa.load(kv, tile_rows(1), tid);
+    sb.load(kv, tile_rows(2), tid);
+  }
+  __builtin_amdgcn_s_waitcnt(DSA_VMCNT(2 * TileStage<NT>::PER));
+  for (int it = 0; it < ntiles; it += 2) {
+    lds_barrier();
+    dq_tile(lds, s_valid[it], qf, dof, scale_log2, lse2, dsum, sm_scale, n, g, acc, ds_base + it * AT_TILE,
+            p_base + it * AT_TILE, has_heads);
+    sa.store(lds + BUF_BYTES, tid);
+    sa.load(kv, tile_rows(it + 3), tid);
+    lds_barrier();
+    dq_tile(lds + BUF_BYTES, (it + 1 < ntiles) ? s_valid[it + 1] : 0u, qf, dof, scale_log2, lse2, dsum, sm_scale, n,
+            g, acc, ds_base + (it + 1) * AT_TILE, p_base + (it + 1) * AT_TILE, has_heads && it + 1 < ntiles);
+    sb.store(lds, tid);
+    sb.load(kv, tile_rows(it + 4), tid);
+  }
+  if (!has_heads) return;
+  // lane (n, g) holds dq^T[16mt + 4g + i][head n]
+  float* dq_row = dq + th * AT_D + 4 * g;
+#pragma unroll
+  for (int mt = 0; mt < AT_D / 16; ++mt) *reinterpret_cast<v4f*>(dq_row + 16 * mt) = acc[mt];
+}
+
+// ---------------------------------------------------------------------------
+// 2. stable LSD radix sort of the row list (8-bit digits)
+// ---------------------------------------------------------------------------
+
+constexpr int RS_NT = 256;
+constexpr int RS_ROUNDS = 16;
+constexpr int RS_BLOCK = RS_NT * RS_ROUNDS;  // elements per block
+
+// per-block digit counts, digit-major: hist[d * nblocks + block]
+__global__ __launch_bounds__(RS_NT) void radix_hist_kernel(const u32* __restrict__ keys, int N, int shift,
+                                                            u32* __restrict__ hist, int nblocks) {
+  __shared__ u32 h[256];
+  const int tid = threadIdx.x;
+  h[tid] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * RS_BLOCK;
+#pragma unroll 4
+  for (int r = 0; r < RS_ROUNDS; ++r) {
+    const int64_t i = base + r * RS_NT + tid;
+    if (i < N) atomicAdd(&h[(keys[i] >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  hist[(int64_t)tid * nblocks + blockIdx.x] = h[tid];
+}
+
+// one workgroup per digit: exclusive scan of its counts over the blocks
+__global__ __launch_bounds__(RS_NT) void radix_scan_kernel(u32* __restrict__ hist, int nblocks,
+                                                            u32* __restrict__ totals) {
+  __shared__ u32 scratch[RS_NT / 64 + 1];
+  u32* row = hist + (int64_t)blockIdx.x * nblocks;
+  u32 carry = 0;
+  for (int i0 = 0; i0 < nblocks; i0 += RS_NT) {
+    const int i = i0 + threadIdx.x;
+    const u32 v = (i < nblocks) ? row[i] : 0u;
+    u32 tot;
+    const u32 incl = block_incl_scan<RS_NT>(v, scratch, &tot);
+    if (i < nblocks) row[i] = carry + incl - v;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) totals[blockIdx.x] = carry;
+}
+
+// Scatter in a stable order: each round takes RS_NT consecutive elements;
+// lanes with equal digits find each other with 8 ballots, and the waves of
+// a round are ranked in order through per-wave digit counts in LDS.
+__global__ __launch_bounds__(RS_NT) void radix_scatter_kernel(const u32* __restrict__ keys_in,
+                                                               const u32* __restrict__ vals_in, int N, int shift,
+                                                               const u32* __restrict__ hist,
+                                                               const u32* __restrict__ totals, int nblocks,
+                                                               u32* __restrict__ keys_out,
+                                                               u32* __restrict__ vals_out) {
+  constexpr int NWV = RS_NT / 64;
+  __shared__ u32 s_base[256];
+  __shared__ u32 s_wcnt[NWV][256];
+  __shared__ u32 scratch[NWV + 1];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  {
+    const u32 tot_d = totals[tid];
+    u32 all;
+    const u32 incl = block_incl_scan<RS_NT>(tot_d, scratch, &all);
+    s_base[tid] = incl - tot_d + hist[(int64_t)tid * nblocks + blockIdx.x];
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) s_wcnt[w][tid] = 0;
+  }
+  __syncthreads();
+  const unsigned long long below = (1ull << lane) - 1ull;
+  const int64_t base = (int64_t)blockIdx.x * RS_BLOCK;
+  for (int r = 0; r < RS_ROUNDS; ++r) {
+    const int64_t i = base + r * RS_NT + tid;
+    const bool valid = i < N;
+    const u32 key = valid ? keys_in[i] : 0u;
+    const u32 val = valid ? (vals_in ? vals_in[i] : (u32)i) : 0u;
+    const u32 dig = (key >> shift) & 255u;
+    unsigned long long peers = __builtin_amdgcn_ballot_w64(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const bool set = (dig >> bit) & 1u;
+      const unsigned long long bb = __builtin_amdgcn_ballot_w64(set);
+      peers &= set ? bb : ~bb;
+    }
+    const u32 rank = (u32)__popcll(peers & below);
+    if (valid && rank == 0) s_wcnt[wid][dig] = (u32)__popcll(peers);
+    __syncthreads();
+    if (valid) {
+      u32 pos = s_base[dig] + rank;
+      for (int w = 0; w < wid; ++w) pos += s_wcnt[w][dig];
+      keys_out[pos] = key;
+      vals_out[pos] = val;
+    }
+    __syncthreads();
+    u32 add = 0;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      add += s_wcnt[w][tid];
+      s_wcnt[w][tid] = 0;
+    }
+    s_base[tid] += add;
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. per-slot gradients
+// ---------------------------------------------------------------------------
+
+constexpr int XS_STRIDE = AT_ROW_BYTES + 16;  // staged [q; dO] row in LDS (1168 B)
+constexpr int DT_STRIDE = 80;                 // staged P / dS row of a tile: 64 B + 16
+
+// Workgroup = one token; wave w owns the gradient dims 128w..128w+127 (no
+// rope) and 512+16w..+15 (rope).  With X = [scale-free q rows; dO rows]
+// (2H rows of 576, dO's rope part zero) and Dt = [scale dS; P] (2H rows per
+// slot): grad^T[dims x slots] = X^T Dt.  A = X^T fragments stay in
+// registers; B = Dt fragments come from the staged tile.
+template <int H>
+__global__ __launch_bounds__(256) void sparse_mla_bwd_slot_kernel(const uint16_t* __restrict__ q,
+                                                                  const uint16_t* __restrict__ dout,
+                                                                  const uint16_t* __restrict__ dsp,
+                                                                  const int32_t* __restrict__ cnt, int kp,
+                                                                  uint16_t* __restrict__ slot_grad, int n_tokens) {
+  constexpr int KS = 2 * H / 32;        // K steps over the stacked rows
+  constexpr int KSR = (H + 31) / 32;    // K steps that reach q rows (rope)
+  constexpr int XBYTES = 32 * XS_STRIDE;
+  constexpr int DBYTES = 2 * H * DT_STRIDE;
+  constexpr int DCHUNKS = 2 * H * 4;     // 16-byte chunks of a Dt tile
+  constexpr int DCH = (DCHUNKS + 255) / 256;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[XBYTES > 2 * DBYTES ? XBYTES : 2 * DBYTES];
+  const int t = blockIdx.x;
+  if (t >= n_tokens) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
+
+  // ---- X^T fragments: 32 stacked rows at a time through LDS
+  v8bf xa[KS][8], xr[KSR];
+  for (int kb = 0; kb < KS; ++kb) {
+    for (int c = tid; c < 32 * 72; c += 256) {
+      const int r = c / 72, ch = c - r * 72;
+      const int kappa = 32 * kb + r;
+      v4i v = v4i{0, 0, 0, 0};
+      if (kappa < H)
+        v = *reinterpret_cast<const v4i*>(q + ((int64_t)t * H + kappa) * AT_D + 8 * ch);
+      else if (ch < 64)
+        v = *reinterpret_cast<const v4i*>(dout + ((int64_t)t * H + kappa - H) * AT_DV + 8 * ch);
+      *reinterpret_cast<LDS_AS v4i*>(lds + r * XS_STRIDE + 16 * ch) = v;
+    }
+    __syncthreads();
+    // source lane n of group g: rows 8g + n/4 (+4), dims d0 + 4(n%4)..+3
+    const LDS_AS uint8_t* src = lds + (8 * g + (n >> 2)) * XS_STRIDE + 8 * (n & 3);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int d0 = 128 * wid + 16 * m;
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(src + 2 * d0));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(src + 4 * XS_STRIDE + 2 * d0));
+      xa[kb][m] = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    if (kb < KSR) {
+      const int d0 = AT_DV + 16 * wid;
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(src + 2 * d0));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(src + 4 * XS_STRIDE + 2 * d0));
+      xr[kb] = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    __syncthreads();
+  }
+
+  // ---- tiles of 32 slots: Dt rows (2H x 64 B) staged in one of two buffers
+  const int ntiles = (cnt[t] + AT_TILE - 1) / AT_TILE;
+  const uint16_t* dt = dsp + (int64_t)t * 2 * H * kp;
+  v4i st[DCH];
+  auto load_tile = [&](int it) {
+    const int itc = min(it, max(ntiles - 1, 0));
+#pragma unroll
+    for (int j = 0; j < DCH; ++j) {
+      const int c = min(tid + 256 * j, DCHUNKS - 1);
+      st[j] = *reinterpret_cast<const v4i*>(dt + (int64_t)(c >> 2) * kp + AT_TILE * itc + 8 * (c & 3));
+    }
+  };
+  auto store_tile = [&](LDS_AS uint8_t* buf) {
+#pragma unroll
+    for (int j = 0; j < DCH; ++j) {
+      const int c = tid + 256 * j;
+      if (DCHUNKS % 256 == 0 || c < DCHUNKS)
+        *reinterpret_cast<LDS_AS v4i*>(buf + (c >> 2) * DT_STRIDE + 16 * (c & 3)) = st[j];
+    }
+  };
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(lds);
+    load_tile(1);
+  }
+  uint16_t* out_base = slot_grad + (int64_t)t * kp * AT_D;
+  for (int it = 0; it < ntiles; ++it) {
+    LDS_AS uint8_t* cur = lds + (it & 1) * DBYTES;
+    __syncthreads();  // tile `it` staged; the other buffer is free
+    if (it + 1 < ntiles) store_tile(lds + ((it + 1) & 1) * DBYTES);
+    load_tile(it + 2);
+    v4f acc[9][2];
+#pragma unroll
+    for (int m = 0; m < 9; ++m) acc[m][0] = acc[m][1] = v4f{0.f, 0.f, 0.f, 0.f};
+    const LDS_AS uint8_t* src = cur + (8 * g + (n >> 2)) * DT_STRIDE + 8 * (n & 3);
+#pragma unroll
+    for (int kb = 0; kb < KS; ++kb) {
+      v8bf bfr[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const LDS_AS uint8_t* p = src + 32 * kb * DT_STRIDE + 32 * nt;
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)p);
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(p + 4 * DT_STRIDE));
+        bfr[nt] = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          acc[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[kb][m], bfr[nt], acc[m][nt], 0, 0, 0);
+      if (kb < KSR)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          acc[8][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xr[kb], bfr[nt], acc[8][nt], 0, 0, 0);
+    }
+    // lane (n, g): dims d0 + 4g..+3 of slot 32it + 16nt + n
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      uint16_t* row = out_base + (int64_t)(AT_TILE * it + 16 * nt + n) * AT_D + 4 * g;
+#pragma unroll
+      for (int m = 0; m < 9; ++m) {
+        const int d0 = m < 8 ? 128 * wid + 16 * m : AT_DV + 16 * wid;
+        v2i pk;
+        pk[0] = (int)((u32)f2bf(acc[m][nt][0]) | ((u32)f2bf(acc[m][nt][1]) << 16));
+        pk[1] = (int)((u32)f2bf(acc[m][nt][2]) | ((u32)f2bf(acc[m][nt][3]) << 16));
+        *reinterpret_cast<v2i*>(row + d0) = pk;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 4. segmented reduction into dkv
+// ---------------------------------------------------------------------------
+
+constexpr int RD_CHUNK = 256;  // sorted entries per wave
+
+__device__ __forceinline__ void add_bf16x8(float* acc, v4i x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc[2 * i] += __uint_as_float((u32)x[i] << 16);
+    acc[2 * i + 1] += __uint_as_float((u32)x[i] & 0xFFFF0000u);
+  }
+}
+
+// Wave: a chunk of the sorted (row, slot) list.  Lane l sums dims 8l..8l+7
+// (and lanes l < 8 also 512+8l..+7) of the slots of a run of equal rows, then
+// adds the run to dkv with fp32 atomics (a run may continue in the next chunk).
+__global__ __launch_bounds__(256) void dkv_reduce_kernel(const u32* __restrict__ keys, const u32* __restrict__ vals,
+                                                         int N, const uint16_t* __restrict__ slot_grad,
+                                                         float* __restrict__ dkv) {
+  const int lane = threadIdx.x & 63;
+  const int64_t base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RD_CHUNK;
+  if (base >= N) return;
+  float a0[8], a1[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a0[i] = a1[i] = 0.f;
+  u32 cur = SLOT_NONE;
+  bool done = false;
+  auto flush = [&]() {
+    float* dst = dkv + (int64_t)cur * AT_D + 8 * lane;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __hip_atomic_fetch_add(dst + i, a0[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      a0[i] = 0.f;
+    }
+    if (lane < 8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) __hip_atomic_fetch_add(dst + AT_DV + i, a1[i], __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a1[i] = 0.f;
+  };
+  for (int sub = 0; sub < RD_CHUNK / 64; ++sub) {
+    const int64_t j = base + 64 * sub + lane;
+    const u32 kj = (j < N) ? keys[j] : SLOT_NONE;
+    const u32 vj = (j < N) ? vals[j] : 0u;
+    if (__builtin_amdgcn_readfirstlane(kj) == SLOT_NONE) break;  // the rest of the list is past the end
+#pragma unroll 1
+    for (int e0 = 0; e0 < 64 && !done; e0 += 8) {
+      v4i x0[8], x1[8];
+      u32 ke[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        ke[u] = __builtin_amdgcn_readlane(kj, e0 + u);
+        const u32 ve = __builtin_amdgcn_readlane(vj, e0 + u);
+        const uint16_t* src = slot_grad + (int64_t)(ke[u] == SLOT_NONE ? 0u : ve) * AT_D;
+        x0[u] = *reinterpret_cast<const v4i*>(src + 8 * lane);
+        x1[u] = *reinterpret_cast<const v4i*>(src + AT_DV + 8 * (lane & 7));
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (ke[u] == SLOT_NONE) {
+          done = true;
+          break;
+        }
+        if (ke[u] != cur) {
+          if (cur != SLOT_NONE) flush();
+          cur = ke[u];
+        }
+        add_bf16x8(a0, x0[u]);
+        if (lane < 8) add_bf16x8(a1, x1[u]);
+      }
+    }
+    if (done) break;
+  }
+  if (cur != SLOT_NONE) flush();
+}
+
+// ---------------------------------------------------------------------------
+// launcher
+// ---------------------------------------------------------------------------
+
+bool attn_bwd_supported(int H) { return H == 16 || H == 32 || H == 64 || H == 128; }
+
+static int bwd_kp(int k) { return ((k + AT_TILE - 1) / AT_TILE) * AT_TILE; }
+
+static int sort_passes(int64_t num_rows) {
+  int bits = 0;
+  while (bits < 32 && (int64_t(1) << bits) <= num_rows) ++bits;  // bit length of num_rows
+  return (bits + 7) / 8;
+}
+
+struct BwdWorkspace {
+  uint16_t* dsp;
+  uint16_t* slot_grad;
+  u32 *keys_a, *keys_b, *vals_a, *vals_b;
+  int32_t* cnt;
+  u32 *hist, *totals;
+};
+
+// Carves the workspace (base may be null: then only the size is computed).
+static size_t carve_bwd(int T, int H, int k, void* base, BwdWorkspace* w) {
+  const size_t kp = (size_t)bwd_kp(k);
+  const size_t N = (size_t)T * kp;
+  const size_t nblocks = (N + RS_BLOCK - 1) / RS_BLOCK;
+  const size_t sizes[9] = {N * 2 * H * 2, N * AT_D * 2, N * 4, N * 4, N * 4, N * 4, (size_t)T * 4, 256 * nblocks * 4,
+                           256 * 4};
+  size_t off[9], total = 0;
+  for (int i = 0; i < 9; ++i) {
+    off[i] = total;
+    total += align256(sizes[i]);
+  }
+  if (base != nullptr) {
+    char* p = static_cast<char*>(base);
+    w->dsp = reinterpret_cast<uint16_t*>(p + off[0]);
+    w->slot_grad = reinterpret_cast<uint16_t*>(p + off[1]);
+    w->keys_a = reinterpret_cast<u32*>(p + off[2]);
+    w->keys_b = reinterpret_cast<u32*>(p + off[3]);
+    w->vals_a = reinterpret_cast<u32*>(p + off[4]);
+    w->vals_b = reinterpret_cast<u32*>(p + off[5]);
+    w->cnt = reinterpret_cast<int32_t*>(p + off[6]);
+    w->hist = reinterpret_cast<u32*>(p + off[7]);
+    w->totals = reinterpret_cast<u32*>(p + off[8]);
+  }
+  return total;
+}
+
+size_t attn_bwd_workspace_bytes(int T, int H, int k) {
+  if (T == 0) return 0;
+  return carve_bwd(T, H, k, nullptr, nullptr);
+}
+
+bool attn_bwd_size_ok(int T, int k) { return (int64_t)T * bwd_kp(k) < (int64_t(1) << 31); }
+
+hipError_t launch_attn_bwd(int T, int H, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                           const int32_t* seq_id, const Layout& lay, int64_t num_rows, int k, float sm_scale,
+                           const uint16_t* out, const float* lse, const uint16_t* dout, float* dq, float* dkv,
+                           void* ws, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  BwdWorkspace w;
+  carve_bwd(T, H, k, ws, &w);
+  const int kp = bwd_kp(k);
+  const int N = T * kp;
+  const int nblocks = (N + RS_BLOCK - 1) / RS_BLOCK;
+
+  // 1. dq, P / dS, row lists
+  const int n_hg = H > 64 ? H / 64 : 1;
+  const int blocks = ((T + 7) / 8) * 8 * n_hg;
+  hipLaunchKernelGGL(sparse_mla_bwd_dq_kernel<4>, dim3(blocks), dim3(256), 0, stream, q,
+                     reinterpret_cast<const uint8_t*>(kv), idx, seq_id, lay, H, k, kp, sm_scale, out, lse, dout, dq,
+                     w.dsp, w.keys_a, w.cnt, T);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  // 2. sort (row, slot) by row
+  const int passes = sort_passes(num_rows);
+  u32 *kin = w.keys_a, *kout = w.keys_b, *vin = nullptr, *vout = w.vals_a;
+  for (int p = 0; p < passes; ++p) {
+    hipLaunchKernelGGL(radix_hist_kernel, dim3(nblocks), dim3(RS_NT), 0, stream, kin, N, 8 * p, w.hist, nblocks);
+    hipLaunchKernelGGL(radix_scan_kernel, dim3(256), dim3(RS_NT), 0, stream, w.hist, nblocks, w.totals);
+    hipLaunchKernelGGL(radix_scatter_kernel, dim3(nblocks), dim3(RS_NT), 0, stream, kin, vin, N, 8 * p, w.hist,
+                       w.totals, nblocks, kout, vout);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    std::swap(kin, kout);
+    vin = vout;
+    vout = (vout == w.vals_a) ? w.vals_b : w.vals_a;
+  }
+
+  // 3. per-slot gradients
+  switch (H) {
+    case 16: hipLaunchKernelGGL(sparse_mla_bwd_slot_kernel<16>, dim3(T), dim3(256), 0, stream, q, dout, w.dsp, w.cnt,
+                                kp, w.slot_grad, T); break;
+    case 32: hipLaunchKernelGGL(sparse_mla_bwd_slot_kernel<32>, dim3(T), dim3(256), 0, stream, q, dout, w.dsp, w.cnt,
+                                kp, w.slot_grad, T); break;
+    case 64: hipLaunchKernelGGL(sparse_mla_bwd_slot_kernel<64>, dim3(T), dim3(256), 0, stream, q, dout, w.dsp, w.cnt,
+                                kp, w.slot_grad, T); break;
+    case 128: hipLaunchKernelGGL(sparse_mla_bwd_slot_kernel<128>, dim3(T), dim3(256), 0, stream, q, dout, w.dsp,
+                                 w.cnt, kp, w.slot_grad, T); break;
+    default: return hipErrorInvalidValue;
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  // 4. reduction into dkv (sorted keys in kin, slots in vin)
+  const int chunks = (N + RD_CHUNK - 1) / RD_CHUNK;
+  hipLaunchKernelGGL(dkv_reduce_kernel, dim3((chunks + 3) / 4), dim3(256), 0, stream, kin, vin, N, w.slot_grad,
+                     dkv);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -23,7 +23,7 @@ FP8_MAX = 448.0
 _MIN_SCALE = 2.0 ** -126
 
 # tensor ids used to derive per-tensor seeds
-_T_IQ, _T_IK, _T_W, _T_Q, _T_KV, _T_LEN, _T_PAGES, _T_PLANT, _T_NQ = range(9)
+_T_IQ, _T_IK, _T_W, _T_Q, _T_KV, _T_LEN, _T_PAGES, _T_PLANT, _T_NQ, _T_DOUT = range(10)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -59,6 +59,10 @@ CONFIGS = {
                             planted_frac=0.02, seed=1002),
     # prefill, 64K tokens all causal queries
     "prefill64k": DSAConfig("prefill64k", "prefill", B=1, L=65536, H_I=64, D_I=128, H=128, k=2048, seed=1003),
+    # training-step backward: the last 4096 tokens of a 64K-token sequence as
+    # queries (each keeps a full k = 2048 selection)
+    "train64k_chunk4k": DSAConfig("train64k_chunk4k", "decode", B=1, L=65536, H_I=64, D_I=128, H=128, k=2048,
+                                  queries_per_seq=4096, seed=1005),
     # ragged paged batch
     "ragged_paged": DSAConfig("ragged_paged", "ragged", B=128, L=131072, H_I=64, D_I=128, H=128, k=2048,
                               paged=True, min_len=2048, seed=1004),
@@ -235,6 +239,13 @@ def _randn_bf16_scaled(shape, gen, device, std: float, chunk_rows: int = 1 << 14
         r1 = min(flat.shape[0], r0 + chunk_rows)
         flat[r0:r1] = (torch.randn((r1 - r0, shape[-1]), generator=gen, device=device) * std).to(torch.bfloat16)
     return out
+
+
+def output_grad(cfg: DSAConfig, T: int, device="cpu") -> torch.Tensor:
+    """Gradient of the attention output for the backward: bf16 [T, H, d_v],
+    N(0, 1) entries (seeded per config)."""
+    dev = torch.device(device)
+    return _randn_bf16_scaled((T, cfg.H, cfg.d_v), _gen(cfg.seed, _T_DOUT, dev), dev, 1.0)
 
 
 def tie_heavy_logits(T: int, n: int, levels: int = 256, seed: int = 7, device="cpu") -> torch.Tensor:

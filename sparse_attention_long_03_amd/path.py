@@ -83,6 +83,25 @@ class DSAPath:
                               self.ws(B.DSA_OP_ATTN), stream)
         return self.out, self.lse
 
+    def attn_bwd(self, idx: torch.Tensor, d_out: torch.Tensor, out=None, lse=None, dkv=None, stream=None):
+        """Backward of the sparse attention for the selection `idx`, given the
+        forward's out / lse (those of the last attn() call by default).
+        Returns (dq float32[T, H, 576], dkv float32 in the cache's layout);
+        the gradients are added into `dkv` when one is given."""
+        x, c = self.x, self.cfg
+        out = self.out if out is None else out
+        lse = self.lse if lse is None else lse
+        dq = torch.empty((self.T, c.H, c.D), dtype=torch.float32, device=self.dev)
+        if dkv is None:
+            dkv = torch.zeros(x.kv.shape, dtype=torch.float32, device=self.dev)
+        k = idx.shape[1]
+        n = B.dsa_workspace_bytes(B.DSA_OP_ATTN_BWD, self.T, x.max_len, c.H, k)
+        if ("bwd", n) not in self._ws:
+            self._ws[("bwd", n)] = B.workspace(n, self.dev)
+        B.dsa_sparse_mla_attn_bwd(self.q, self.layout, c.H, x.q, x.kv, idx, k, c.scale, out, lse, d_out, dq, dkv,
+                                  self._ws[("bwd", n)], stream)
+        return dq, dkv
+
     def dense_attn(self, idx: torch.Tensor, out=None, lse=None, stream=None):
         """The masked dense variant over the same selection (contiguous rows)."""
         x, c = self.x, self.cfg

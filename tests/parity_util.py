@@ -93,3 +93,62 @@ def bf16_to_np(t):
 
 def torch_seed_all(s=0):
     torch.manual_seed(s)
+
+
+# Attention backward (float32 dq and dkv).  The GPU rounds P and scale*dS to
+# bf16 for its products (relative 2^-9 each), rounds each selected row's
+# gradient to bf16 before the sum over queries (2^-9), and takes D = dO . out
+# from the forward's bf16 output, whose own error is at most 2^-9 of
+# sum_i P_i |v_i| per value.  Every dq / dkv entry is therefore within
+# 3 * 2^-9 (rounded up to 2^-7) of the sum of absolute values of its terms,
+# with A_h = sum_c |dO_hc| sum_i P_i |v_ic| standing for D's error:
+#   M_dq[t,h,d] = scale sum_i P_i (|dP_i - D_h| + A_h) |kv_i[d]|
+#   M_dkv[r,d]  = sum over (t, i) selecting row r, over h, of
+#                 scale P_hi (|dP_hi - D_h| + A_h) |q_h[d]|  +  P_hi |dO_h[d]| (d < 512)
+BWD_REL = 2.0 ** -7
+BWD_FRO = 1e-2
+
+
+def attn_bwd_magnitudes(q_bits, kv_bits, idx, seq_id, scale, d_out, block_table=None, page_size=64):
+    """(M_dq [T, H, 576], M_dkv in the cache's shape), float64."""
+    q = O.decode_bf16(q_bits)
+    kv = O.decode_bf16(kv_bits)
+    dO = np.asarray(d_out, dtype=np.float64)
+    T, H, D = q.shape
+    m_dq = np.zeros((T, H, D))
+    m_dkv = np.zeros(kv.shape)
+    for t in range(T):
+        sel = np.asarray(idx[t])
+        pos = sel[sel >= 0]
+        if len(pos) == 0:
+            continue
+        b = int(seq_id[t])
+        if block_table is None:
+            where = [(b, int(s)) for s in pos]
+        else:
+            where = [(int(block_table[b, int(s) // page_size]), int(s) % page_size) for s in pos]
+        rows = np.stack([kv[w] for w in where])
+        z = scale * (q[t] @ rows.T)
+        p = np.exp(z - z.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        dP = dO[t] @ rows[:, :512].T
+        Dh = np.sum(dO[t] * (p @ rows[:, :512]), axis=1, keepdims=True)
+        A = np.sum(np.abs(dO[t]) * (p @ np.abs(rows[:, :512])), axis=1, keepdims=True)
+        c = p * (np.abs(dP - Dh) + A)                               # [H, n]
+        m_dq[t] = scale * (c @ np.abs(rows))
+        g = scale * (c.T @ np.abs(q[t]))
+        g[:, :512] += p.T @ np.abs(dO[t])
+        for r, w in enumerate(where):
+            m_dkv[w] += g[r]
+    return m_dq, m_dkv
+
+
+def check_bwd(gpu, ref, mag, what=""):
+    g = np.asarray(gpu, dtype=np.float64)
+    o = np.asarray(ref, dtype=np.float64)
+    err = np.abs(g - o)
+    bad = err > BWD_REL * mag + 1e-30
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} values beyond 2^-7 of their term magnitude; "
+                           f"worst ratio {np.max(err / np.maximum(mag, 1e-30)):.3g}")
+    fro = np.linalg.norm(g - o) / max(np.linalg.norm(o), 1e-30)
+    assert fro <= BWD_FRO, f"{what}: relative Frobenius error {fro}"

@@ -183,3 +183,35 @@ def test_masked_dense_validation(lib):
     assert need > 0
     q16 = _q(max_len=16384)
     assert f(ctypes.byref(q16), ctypes.byref(_lay(cap=16384)), 128, FAKE, FAKE, FAKE, 2048, 0.1, FAKE, None, FAKE, need - 1, None) == B.DSA_ERR_WORKSPACE
+
+
+def test_attention_backward_validation(lib):
+    f = lib.dsa_sparse_mla_attn_bwd
+    q, lay = _q(T=4), _lay()
+    need = B.dsa_workspace_bytes(B.DSA_OP_ATTN_BWD, 4, 100, 128, 2048)
+    # per token: P / dS rows, one bf16 gradient row per slot, four sort words per slot
+    assert need >= 4 * 2048 * (4 * 128 + 1152 + 16)
+
+    def call(H=128, k=2048, scale=0.1, ptrs=None, ws=FAKE, nbytes=need, q_=None, lay_=None):
+        p = list(ptrs or (FAKE,) * 8)  # q, kv, idx, out, lse, d_out, dq, dkv
+        return f(ctypes.byref(q_ or q), ctypes.byref(lay_ or lay), H, p[0], p[1], p[2], k, scale, p[3], p[4], p[5],
+                 p[6], p[7], ws, nbytes, None)
+
+    assert call(H=48) == B.DSA_ERR_UNSUPPORTED
+    assert call(k=4096) == B.DSA_ERR_UNSUPPORTED
+    assert call(scale=0.0) == B.DSA_ERR_INVALID_ARG
+    for i in range(8):
+        ptrs = [FAKE] * 8
+        ptrs[i] = None
+        assert call(ptrs=ptrs) == B.DSA_ERR_INVALID_ARG, i
+    mis = [FAKE] * 8
+    mis[7] = ctypes.c_void_p((1 << 20) + 4)  # dkv misaligned
+    assert call(ptrs=mis) == B.DSA_ERR_INVALID_ARG
+    assert call(ws=None) == B.DSA_ERR_WORKSPACE
+    assert call(nbytes=need - 1) == B.DSA_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p((1 << 20) + 64)) == B.DSA_ERR_WORKSPACE
+    # caches of 2^31 rows or more are not handled (row ids are 31-bit)
+    assert call(lay_=B.contiguous_layout(1 << 31)) == B.DSA_ERR_UNSUPPORTED
+    assert call(q_=_q(T=0, seq=None, pos=None), ptrs=[None] * 8, ws=None, nbytes=0) == B.DSA_OK
+    assert B.dsa_workspace_bytes(B.DSA_OP_ATTN_BWD, 0, 100, 128, 2048) == 0
+    assert B.dsa_workspace_bytes(B.DSA_OP_ATTN_BWD, 8, 100, 128, 2048) > need

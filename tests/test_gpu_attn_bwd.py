@@ -1,0 +1,152 @@
+"""GPU parity of the sparse attention backward (dsa_sparse_mla_attn_bwd):
+dq and the dkv cache gradient against the float64 oracle, within 2^-7 of the
+magnitude of each entry's terms (the bf16 roundings of P, dS and the per-row
+gradients; see parity_util)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_attention_long_03_amd import inputs as I
+from sparse_attention_long_03_amd.path import DSAPath
+
+from parity_util import attn_bwd_magnitudes, check_bwd, np_
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+CASES = {
+    # 16 decode queries of one 4K sequence, 16 heads, k = 256
+    "tiny": I.CONFIGS["tiny"],
+    # all 128 heads, full k = 2048 out of 3000 positions, three sequences
+    "h128_k2048": I.scaled(I.CONFIGS["decode32k"], B=3, L=3000, queries_per_seq=3),
+    # 64 heads over shuffled 64-token pages, ragged lengths (short rows padded with -1)
+    "h64_paged": I.scaled(I.CONFIGS["ragged_paged"], B=4, L=2500, min_len=100, H=64, k=512),
+    # prefill: 600 causal queries share most of their rows (the reduction's long runs)
+    "h32_prefill": I.scaled(I.CONFIGS["prefill64k"], L=600, H=32, k=128),
+}
+
+
+def _run(x, idx=None):
+    p = DSAPath(x)
+    out, lse, sel = p.forward()
+    if idx is not None:
+        p.attn(idx)
+        sel = idx
+    dO = I.output_grad(x.cfg, x.T, DEV)
+    dq, dkv = p.attn_bwd(sel, dO)
+    torch.cuda.synchronize()
+    return p, sel, dO, dq, dkv
+
+
+def _oracle(x, idx, dO):
+    bt = None if x.block_table is None else np_(x.block_table)
+    args = (I.bf16_bits(x.q), I.bf16_bits(x.kv), np_(idx), np_(x.seq_id), x.cfg.scale)
+    dO64 = dO.float().cpu().numpy().astype(np.float64)
+    dq, _, dkv = O.sparse_mla_attention_backward(*args, dO64, block_table=bt)
+    m_dq, m_dkv = attn_bwd_magnitudes(*args, dO64, block_table=bt)
+    return dq, dkv, m_dq, m_dkv
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_backward_matches_oracle(name):
+    x = I.make_inputs(CASES[name], DEV)
+    print(f"backward parity {name}: T={x.T} H={x.cfg.H} k={x.cfg.k}", flush=True)
+    p, idx, dO, dq, dkv = _run(x)
+    rdq, rdkv, m_dq, m_dkv = _oracle(x, idx, dO)
+    check_bwd(np_(dq), rdq, m_dq, f"{name} dq")
+    check_bwd(np_(dkv), rdkv, m_dkv, f"{name} dkv")
+    # rows no query selected are left exactly as they were (zero)
+    assert np.all(np_(dkv)[m_dkv.sum(axis=-1) == 0] == 0)
+
+
+def test_backward_edge_selections():
+    """Padding anywhere in a row, a row selected twice by one query, a query
+    with no selection at all, and a ragged final tile."""
+    cfg = I.scaled(I.CONFIGS["decode32k"], B=2, L=700, queries_per_seq=4, H=16, k=100)
+    x = I.make_inputs(cfg, DEV)
+    g = np.random.default_rng(5)
+    pos = np_(x.pos)
+    idx = np.full((x.T, cfg.k), -1, dtype=np.int32)
+    for t in range(x.T):
+        n = [100, 37, 64, 1, 0, 99, 33, 65][t]
+        if n:
+            idx[t, g.choice(cfg.k, n, replace=False)] = g.choice(int(pos[t]) + 1, n, replace=False)
+    idx[1, 5] = idx[1, 6] = 17            # one row twice in one query
+    idx_t = torch.from_numpy(idx).to(DEV)
+    p, _, dO, dq, dkv = _run(x, idx_t)
+    rdq, rdkv, m_dq, m_dkv = _oracle(x, idx_t, dO)
+    check_bwd(np_(dq), rdq, m_dq, "edge dq")
+    check_bwd(np_(dkv), rdkv, m_dkv, "edge dkv")
+    assert np.all(np_(dq[4]) == 0)        # no selection: zero gradient
+
+
+def test_backward_accumulates_into_dkv():
+    x = I.make_inputs(CASES["tiny"], DEV)
+    p = DSAPath(x)
+    _, _, idx = p.forward()
+    dO = I.output_grad(x.cfg, x.T, DEV)
+    dq1, dkv = p.attn_bwd(idx, dO)
+    once = dkv.clone()
+    dq2, dkv = p.attn_bwd(idx, dO, dkv=dkv)
+    torch.cuda.synchronize()
+    assert torch.equal(dq1, dq2)          # dq is written, not accumulated
+    np.testing.assert_allclose(np_(dkv), 2 * np_(once), rtol=1e-6, atol=1e-12)
+
+
+def test_backward_heads_are_independent_of_head_groups():
+    """128 heads run as two workgroups of 64: the dq of heads 64..127 equals
+    that of the same heads run as a 64-head problem."""
+    x = I.make_inputs(CASES["h128_k2048"], DEV)
+    p, idx, dO, dq, _ = _run(x)
+    x64 = I.DSAInputs(cfg=I.scaled(x.cfg, H=64), seq_id=x.seq_id, pos=x.pos, iq8=x.iq8, iqs=x.iqs, iw=x.iw,
+                      q=x.q[:, 64:].contiguous(), ik8=x.ik8, iks=x.iks, kv=x.kv, block_table=x.block_table,
+                      seq_lens=x.seq_lens, max_len=x.max_len)
+    p64 = DSAPath(x64)
+    dq64, _ = p64.attn_bwd(idx, dO[:, 64:].contiguous(), out=p.out[:, 64:].contiguous(),
+                           lse=p.lse[:, 64:].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(dq[:, 64:], dq64)
+
+
+def test_full_size_train_chunk_sampled():
+    """The 4096-query chunk of a 64K sequence at full size (H = 128,
+    k = 2048): dq of sampled queries, and dkv of sampled rows that few
+    queries select, against the oracle run on just those queries."""
+    cfg = I.CONFIGS["train64k_chunk4k"]
+    x = I.make_inputs(cfg, DEV)
+    print(f"backward full size: T={x.T} L={cfg.L}", flush=True)
+    p, idx, dO, dq, dkv = _run(x)
+    idx_h = np_(idx)
+    dO64 = dO.float().cpu().numpy().astype(np.float64)
+    kv0 = x.kv[0]
+
+    def token_oracle(t):
+        sel = idx_h[t][idx_h[t] >= 0]
+        rows = I.bf16_bits(kv0[torch.as_tensor(sel, dtype=torch.int64, device=DEV)])[None]
+        args = (I.bf16_bits(x.q[t:t + 1]), rows, np.arange(len(sel))[None], np.zeros(1, int), cfg.scale)
+        rdq, rsel, _ = O.sparse_mla_attention_backward(*args, dO64[t:t + 1])
+        m_dq, m_rows = attn_bwd_magnitudes(*args, dO64[t:t + 1])
+        return sel, rdq[0], rsel[0], m_dq[0], m_rows[0]
+
+    for t in [0, 1, 2047, 2048, x.T - 1]:
+        _, rdq, _, m_dq, _ = token_oracle(t)
+        check_bwd(np_(dq[t]), rdq, m_dq, f"full-size dq query {t}")
+
+    # rows selected by one to three queries
+    flat = idx[idx >= 0].long()
+    counts = torch.bincount(flat, minlength=cfg.L)
+    few = torch.nonzero((counts >= 1) & (counts <= 3)).flatten()
+    rows = np_(few[torch.linspace(0, len(few) - 1, 6).long()])
+    want = {int(r): (np.zeros(576), np.zeros(576)) for r in rows}
+    for t in sorted({int(t) for r in rows for t in np.nonzero((idx_h == r).any(axis=1))[0]}):
+        sel, _, rsel, _, m_rows = token_oracle(t)
+        for j, s in enumerate(sel):
+            if int(s) in want:
+                want[int(s)][0][:] += rsel[j]
+                want[int(s)][1][:] += m_rows[j]
+    got = np_(dkv[0])
+    for r, (ref, mag) in want.items():
+        check_bwd(got[r], ref, mag, f"full-size dkv row {r}")
