@@ -1,0 +1,93 @@
+"""The backward's parity check has teeth: mistakes a kernel could plausibly
+make (planted here in the oracle's result, on the CPU) fail it, while the
+roundings the GPU is allowed (bf16 on P, dS and per-row gradients) pass."""
+
+import numpy as np
+import torch
+
+import oracle as O
+from sparse_attention_long_03_amd import inputs as I
+
+from parity_util import attn_bwd_magnitudes, check_bwd
+
+
+def _case():
+    cfg = I.scaled(I.CONFIGS["tiny"], B=2, L=300, queries_per_seq=3, H=16, k=64)
+    x = I.make_inputs(cfg)
+    g = np.random.default_rng(3)
+    idx = np.stack([g.choice(int(p) + 1, cfg.k, replace=False) for p in x.pos.numpy()])
+    dO = I.output_grad(cfg, x.T).float().numpy().astype(np.float64)
+    args = (I.bf16_bits(x.q), I.bf16_bits(x.kv), idx, x.seq_id.numpy(), cfg.scale)
+    return x, cfg, idx, dO, args
+
+
+def _bf16(a):
+    return torch.from_numpy(np.asarray(a, dtype=np.float32)).to(torch.bfloat16).double().numpy()
+
+
+def _variant(x, cfg, idx, dO, drop_D=False, no_scale=False, p_for_ds=False, bf16=False):
+    """The backward with one planted mistake (same loop as the definition);
+    bf16=True instead rounds what the GPU rounds: the output used for D, P,
+    scale*dS and each selected row's gradient."""
+    q = O.decode_bf16(I.bf16_bits(x.q))
+    kv = O.decode_bf16(I.bf16_bits(x.kv))
+    dq = np.zeros(q.shape)
+    dkv = np.zeros(kv.shape)
+    for t in range(x.T):
+        b = int(x.seq_id[t])
+        rows = kv[b, idx[t]]
+        z = cfg.scale * q[t] @ rows.T
+        p = np.exp(z - z.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        dP = dO[t] @ rows[:, :512].T
+        o = p @ rows[:, :512]
+        D = 0.0 if drop_D else np.sum(dO[t] * (_bf16(o) if bf16 else o), 1, keepdims=True)
+        dS = p if p_for_ds else p * (dP - D)
+        s = 1.0 if no_scale else cfg.scale
+        sdS = _bf16(s * dS) if bf16 else s * dS
+        pp = _bf16(p) if bf16 else p
+        dq[t] = sdS @ rows
+        gr = sdS.T @ q[t]
+        gr[:, :512] += pp.T @ dO[t]
+        if bf16:
+            gr = _bf16(gr)
+        for j, r in enumerate(idx[t]):
+            dkv[b, r] += gr[j]
+    return dq, dkv
+
+
+def test_planted_mistakes_fail_and_roundings_pass():
+    x, cfg, idx, dO, args = _case()
+    dq, _, dkv = O.sparse_mla_attention_backward(*args, dO)
+    m_dq, m_dkv = attn_bwd_magnitudes(*args, dO)
+
+    def fails(fn):
+        try:
+            fn()
+        except AssertionError:
+            return True
+        return False
+
+    # allowed: the roundings the GPU makes
+    bdq, bdkv = _variant(x, cfg, idx, dO, bf16=True)
+    check_bwd(bdq, dq, m_dq)
+    check_bwd(bdkv, dkv, m_dkv)
+    assert not np.array_equal(bdq, dq)
+    # planted: D dropped, softmax scale dropped, P used for dS
+    for kw in (dict(drop_D=True), dict(no_scale=True), dict(p_for_ds=True)):
+        wdq, wdkv = _variant(x, cfg, idx, dO, **kw)
+        assert fails(lambda: check_bwd(wdq, dq, m_dq)), kw
+        assert fails(lambda: check_bwd(wdkv, dkv, m_dkv)), kw
+    # planted: the rope part of dkv or the value part (P^T dO) missing
+    no_rope = dkv.copy()
+    no_rope[..., 512:] = 0
+    assert fails(lambda: check_bwd(no_rope, dkv, m_dkv))
+    _, no_dv = _variant(x, cfg, idx, np.zeros_like(dO))
+    assert fails(lambda: check_bwd(no_dv, dkv, m_dkv))
+    # planted: a gradient added to the wrong row (off by one position)
+    shifted = np.roll(dkv, 1, axis=1)
+    assert fails(lambda: check_bwd(shifted, dkv, m_dkv))
+    # the variant loop without a mistake reproduces the oracle
+    rdq, rdkv = _variant(x, cfg, idx, dO)
+    np.testing.assert_allclose(rdq, dq, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(rdkv, dkv, rtol=1e-12, atol=1e-15)
