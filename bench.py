@@ -43,14 +43,15 @@ REPLICAS = 4
 # device copy in the same pass.  Valid only for the kernel sources they were
 # taken on (hash below); otherwise the field is reported as null.
 TRAFFIC = {
-    "sources_sha256": "ce18cf7f112a8375f525873aadd7c78331236a63fccad0841ab8a8e711e1ce2b",
+    "sources_sha256": "65da00adf116d9c766483f6dd491ea606e1950eed4c0c7681bdd2a4199e83623",
     # FETCH_SIZE 135759.4 KiB/launch x 1.99982 (copy: 131084.0 KiB counted for 262144 KiB read)
     "fetch_bytes": 278009696,
     # WRITE_SIZE 8192.0 KiB/launch x 1.0 (copy: 262144 KiB counted for 262144 KiB written)
     "write_bytes": 8388608,
 }
+# the indexer kernel's device code (launch.h holds host declarations only)
 TRAFFIC_SOURCES = ("sparse_attention_long_03_amd/csrc/indexer.hip", "sparse_attention_long_03_amd/csrc/indexer_math.h",
-                   "sparse_attention_long_03_amd/csrc/common.h", "sparse_attention_long_03_amd/csrc/launch.h")
+                   "sparse_attention_long_03_amd/csrc/common.h")
 
 
 def sources_hash():
@@ -264,6 +265,79 @@ def bench_prefill(args, cfg):
     print(json.dumps(out), flush=True)
 
 
+def bench_backward(args, cfg):
+    """Training-step backward of the sparse attention: the last 4096 tokens
+    of a 64K-token sequence as queries, each with its full top-2048
+    selection (from the forward, untimed).  A step zeroes dkv and runs
+    dsa_sparse_mla_attn_bwd (dq kernel, row sort, per-slot dkv, reduction).
+    The dq kernel, the largest part, is also timed alone through
+    dsa_sparse_mla_attn_bwd_dq: its roofline is bf16 MFMA."""
+    import torch
+    from sparse_attention_long_03_amd import binding as B
+    from sparse_attention_long_03_amd import inputs as I
+    from sparse_attention_long_03_amd.path import DSAPath
+
+    x = I.make_inputs(cfg, "cuda")
+    p = DSAPath(x)
+    _, _, idx = p.forward()
+    dO = I.output_grad(cfg, x.T, "cuda")
+    dq, dkv = p.attn_bwd(idx, dO)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        dkv.zero_()
+        p.attn_bwd(idx, dO, dkv=dkv)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    k = cfg.k
+    ws = p._ws[("bwd", B.dsa_workspace_bytes(B.DSA_OP_ATTN_BWD, x.T, x.max_len, cfg.H, k))]
+    dq_only = lambda: B.dsa_sparse_mla_attn_bwd_dq(p.q, p.layout, cfg.H, x.q, x.kv, idx, k, cfg.scale, p.out, p.lse,
+                                                   dO, dq, ws)
+    n_launch = max(args.steps, 5)
+    timed_rotation([dq_only], 2, stream)
+    dq_avg = mean(timed_rotation([dq_only], n_launch, stream))
+    step_avg = mean(timed_rotation([step], n_launch, stream))
+
+    sel = sum(min(int(q) + 1, k) for q in x.pos.tolist())
+    # per (selected row, head): S and dq over 576, dP over 512, the stacked
+    # [scale dS; P] product over 512 (dK no-rope + dV) twice, dK rope over 64
+    bwd_flops = 2 * sel * cfg.H * (576 + 512 + 576 + 2 * 512 + 64)
+    dq_flops = 2 * sel * cfg.H * (576 + 512 + 576)
+    dq_tf = dq_flops / (dq_avg * 1e-3) / 1e12
+    out = {
+        "metric": "sparse MLA-MQA backward query tokens/s @64K ctx, k=2048",
+        "value": round(x.T / (wall_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 MFMA, fp32 accumulate; P, dS and per-row gradients rounded to bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: backward of the sparse attention for {x.T} query tokens at positions "
+                               f"{cfg.L - x.T}..{cfg.L - 1} of one {cfg.L}-token sequence, top-{k} selection each, "
+                               f"MLA-MQA {cfg.H} heads x 576", "L": cfg.L, "T": x.T, "k": k, "H": cfg.H},
+        "roofline": {"bound": "mfma", "kernel": "sparse_mla_bwd_dq_kernel<4>", "achieved": round(dq_tf, 1),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(dq_tf / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "flops_per_launch": dq_flops, "avg_launch_us": round(dq_avg * 1e3, 1)},
+        "kernels": {"dq_ms": round(dq_avg, 3), "backward_ms": round(step_avg, 3),
+                    "backward_tflops": round(bwd_flops / (step_avg * 1e-3) / 1e12, 1),
+                    "backward_frac_bf16": round(bwd_flops / (step_avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def bench_crossover(args):
     """Sparse gather vs masked dense attention on the same top-2048 selection,
     prefill (every token a query) and 16-sequence decode, L = 1K .. 16K: the
@@ -317,6 +391,9 @@ def main():
     cfg = I.CONFIGS[args.config]
     if cfg.kind == "prefill":
         bench_prefill(args, cfg)
+        return
+    if cfg.name == "train64k_chunk4k":
+        bench_backward(args, cfg)
         return
     x0 = I.make_inputs(cfg, "cuda")
     xs = replicas(x0, REPLICAS)

@@ -223,6 +223,22 @@ int dsa_sparse_mla_attn_bwd(const dsa_queries* q, const dsa_kv_layout* layout, i
                             const float* lse, const void* d_out_bf16, float* dq, float* dkv, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
+/* The two steps of dsa_sparse_mla_attn_bwd, for callers that want dq first
+ * (it is on the critical path of the layers below) and dkv later or on
+ * another stream.  dsa_sparse_mla_attn_bwd_dq computes dq and leaves P, dS and
+ * the selected rows in the workspace; dsa_sparse_mla_attn_bwd_dkv then adds
+ * the dkv gradient.  The dkv step must be enqueued after the dq step (same
+ * stream, or ordered by an event) with the same q, layout, H, k, q_bf16,
+ * d_out_bf16 and workspace, and nothing may write the workspace in between.
+ * Arguments and errors as for dsa_sparse_mla_attn_bwd.                     */
+int dsa_sparse_mla_attn_bwd_dq(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H, const void* q_bf16,
+                               const void* kv_bf16, const int32_t* idx, int32_t k, float sm_scale,
+                               const void* out_bf16, const float* lse, const void* d_out_bf16, float* dq,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+int dsa_sparse_mla_attn_bwd_dkv(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H, const void* q_bf16,
+                                int32_t k, const void* d_out_bf16, float* dkv, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * (3') Masked dense variant of (3) ("... Sparse Consideration (DSA)", "Lets
  * Discuss it's effectivity and accuracy": at short lengths the prefill runs

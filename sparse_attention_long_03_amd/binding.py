@@ -42,8 +42,8 @@ class dsa_kv_layout(ctypes.Structure):
 
 
 EXPORTS = ("dsa_cache_write", "dsa_indexer_logits", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_attn",
-           "dsa_sparse_mla_attn_bwd", "dsa_masked_dense_attn", "dsa_forward", "dsa_workspace_bytes",
-           "dsa_status_str", "dsa_abi_version")
+           "dsa_sparse_mla_attn_bwd", "dsa_sparse_mla_attn_bwd_dq", "dsa_sparse_mla_attn_bwd_dkv",
+           "dsa_masked_dense_attn", "dsa_forward", "dsa_workspace_bytes", "dsa_status_str", "dsa_abi_version")
 
 _lib = None
 
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
     L.dsa_topk.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp, sz, vp]
     L.dsa_sparse_mla_attn.argtypes = [Q, KV, i32, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
     L.dsa_sparse_mla_attn_bwd.argtypes = [Q, KV, i32, vp, vp, vp, i32, f32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dsa_sparse_mla_attn_bwd_dq.argtypes = [Q, KV, i32, vp, vp, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]
+    L.dsa_sparse_mla_attn_bwd_dkv.argtypes = [Q, KV, i32, vp, i32, vp, vp, vp, sz, vp]
     L.dsa_masked_dense_attn.argtypes = [Q, KV, i32, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
     L.dsa_forward.argtypes = [Q, KV, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]
     L.dsa_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
@@ -72,7 +74,7 @@ def lib() -> ctypes.CDLL:
     L.dsa_status_str.restype = ctypes.c_char_p
     L.dsa_abi_version.restype = i32
     for name in ("dsa_cache_write", "dsa_indexer_logits", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_attn",
-                 "dsa_sparse_mla_attn_bwd", "dsa_masked_dense_attn", "dsa_forward"):
+                 "dsa_sparse_mla_attn_bwd", "dsa_sparse_mla_attn_bwd_dq", "dsa_sparse_mla_attn_bwd_dkv", "dsa_masked_dense_attn", "dsa_forward"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -187,6 +189,23 @@ def dsa_sparse_mla_attn_bwd(q: dsa_queries, layout: dsa_kv_layout, H: int, q_bf1
                                        _ptr(idx), int(k), float(sm_scale), _ptr(out_bf16), _ptr(lse),
                                        _ptr(d_out_bf16), _ptr(dq), _ptr(dkv), _ptr(ws), nbytes, _stream(stream))
     _check(st, "dsa_sparse_mla_attn_bwd")
+
+
+def dsa_sparse_mla_attn_bwd_dq(q: dsa_queries, layout: dsa_kv_layout, H: int, q_bf16, kv_bf16, idx: torch.Tensor,
+                               k: int, sm_scale: float, out_bf16, lse, d_out_bf16, dq, ws: torch.Tensor, stream=None):
+    st = lib().dsa_sparse_mla_attn_bwd_dq(ctypes.byref(q), ctypes.byref(layout), H, _ptr(q_bf16), _ptr(kv_bf16),
+                                          _ptr(idx), int(k), float(sm_scale), _ptr(out_bf16), _ptr(lse),
+                                          _ptr(d_out_bf16), _ptr(dq), _ptr(ws), ws.numel() * ws.element_size(),
+                                          _stream(stream))
+    _check(st, "dsa_sparse_mla_attn_bwd_dq")
+
+
+def dsa_sparse_mla_attn_bwd_dkv(q: dsa_queries, layout: dsa_kv_layout, H: int, q_bf16, k: int, d_out_bf16, dkv,
+                                ws: torch.Tensor, stream=None):
+    st = lib().dsa_sparse_mla_attn_bwd_dkv(ctypes.byref(q), ctypes.byref(layout), H, _ptr(q_bf16), int(k),
+                                           _ptr(d_out_bf16), _ptr(dkv), _ptr(ws), ws.numel() * ws.element_size(),
+                                           _stream(stream))
+    _check(st, "dsa_sparse_mla_attn_bwd_dkv")
 
 
 def dsa_masked_dense_attn(q: dsa_queries, layout: dsa_kv_layout, H: int, q_bf16, kv_bf16, idx: torch.Tensor, k: int,

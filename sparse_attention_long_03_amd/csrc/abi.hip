@@ -217,25 +217,80 @@ int dsa_masked_dense_attn(const dsa_queries* q, const dsa_kv_layout* layout, int
                                       q->max_len, sm_scale, static_cast<uint16_t*>(out_bf16), lse, workspace, stream));
 }
 
+namespace {
+
+// Validation shared by the backward entry points.  `need_fwd` covers the
+// arguments of the dq step (kv, idx, out, lse, dq), `need_dkv` those of the
+// dkv step (dkv).  Fills lay and num_rows.
+int validate_bwd(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H, const void* q_bf16,
+                 const void* kv_bf16, const int32_t* idx, int32_t k, float sm_scale, const void* out_bf16,
+                 const float* lse, const void* d_out_bf16, const float* dq, const float* dkv, const void* workspace,
+                 size_t workspace_bytes, bool need_fwd, bool need_dkv, Layout* lay, int64_t* num_rows) {
+  int st = check_queries(q);
+  if (st) return st;
+  if ((st = check_layout(layout, q, lay))) return st;
+  if (H < 1 || k < 1) return DSA_ERR_INVALID_ARG;
+  if (!(sm_scale > 0.f) || sm_scale != sm_scale) return DSA_ERR_INVALID_ARG;
+  if (k > kMaxK || !attn_bwd_supported(H)) return DSA_ERR_UNSUPPORTED;
+  *num_rows = layout->paged ? (int64_t)layout->num_pages * 64 : (int64_t)q->B * layout->seq_capacity;
+  if (*num_rows >= (int64_t(1) << 31) || !attn_bwd_size_ok(q->T, k)) return DSA_ERR_UNSUPPORTED;
+  if (q->T == 0) return DSA_OK;
+  if (!q_bf16 || !d_out_bf16 || !aligned(q_bf16, 16) || !aligned(d_out_bf16, 16)) return DSA_ERR_INVALID_ARG;
+  if (need_fwd) {
+    if (!kv_bf16 || !idx || !out_bf16 || !lse || !dq) return DSA_ERR_INVALID_ARG;
+    if (!aligned(kv_bf16, 16) || !aligned(out_bf16, 16) || !aligned(dq, 16)) return DSA_ERR_INVALID_ARG;
+  }
+  if (need_dkv && (!dkv || !aligned(dkv, 16))) return DSA_ERR_INVALID_ARG;
+  const size_t need = attn_bwd_workspace_bytes(q->T, H, k);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)) return DSA_ERR_WORKSPACE;
+  return DSA_OK;
+}
+
+}  // namespace
+
 int dsa_sparse_mla_attn_bwd(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H, const void* q_bf16,
                             const void* kv_bf16, const int32_t* idx, int32_t k, float sm_scale, const void* out_bf16,
                             const float* lse, const void* d_out_bf16, float* dq, float* dkv, void* workspace,
                             size_t workspace_bytes, hipStream_t stream) {
   Layout lay;
-  int st = validate_attn(q, layout, H, q_bf16, kv_bf16, idx, k, sm_scale, out_bf16, &lay);
-  if (st) return st;
-  if (!attn_bwd_supported(H)) return DSA_ERR_UNSUPPORTED;
-  const int64_t num_rows = layout->paged ? (int64_t)layout->num_pages * 64 : (int64_t)q->B * layout->seq_capacity;
-  if (num_rows >= (int64_t(1) << 31) || !attn_bwd_size_ok(q->T, k)) return DSA_ERR_UNSUPPORTED;
-  if (q->T == 0) return DSA_OK;
-  if (!lse || !d_out_bf16 || !dq || !dkv) return DSA_ERR_INVALID_ARG;
-  if (!aligned(d_out_bf16, 16) || !aligned(dq, 16) || !aligned(dkv, 16)) return DSA_ERR_INVALID_ARG;
-  const size_t need = attn_bwd_workspace_bytes(q->T, H, k);
-  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)) return DSA_ERR_WORKSPACE;
-  return hip_status(launch_attn_bwd(q->T, H, static_cast<const uint16_t*>(q_bf16),
-                                    static_cast<const uint16_t*>(kv_bf16), idx, q->seq_id, lay, num_rows, k, sm_scale,
-                                    static_cast<const uint16_t*>(out_bf16), lse,
-                                    static_cast<const uint16_t*>(d_out_bf16), dq, dkv, workspace, stream));
+  int64_t num_rows;
+  int st = validate_bwd(q, layout, H, q_bf16, kv_bf16, idx, k, sm_scale, out_bf16, lse, d_out_bf16, dq, dkv,
+                        workspace, workspace_bytes, true, true, &lay, &num_rows);
+  if (st || q->T == 0) return st;
+  const uint16_t* qb = static_cast<const uint16_t*>(q_bf16);
+  const uint16_t* dob = static_cast<const uint16_t*>(d_out_bf16);
+  hipError_t e = launch_attn_bwd_dq(q->T, H, qb, static_cast<const uint16_t*>(kv_bf16), idx, q->seq_id, lay, k,
+                                    sm_scale, static_cast<const uint16_t*>(out_bf16), lse, dob, dq, workspace, stream);
+  if (e != hipSuccess) return DSA_ERR_HIP;
+  return hip_status(launch_attn_bwd_dkv(q->T, H, qb, dob, num_rows, k, dkv, workspace, stream));
+}
+
+int dsa_sparse_mla_attn_bwd_dq(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H, const void* q_bf16,
+                               const void* kv_bf16, const int32_t* idx, int32_t k, float sm_scale,
+                               const void* out_bf16, const float* lse, const void* d_out_bf16, float* dq,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Layout lay;
+  int64_t num_rows;
+  int st = validate_bwd(q, layout, H, q_bf16, kv_bf16, idx, k, sm_scale, out_bf16, lse, d_out_bf16, dq, nullptr,
+                        workspace, workspace_bytes, true, false, &lay, &num_rows);
+  if (st || q->T == 0) return st;
+  return hip_status(launch_attn_bwd_dq(q->T, H, static_cast<const uint16_t*>(q_bf16),
+                                       static_cast<const uint16_t*>(kv_bf16), idx, q->seq_id, lay, k, sm_scale,
+                                       static_cast<const uint16_t*>(out_bf16), lse,
+                                       static_cast<const uint16_t*>(d_out_bf16), dq, workspace, stream));
+}
+
+int dsa_sparse_mla_attn_bwd_dkv(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H, const void* q_bf16,
+                                int32_t k, const void* d_out_bf16, float* dkv, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  Layout lay;
+  int64_t num_rows;
+  int st = validate_bwd(q, layout, H, q_bf16, nullptr, nullptr, k, 1.f, nullptr, nullptr, d_out_bf16, nullptr, dkv,
+                        workspace, workspace_bytes, false, true, &lay, &num_rows);
+  if (st || q->T == 0) return st;
+  return hip_status(launch_attn_bwd_dkv(q->T, H, static_cast<const uint16_t*>(q_bf16),
+                                        static_cast<const uint16_t*>(d_out_bf16), num_rows, k, dkv, workspace,
+                                        stream));
 }
 
 int dsa_forward(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,

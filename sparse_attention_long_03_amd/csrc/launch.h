@@ -62,10 +62,11 @@ hipError_t launch_dense_attn(int T, int H, const uint16_t* q, const uint16_t* kv
 bool attn_bwd_supported(int H);
 bool attn_bwd_size_ok(int T, int k);
 size_t attn_bwd_workspace_bytes(int T, int H, int k);
-hipError_t launch_attn_bwd(int T, int H, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
-                           const int32_t* seq_id, const Layout& lay, int64_t num_rows, int k, float sm_scale,
-                           const uint16_t* out, const float* lse, const uint16_t* dout, float* dq, float* dkv,
-                           void* ws, hipStream_t stream);
+hipError_t launch_attn_bwd_dq(int T, int H, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                              const int32_t* seq_id, const Layout& lay, int k, float sm_scale, const uint16_t* out,
+                              const float* lse, const uint16_t* dout, float* dq, void* ws, hipStream_t stream);
+hipError_t launch_attn_bwd_dkv(int T, int H, const uint16_t* q, const uint16_t* dout, int64_t num_rows, int k,
+                               float* dkv, void* ws, hipStream_t stream);
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 

@@ -97,7 +97,7 @@ __device__ __forceinline__ void attend_tile(const LDS_AS uint8_t* __restrict__ b
   v8bf pb;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float p = exp2f(z[i] - m_use);
+    const float p = __builtin_amdgcn_exp2f(z[i] - m_use);  // v_exp_f32; results below 2^-126 flush to 0
     l_part += p;
     pb[i] = (__bf16)p;
   }

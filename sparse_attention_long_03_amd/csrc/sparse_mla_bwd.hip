@@ -86,8 +86,9 @@ __device__ __forceinline__ void dq_tile(const LDS_AS uint8_t* __restrict__ buf, 
   v8bf pb, db;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float p0 = ((valid >> (4 * g + i)) & 1u) ? exp2f(s0[i] * scale_log2 - lse2) : 0.f;
-    const float p1 = ((valid >> (16 + 4 * g + i)) & 1u) ? exp2f(s1[i] * scale_log2 - lse2) : 0.f;
+    // v_exp_f32 (values below 2^-126 flush to 0, far below bf16's resolution of P)
+    const float p0 = ((valid >> (4 * g + i)) & 1u) ? __builtin_amdgcn_exp2f(s0[i] * scale_log2 - lse2) : 0.f;
+    const float p1 = ((valid >> (16 + 4 * g + i)) & 1u) ? __builtin_amdgcn_exp2f(s1[i] * scale_log2 - lse2) : 0.f;
     pb[i] = (__bf16)p0;
     pb[4 + i] = (__bf16)p1;
     db[i] = (__bf16)(p0 * (d0[i] - dsum) * sm_scale);
@@ -103,28 +104,35 @@ __device__ __forceinline__ void dq_tile(const LDS_AS uint8_t* __restrict__ buf, 
   // dq^T += K^T (scale dS)^T: K^T through the LDS transpose read.  Source
   // lane n of group g points at rows 4g + n/4 (and 16 rows on), dims
   // 16mt + 4(n%4)..+3, so the fragment's K order is the keys' order in db.
+  // Fragments 32..35 are the rope dims, with the rope block's chunk swizzle.
+  // The reads run DPIPE fragments ahead of the MFMAs that use them.
   const LDS_AS uint8_t* vsrc0 = nope + (4 * g + (n >> 2)) * NOPE_STRIDE + 8 * (n & 3);
-  const LDS_AS uint8_t* vsrc1 = vsrc0 + 16 * NOPE_STRIDE;
-#pragma unroll
-  for (int mt = 0; mt < AT_DV / 16; ++mt) {
-    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(vsrc0 + 32 * mt));
-    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(vsrc1 + 32 * mt));
-    const v8bf av = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, db, acc[mt], 0, 0, 0);
-    if ((mt & 7) == 7) __builtin_amdgcn_sched_barrier(0);
-  }
-  // rope dims: the same rows, with the chunk swizzle of the rope block
-  {
-    const int r = 4 * g + (n >> 2);
-#pragma unroll
-    for (int mr = 0; mr < 4; ++mr) {
-      const int c = 2 * mr + ((n & 3) >> 1);
-      const LDS_AS uint8_t* src = rope + r * 128 + 16 * (c ^ (r & 7)) + 8 * (n & 1);
-      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)src);
-      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(src + 16 * 128));
-      const v8bf av = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc[32 + mr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, db, acc[32 + mr], 0, 0, 0);
+  const int rr = 4 * g + (n >> 2);
+  auto kt = [&](int mt) -> v8bf {
+    const LDS_AS uint8_t* p0;
+    int step;
+    if (mt < AT_DV / 16) {
+      p0 = vsrc0 + 32 * mt;
+      step = 16 * NOPE_STRIDE;
+    } else {
+      const int c = 2 * (mt - AT_DV / 16) + ((n & 3) >> 1);
+      p0 = rope + rr * 128 + 16 * (c ^ (rr & 7)) + 8 * (n & 1);
+      step = 16 * 128;
     }
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)p0);
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(p0 + step));
+    return __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  constexpr int DPIPE = 6;
+  constexpr int NKT = AT_D / 16;
+  v8bf ring[DPIPE];
+#pragma unroll
+  for (int j = 0; j < DPIPE; ++j) ring[j] = kt(j);
+#pragma unroll
+  for (int mt = 0; mt < NKT; ++mt) {
+    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[mt % DPIPE], db, acc[mt], 0, 0, 0);
+    if (mt + DPIPE < NKT) ring[mt % DPIPE] = kt(mt + DPIPE);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -601,27 +609,32 @@ size_t attn_bwd_workspace_bytes(int T, int H, int k) {
 
 bool attn_bwd_size_ok(int T, int k) { return (int64_t)T * bwd_kp(k) < (int64_t(1) << 31); }
 
-hipError_t launch_attn_bwd(int T, int H, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
-                           const int32_t* seq_id, const Layout& lay, int64_t num_rows, int k, float sm_scale,
-                           const uint16_t* out, const float* lse, const uint16_t* dout, float* dq, float* dkv,
-                           void* ws, hipStream_t stream) {
+hipError_t launch_attn_bwd_dq(int T, int H, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                              const int32_t* seq_id, const Layout& lay, int k, float sm_scale, const uint16_t* out,
+                              const float* lse, const uint16_t* dout, float* dq, void* ws, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  BwdWorkspace w;
+  carve_bwd(T, H, k, ws, &w);
+  const int kp = bwd_kp(k);
+  const int n_hg = H > 64 ? H / 64 : 1;
+  const int blocks = ((T + 7) / 8) * 8 * n_hg;
+  hipLaunchKernelGGL(sparse_mla_bwd_dq_kernel<4>, dim3(blocks), dim3(256), 0, stream, q,
+                     reinterpret_cast<const uint8_t*>(kv), idx, seq_id, lay, H, k, kp, sm_scale, out, lse, dout, dq,
+                     w.dsp, w.keys_a, w.cnt, T);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_dkv(int T, int H, const uint16_t* q, const uint16_t* dout, int64_t num_rows, int k,
+                               float* dkv, void* ws, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   BwdWorkspace w;
   carve_bwd(T, H, k, ws, &w);
   const int kp = bwd_kp(k);
   const int N = T * kp;
   const int nblocks = (N + RS_BLOCK - 1) / RS_BLOCK;
+  hipError_t e;
 
-  // 1. dq, P / dS, row lists
-  const int n_hg = H > 64 ? H / 64 : 1;
-  const int blocks = ((T + 7) / 8) * 8 * n_hg;
-  hipLaunchKernelGGL(sparse_mla_bwd_dq_kernel<4>, dim3(blocks), dim3(256), 0, stream, q,
-                     reinterpret_cast<const uint8_t*>(kv), idx, seq_id, lay, H, k, kp, sm_scale, out, lse, dout, dq,
-                     w.dsp, w.keys_a, w.cnt, T);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
-  // 2. sort (row, slot) by row
+  // sort (row, slot) by row
   const int passes = sort_passes(num_rows);
   u32 *kin = w.keys_a, *kout = w.keys_b, *vin = nullptr, *vout = w.vals_a;
   for (int p = 0; p < passes; ++p) {
@@ -635,7 +648,7 @@ hipError_t launch_attn_bwd(int T, int H, const uint16_t* q, const uint16_t* kv, 
     vout = (vout == w.vals_a) ? w.vals_b : w.vals_a;
   }
 
-  // 3. per-slot gradients
+  // per-slot gradients
   switch (H) {
     case 16: hipLaunchKernelGGL(sparse_mla_bwd_slot_kernel<16>, dim3(T), dim3(256), 0, stream, q, dout, w.dsp, w.cnt,
                                 kp, w.slot_grad, T); break;
@@ -649,7 +662,7 @@ hipError_t launch_attn_bwd(int T, int H, const uint16_t* q, const uint16_t* kv, 
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
-  // 4. reduction into dkv (sorted keys in kin, slots in vin)
+  // reduction into dkv (sorted keys in kin, slots in vin)
   const int chunks = (N + RD_CHUNK - 1) / RD_CHUNK;
   hipLaunchKernelGGL(dkv_reduce_kernel, dim3((chunks + 3) / 4), dim3(256), 0, stream, kin, vin, N, w.slot_grad,
                      dkv);

@@ -102,6 +102,20 @@ class DSAPath:
                                   self._ws[("bwd", n)], stream)
         return dq, dkv
 
+    def attn_bwd_steps(self, idx: torch.Tensor, d_out: torch.Tensor, dkv: torch.Tensor, stream=None):
+        """The same backward as attn_bwd, as its two steps (dq, then dkv)."""
+        x, c = self.x, self.cfg
+        dq = torch.empty((self.T, c.H, c.D), dtype=torch.float32, device=self.dev)
+        k = idx.shape[1]
+        n = B.dsa_workspace_bytes(B.DSA_OP_ATTN_BWD, self.T, x.max_len, c.H, k)
+        if ("bwd", n) not in self._ws:
+            self._ws[("bwd", n)] = B.workspace(n, self.dev)
+        ws = self._ws[("bwd", n)]
+        B.dsa_sparse_mla_attn_bwd_dq(self.q, self.layout, c.H, x.q, x.kv, idx, k, c.scale, self.out, self.lse, d_out,
+                                     dq, ws, stream)
+        B.dsa_sparse_mla_attn_bwd_dkv(self.q, self.layout, c.H, x.q, k, d_out, dkv, ws, stream)
+        return dq, dkv
+
     def dense_attn(self, idx: torch.Tensor, out=None, lse=None, stream=None):
         """The masked dense variant over the same selection (contiguous rows)."""
         x, c = self.x, self.cfg

@@ -214,4 +214,17 @@ def test_attention_backward_validation(lib):
     assert call(lay_=B.contiguous_layout(1 << 31)) == B.DSA_ERR_UNSUPPORTED
     assert call(q_=_q(T=0, seq=None, pos=None), ptrs=[None] * 8, ws=None, nbytes=0) == B.DSA_OK
     assert B.dsa_workspace_bytes(B.DSA_OP_ATTN_BWD, 0, 100, 128, 2048) == 0
+    # the two steps check their own arguments
+    fdq, fdkv = lib.dsa_sparse_mla_attn_bwd_dq, lib.dsa_sparse_mla_attn_bwd_dkv
+    a = [FAKE] * 7  # q, kv, idx, out, lse, d_out, dq
+    assert fdq(ctypes.byref(q), ctypes.byref(lay), 128, a[0], None, a[2], 2048, 0.1, a[3], a[4], a[5], a[6], FAKE,
+               need, None) == B.DSA_ERR_INVALID_ARG
+    assert fdq(ctypes.byref(q), ctypes.byref(lay), 128, a[0], a[1], a[2], 2048, 0.1, a[3], a[4], a[5], None, FAKE,
+               need, None) == B.DSA_ERR_INVALID_ARG
+    assert fdq(ctypes.byref(q), ctypes.byref(lay), 128, a[0], a[1], a[2], 2048, 0.1, a[3], a[4], a[5], a[6], FAKE,
+               need - 1, None) == B.DSA_ERR_WORKSPACE
+    assert fdkv(ctypes.byref(q), ctypes.byref(lay), 128, FAKE, 2048, FAKE, None, FAKE, need, None) == B.DSA_ERR_INVALID_ARG
+    assert fdkv(ctypes.byref(q), ctypes.byref(lay), 128, None, 2048, FAKE, FAKE, FAKE, need, None) == B.DSA_ERR_INVALID_ARG
+    assert fdkv(ctypes.byref(q), ctypes.byref(lay), 48, FAKE, 2048, FAKE, FAKE, FAKE, need, None) == B.DSA_ERR_UNSUPPORTED
+    assert fdkv(ctypes.byref(q), ctypes.byref(lay), 128, FAKE, 2048, FAKE, FAKE, FAKE, need - 1, None) == B.DSA_ERR_WORKSPACE
     assert B.dsa_workspace_bytes(B.DSA_OP_ATTN_BWD, 8, 100, 128, 2048) > need

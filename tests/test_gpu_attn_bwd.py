@@ -96,6 +96,17 @@ def test_backward_accumulates_into_dkv():
     np.testing.assert_allclose(np_(dkv), 2 * np_(once), rtol=1e-6, atol=1e-12)
 
 
+def test_backward_in_two_steps_equals_one_call():
+    x = I.make_inputs(CASES["h64_paged"], DEV)
+    p, idx, dO, dq, dkv = _run(x)
+    dkv2 = torch.zeros_like(dkv)
+    dq2, dkv2 = p.attn_bwd_steps(idx, dO, dkv2)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2)
+    # the fp32 sums into dkv may run in another order
+    np.testing.assert_allclose(np_(dkv2), np_(dkv), rtol=1e-5, atol=1e-9)
+
+
 def test_backward_heads_are_independent_of_head_groups():
     """128 heads run as two workgroups of 64: the dq of heads 64..127 equals
     that of the same heads run as a 64-head problem."""
