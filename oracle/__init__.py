@@ -28,4 +28,6 @@ from .dsa_oracle import (  # noqa: F401
     cache_write,
     masked_dense_attention,
     sparse_mla_attention_backward,
+    indexer_kl_target,
+    indexer_kl,
 )

@@ -422,3 +422,98 @@ def sparse_mla_attention_backward(q_bits, kv_bits, idx, seq_id, scale: float, d_
         for r, w in enumerate(where):
             dkv[w] += g[r]
     return dq, dkv_sel, dkv
+
+
+# ---------------------------------------------------------------------------
+# (f2) Indexer training signal: KL divergence to the attention distribution
+# ---------------------------------------------------------------------------
+#
+# [DSA-article] "Teaching signal": the indexer learns to imitate the main
+# attention's distribution summed over heads, through a KL divergence; the
+# target takes no gradient (the indexer's gradients stay apart from the
+# language loss).  Reading, for the sparse stage (the selected set of each
+# query; the dense warm-up is the same with every position 0..pos[t]
+# selected):
+#   target   p_t[j] = (1/H) sum_h softmax_h(z_t)[j]   over the selected entries
+#            (the head sum, normalised to total 1)
+#   indexer  q_t[j] = softmax_j(I[t, idx[t, j]])      over the same entries
+#   loss     L_t = sum_j p_t[j] (log p_t[j] - log q_t[j])  (terms with p = 0 are 0)
+#   dL/dI[t, idx[t, j]] = q_t[j] - p_t[j]
+# and through I = sum_h w_h ReLU(qd_h . kd_s), with qd = qs * q8 and
+# kd = ks * k8 the dequantised FP8 query and key (quantisation taken as the
+# identity in the backward):
+#   dL/dw_h  = sum_j dI_j ReLU(qd_h . kd_j)
+#   dL/dqd_h = w_h sum_j dI_j [qd_h . kd_j > 0] kd_j
+#   dL/dkd_j = dI_j sum_h w_h [qd_h . kd_j > 0] qd_h     (added per cache row)
+
+
+def indexer_kl_target(q_bits, kv_bits, idx, seq_id, scale: float, block_table=None, page_size: int = 64):
+    """float64 [T, k]: the head-mean attention probability of each selected
+    entry (0 for padding entries)."""
+    q = decode_bf16(q_bits)
+    kv = decode_bf16(kv_bits)
+    T, H, D = q.shape
+    idx = np.asarray(idx)
+    out = np.zeros(idx.shape)
+    bt = None if block_table is None else np.asarray(block_table)
+    for t in range(T):
+        js = np.nonzero(idx[t] >= 0)[0]
+        if len(js) == 0:
+            continue
+        b = int(seq_id[t])
+        if bt is None:
+            rows = kv[b, idx[t, js]]
+        else:
+            rows = np.stack([kv[int(bt[b, int(s) // page_size]), int(s) % page_size] for s in idx[t, js]])
+        z = scale * (q[t] @ rows.T)                            # [H, n]
+        p = np.exp(z - z.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        out[t, js] = p.mean(axis=0)
+    return out
+
+
+def indexer_kl(q8, qs, w, k8, ks, idx, seq_id, target, block_table=None, page_size: int = 64):
+    """KL loss of the indexer against `target` and its gradients.
+
+    Returns (loss [T], dI [T, k], dq [T, H_I, D_I], dw [T, H_I], dk in the
+    key cache's shape [..., D_I]), float64; padding entries of idx get dI = 0.
+    """
+    qd = decode_e4m3fn(np.asarray(q8)) * np.asarray(qs, dtype=np.float64)[:, None, None]   # [T, H_I, D_I]
+    w = np.asarray(w, dtype=np.float64)
+    k8 = np.asarray(k8)
+    kscale = np.asarray(ks, dtype=np.float64)
+    target = np.asarray(target, dtype=np.float64)
+    idx = np.asarray(idx)
+    T = qd.shape[0]
+    loss = np.zeros(T)
+    dI = np.zeros(idx.shape)
+    dq = np.zeros(qd.shape)
+    dw = np.zeros(w.shape)
+    dk = np.zeros(k8.shape)
+    bt = None if block_table is None else np.asarray(block_table)
+    for t in range(T):
+        js = np.nonzero(idx[t] >= 0)[0]
+        if len(js) == 0:
+            continue
+        b = int(seq_id[t])
+        if bt is None:
+            where = [(b, int(s)) for s in idx[t, js]]
+        else:
+            where = [(int(bt[b, int(s) // page_size]), int(s) % page_size) for s in idx[t, js]]
+        kd = np.stack([decode_e4m3fn(k8[wh]) * kscale[wh] for wh in where])   # [n, D_I]
+        r = qd[t] @ kd.T                                                     # [H_I, n]
+        logit = w[t] @ np.maximum(r, 0.0)                                    # [n]
+        qdist = np.exp(logit - logit.max())
+        qdist /= qdist.sum()
+        p = target[t, js]
+        pos = p > 0
+        loss[t] = np.sum(p[pos] * (np.log(p[pos]) - np.log(qdist[pos])))
+        g = qdist - p                                                        # dL/dI
+        dI[t, js] = g
+        m = (r > 0).astype(np.float64)
+        dw[t] = np.maximum(r, 0.0) @ g
+        dq[t] = w[t][:, None] * ((m * g[None, :]) @ kd)
+        gk = g[:, None] * ((m * w[t][:, None]).T @ qd[t])                    # [n, D_I]
+        for i, wh in enumerate(where):
+            dk[wh] += gk[i]
+    return loss, dI, dq, dw, dk

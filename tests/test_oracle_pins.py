@@ -544,3 +544,114 @@ def test_attention_backward_matches_autograd():
             if idx[t, j] >= 0:
                 acc[seq_id[t], idx[t, j]] += dkv_sel[t, j]
     np.testing.assert_allclose(acc, dkv, rtol=1e-12, atol=1e-14)
+
+
+# ----------------------------------------------------------------- indexer KL signal
+
+def _kl_case(seed=20, T=3, H_I=4, D_I=16, B=2, L=60, k=12):
+    rng = np.random.default_rng(seed)
+    x = torch.from_numpy(rng.normal(size=(T, H_I, D_I)))
+    q8, qs = I.quantize_e4m3fn(x.float())
+    kx = torch.from_numpy(rng.normal(size=(B * L, D_I)))
+    k8, ks = I.quantize_e4m3fn(kx.float())
+    k8 = k8.numpy().reshape(B, L, D_I)
+    ks = ks.numpy().reshape(B, L).astype(np.float64)
+    w = rng.uniform(-0.5, 1.0, size=(T, H_I))
+    seq_id = np.array([0, 1, 1])[:T]
+    idx = np.full((T, k), -1)
+    for t in range(T):
+        n = [k, 7, 1][t]
+        idx[t, rng.choice(k, n, replace=False)] = rng.choice(L, n, replace=False)
+    target = np.zeros((T, k))
+    for t in range(T):
+        js = idx[t] >= 0
+        v = rng.uniform(0.0, 1.0, size=js.sum())
+        v[0] = 0.0 if js.sum() > 2 else v[0]       # a zero target entry
+        target[t, js] = v / v.sum()
+    return q8.numpy(), qs.numpy().astype(np.float64), w, k8, ks, idx, seq_id, target
+
+
+def test_kl_target_matches_head_mean_of_attention():
+    """sum_j p_t[j] kv_j[:512] is the head mean of the attention output (the
+    attention oracle is pinned to SDPA), and each row of p sums to 1."""
+    rng = np.random.default_rng(21)
+    T, H, B, L, k = 3, 6, 2, 50, 10
+    q = I.bf16_bits((torch.randn(T, H, 576) / 5).to(torch.bfloat16))
+    kv = I.bf16_bits((torch.randn(B, L, 576) / 5).to(torch.bfloat16))
+    seq_id = np.array([0, 1, 0])
+    idx = np.full((T, k), -1)
+    for t in range(T):
+        n = [10, 4, 0][t]
+        idx[t, :n] = rng.choice(L, n, replace=False)
+    p = O.indexer_kl_target(q, kv, idx, seq_id, 1 / 24)
+    out, _ = O.sparse_mla_attention(q, kv, idx, seq_id, 1 / 24)
+    kvd = O.decode_bf16(kv)
+    for t in range(2):
+        js = idx[t] >= 0
+        np.testing.assert_allclose(p[t, js] @ kvd[seq_id[t], idx[t, js], :512], out[t].mean(axis=0),
+                                   rtol=1e-12, atol=1e-14)
+        assert abs(p[t].sum() - 1) < 1e-12
+    assert np.all(p[2] == 0) and np.all(p[idx < 0] == 0)
+
+
+def test_kl_loss_and_gradients_by_finite_differences_on_inputs():
+    q8, qs, w, k8, ks, idx, seq_id, target = _kl_case()
+    loss, dI, dq, dw, dk = O.indexer_kl(q8, qs, w, k8, ks, idx, seq_id, target)
+    assert np.all(loss >= 0)
+    np.testing.assert_allclose(dI.sum(axis=1), 0, atol=1e-15)
+    eps = 1e-6
+
+    def L(**kw):
+        a = dict(q8=q8, qs=qs, w=w, k8=k8, ks=ks)
+        a.update(kw)
+        return O.indexer_kl(a["q8"], a["qs"], a["w"], a["k8"], a["ks"], idx, seq_id, target)[0].sum()
+
+    for t, h in [(0, 0), (0, 3), (1, 2)]:
+        e = np.zeros_like(w); e[t, h] = eps
+        fd = (L(w=w + e) - L(w=w - e)) / (2 * eps)
+        assert abs(fd - dw[t, h]) <= 1e-6 * max(1.0, abs(fd))
+    # qd = qs * q8, so dL/dqs[t] = sum_(h,d) dq[t,h,d] q8[t,h,d]
+    for t in range(3):
+        e = np.zeros_like(qs); e[t] = eps * qs[t]
+        fd = (L(qs=qs + e) - L(qs=qs - e)) / (2 * eps * qs[t])
+        assert abs(fd - np.sum(dq[t] * O.decode_e4m3fn(q8[t]))) <= 1e-6 * max(1.0, abs(fd))
+    # kd = ks * k8, so dL/dks[b, s] = sum_d dk[b,s,d] k8[b,s,d] (a selected row, one never selected)
+    for (b, s) in [(int(seq_id[0]), int(idx[0][idx[0] >= 0][0])), (1, int(idx[1][idx[1] >= 0][0]))]:
+        e = np.zeros_like(ks); e[b, s] = eps * ks[b, s]
+        fd = (L(ks=ks + e) - L(ks=ks - e)) / (2 * eps * ks[b, s])
+        assert abs(fd - np.sum(dk[b, s] * O.decode_e4m3fn(k8[b, s]))) <= 1e-6 * max(1.0, abs(fd))
+    unselected = np.setdiff1d(np.arange(k8.shape[1]), idx[seq_id == 0].ravel())
+    assert np.all(dk[0, unselected] == 0)
+
+
+def test_kl_gradients_match_autograd_and_kl_div():
+    q8, qs, w, k8, ks, idx, seq_id, target = _kl_case(seed=22)
+    loss, dI, dq, dw, dk = O.indexer_kl(q8, qs, w, k8, ks, idx, seq_id, target)
+    qd = torch.tensor(O.decode_e4m3fn(q8) * qs[:, None, None], requires_grad=True)
+    kd = torch.tensor(O.decode_e4m3fn(k8) * ks[..., None], requires_grad=True)
+    wt = torch.tensor(w, requires_grad=True)
+    total = 0.0
+    for t in range(qd.shape[0]):
+        js = np.nonzero(idx[t] >= 0)[0]
+        rows = kd[int(seq_id[t])][torch.tensor(idx[t, js])]
+        logit = (wt[t][:, None] * torch.relu(qd[t] @ rows.T)).sum(0)
+        p = torch.tensor(target[t, js])
+        kl = torch.nn.functional.kl_div(torch.log_softmax(logit, 0), p, reduction="sum")
+        np.testing.assert_allclose(kl.item(), loss[t], rtol=1e-12, atol=1e-15)
+        total = total + kl
+    total.backward()
+    np.testing.assert_allclose(dq, qd.grad.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(dw, wt.grad.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(dk, kd.grad.numpy(), rtol=1e-10, atol=1e-13)
+
+
+def test_kl_zero_when_the_indexer_matches_the_target():
+    q8, qs, w, k8, ks, idx, seq_id, _ = _kl_case(seed=23)
+    # target = the indexer's own softmax over each selection
+    _, dI0, _, _, _ = O.indexer_kl(q8, qs, w, k8, ks, idx, seq_id, np.zeros(idx.shape))
+    own = np.where(idx >= 0, dI0, 0.0)            # with p = 0, dI = q (the indexer distribution)
+    loss, dI, dq, dw, dk = O.indexer_kl(q8, qs, w, k8, ks, idx, seq_id, own)
+    np.testing.assert_allclose(loss, 0, atol=1e-14)
+    np.testing.assert_allclose(dI, 0, atol=1e-15)
+    np.testing.assert_allclose(dq, 0, atol=1e-13)
+    np.testing.assert_allclose(dk, 0, atol=1e-13)
