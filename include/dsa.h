@@ -240,6 +240,51 @@ int dsa_sparse_mla_attn_bwd_dkv(const dsa_queries* q, const dsa_kv_layout* layou
                                 size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * (1b) The indexer's training signal ("... Sparse Consideration (DSA)",
+ * "Teaching signal": the indexer learns the main attention's head-summed
+ * distribution through a KL divergence; the target takes no gradient).
+ *
+ * dsa_indexer_kl_target: for the entries j of idx[t, :] (the sparse stage's
+ * selection; the dense warm-up passes every position 0..pos[t]),
+ *     target[t, j] = (1/H) sum_h exp(z[t,h,j] - lse[t,h]),
+ *     z = sm_scale * <q[t,h,:], kv_row_j>,
+ * the head-summed attention probabilities normalised to total 1; 0 for
+ * padding entries (-1).  q, kv, idx, k, sm_scale and lse are those of the
+ * forward (dsa_sparse_mla_attn); the rows sum to 1 up to rounding.
+ *   target    : device float[T, k] (16-byte aligned)
+ *   built     : H in {16, 32, 64, 128}, k <= 2048; no workspace
+ * ------------------------------------------------------------------------- */
+int dsa_indexer_kl_target(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H, const void* q_bf16,
+                          const void* kv_bf16, const int32_t* idx, int32_t k, float sm_scale, const float* lse,
+                          float* target, hipStream_t stream);
+
+/* dsa_indexer_kl: with the indexer logits I (as dsa_indexer_logits) at the
+ * selected entries, q[t, j] = softmax_j I[t, idx[t, j]] over the entries != -1:
+ *     loss[t] = sum_j target[t,j] (log target[t,j] - log q[t,j])
+ * (entries with target 0 contribute 0; the target rows should sum to 1), and
+ * the gradients of sum_t loss[t] through I = sum_h w_h ReLU(qd_h . kd_s),
+ * qd = q_scale * q_fp8 and kd = k_scale * k_fp8 (the FP8 quantisation taken
+ * as the identity), with dI = q - target:
+ *     dw[t,h]   = sum_j dI_j ReLU(qd_h . kd_j)
+ *     dq[t,h,:] = w_h sum_j dI_j [qd_h . kd_j > 0] kd_j
+ *     dk[row_j] += dI_j sum_h w_h [qd_h . kd_j > 0] qd_h
+ *   indexer arguments as for dsa_indexer_logits; built: H_I = 64, D_I = 128
+ *   idx, k    : the selection (k <= 2048)
+ *   target    : device float[T, k], e.g. from dsa_indexer_kl_target
+ *   loss      : device float[T];  dq : device float[T, H_I, D_I];  dw : device float[T, H_I]
+ *   dk        : device float cache, D_I per token in the layout of k_fp8; the
+ *               gradients are ADDED (zero it first); 16-byte aligned
+ *   workspace : device, >= dsa_workspace_bytes(DSA_OP_INDEXER_KL, T, 0, 0, k),
+ *               256-byte aligned (about 17.5 * k bytes per query token)
+ * The per-entry key gradients are rounded to bf16 before their sum per cache
+ * row, as are the ReLU-masked products inside the dq and dk contractions.
+ * ------------------------------------------------------------------------- */
+int dsa_indexer_kl(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,
+                   const uint8_t* q_fp8, const float* q_scale, const float* w, const uint8_t* k_fp8,
+                   const float* k_scale, const int32_t* idx, int32_t k, const float* target, float* loss, float* dq,
+                   float* dw, float* dk, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * (3') Masked dense variant of (3) ("... Sparse Consideration (DSA)", "Lets
  * Discuss it's effectivity and accuracy": at short lengths the prefill runs
  * as a masked dense attention).  For query t every position s <= pos[t] of
@@ -278,6 +323,7 @@ int dsa_forward(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, 
 #define DSA_OP_INDEXER_TOPK 4
 #define DSA_OP_DENSE_ATTN 5
 #define DSA_OP_ATTN_BWD 6
+#define DSA_OP_INDEXER_KL 7
 size_t dsa_workspace_bytes(int32_t op, int32_t T, int32_t max_len, int32_t H, int32_t k);
 
 /* Static string for a status code (never NULL). */

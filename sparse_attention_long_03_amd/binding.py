@@ -23,6 +23,7 @@ DSA_ERR_UNSUPPORTED = -2
 DSA_ERR_WORKSPACE = -3
 DSA_ERR_HIP = -4
 DSA_OP_TOPK, DSA_OP_ATTN, DSA_OP_FORWARD, DSA_OP_INDEXER_TOPK, DSA_OP_DENSE_ATTN, DSA_OP_ATTN_BWD = 1, 2, 3, 4, 5, 6
+DSA_OP_INDEXER_KL = 7
 
 
 class DSAError(RuntimeError):
@@ -43,7 +44,8 @@ class dsa_kv_layout(ctypes.Structure):
 
 EXPORTS = ("dsa_cache_write", "dsa_indexer_logits", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_attn",
            "dsa_sparse_mla_attn_bwd", "dsa_sparse_mla_attn_bwd_dq", "dsa_sparse_mla_attn_bwd_dkv",
-           "dsa_masked_dense_attn", "dsa_forward", "dsa_workspace_bytes", "dsa_status_str", "dsa_abi_version")
+           "dsa_indexer_kl_target", "dsa_indexer_kl", "dsa_masked_dense_attn", "dsa_forward", "dsa_workspace_bytes",
+           "dsa_status_str", "dsa_abi_version")
 
 _lib = None
 
@@ -66,6 +68,8 @@ def lib() -> ctypes.CDLL:
     L.dsa_sparse_mla_attn_bwd.argtypes = [Q, KV, i32, vp, vp, vp, i32, f32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_sparse_mla_attn_bwd_dq.argtypes = [Q, KV, i32, vp, vp, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_sparse_mla_attn_bwd_dkv.argtypes = [Q, KV, i32, vp, i32, vp, vp, vp, sz, vp]
+    L.dsa_indexer_kl_target.argtypes = [Q, KV, i32, vp, vp, vp, i32, f32, vp, vp, vp]
+    L.dsa_indexer_kl.argtypes = [Q, KV, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_masked_dense_attn.argtypes = [Q, KV, i32, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
     L.dsa_forward.argtypes = [Q, KV, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]
     L.dsa_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
@@ -206,6 +210,21 @@ def dsa_sparse_mla_attn_bwd_dkv(q: dsa_queries, layout: dsa_kv_layout, H: int, q
                                            _ptr(d_out_bf16), _ptr(dkv), _ptr(ws), ws.numel() * ws.element_size(),
                                            _stream(stream))
     _check(st, "dsa_sparse_mla_attn_bwd_dkv")
+
+
+def dsa_indexer_kl_target(q: dsa_queries, layout: dsa_kv_layout, H: int, q_bf16, kv_bf16, idx: torch.Tensor, k: int,
+                          sm_scale: float, lse, target, stream=None):
+    st = lib().dsa_indexer_kl_target(ctypes.byref(q), ctypes.byref(layout), H, _ptr(q_bf16), _ptr(kv_bf16), _ptr(idx),
+                                     int(k), float(sm_scale), _ptr(lse), _ptr(target), _stream(stream))
+    _check(st, "dsa_indexer_kl_target")
+
+
+def dsa_indexer_kl(q: dsa_queries, layout: dsa_kv_layout, H_I: int, D_I: int, q_fp8, q_scale, w, k_fp8, k_scale,
+                   idx: torch.Tensor, k: int, target, loss, dq, dw, dk, ws: torch.Tensor, stream=None):
+    st = lib().dsa_indexer_kl(ctypes.byref(q), ctypes.byref(layout), H_I, D_I, _ptr(q_fp8), _ptr(q_scale), _ptr(w),
+                              _ptr(k_fp8), _ptr(k_scale), _ptr(idx), int(k), _ptr(target), _ptr(loss), _ptr(dq),
+                              _ptr(dw), _ptr(dk), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "dsa_indexer_kl")
 
 
 def dsa_masked_dense_attn(q: dsa_queries, layout: dsa_kv_layout, H: int, q_bf16, kv_bf16, idx: torch.Tensor, k: int,

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
 SOURCES = ["abi.hip", "cache_write.hip", "indexer.hip", "indexer_topk.hip", "topk.hip", "sparse_mla.hip",
-           "sparse_mla_bwd.hip"]
+           "sparse_mla_bwd.hip", "row_scatter.hip", "indexer_kl.hip"]
 ARCH = "gfx950"
 
 
@@ -41,7 +41,8 @@ def _flags():
 
 # Per-file code-generation options.  The indexer reads its MFMA results with
 # VALU code, so it asks for the VGPR form of the MFMAs (no AGPR round trips).
-EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "indexer_topk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "indexer_topk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "indexer_kl.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -126,6 +126,7 @@ size_t dsa_workspace_bytes(int32_t op, int32_t T, int32_t max_len, int32_t H, in
     case DSA_OP_INDEXER_TOPK: return (k > 0) ? fused_topk_workspace_bytes(T, fused_topk_cap(max_len, k)) : 0;
     case DSA_OP_DENSE_ATTN: return (H > 0) ? dense_attn_workspace_bytes(T, H, max_len) : 0;
     case DSA_OP_ATTN_BWD: return (H > 0 && k > 0 && attn_bwd_size_ok(T, k)) ? attn_bwd_workspace_bytes(T, H, k) : 0;
+    case DSA_OP_INDEXER_KL: return (k > 0 && kl_size_ok(T, k)) ? kl_workspace_bytes(T, k) : 0;
     default: return 0;
   }
 }
@@ -291,6 +292,38 @@ int dsa_sparse_mla_attn_bwd_dkv(const dsa_queries* q, const dsa_kv_layout* layou
   return hip_status(launch_attn_bwd_dkv(q->T, H, static_cast<const uint16_t*>(q_bf16),
                                         static_cast<const uint16_t*>(d_out_bf16), num_rows, k, dkv, workspace,
                                         stream));
+}
+
+int dsa_indexer_kl_target(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H, const void* q_bf16,
+                          const void* kv_bf16, const int32_t* idx, int32_t k, float sm_scale, const float* lse,
+                          float* target, hipStream_t stream) {
+  Layout lay;
+  int st = validate_attn(q, layout, H, q_bf16, kv_bf16, idx, k, sm_scale, target, &lay);
+  if (st || q->T == 0) return st;
+  if (!lse || !aligned(target, 4)) return DSA_ERR_INVALID_ARG;
+  return hip_status(launch_kl_target(q->T, H, static_cast<const uint16_t*>(q_bf16),
+                                     static_cast<const uint16_t*>(kv_bf16), idx, q->seq_id, lay, k, sm_scale, lse,
+                                     target, stream));
+}
+
+int dsa_indexer_kl(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,
+                   const uint8_t* q_fp8, const float* q_scale, const float* w, const uint8_t* k_fp8,
+                   const float* k_scale, const int32_t* idx, int32_t k, const float* target, float* loss, float* dq,
+                   float* dw, float* dk, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Layout lay;
+  int st = validate_indexer_inputs(q, layout, H_I, D_I, q_fp8, q_scale, w, k_fp8, k_scale, &lay);
+  if (st) return st;
+  if (!kl_supported(H_I, D_I)) return DSA_ERR_UNSUPPORTED;
+  if (k < 1) return DSA_ERR_INVALID_ARG;
+  const int64_t num_rows = layout->paged ? (int64_t)layout->num_pages * 64 : (int64_t)q->B * layout->seq_capacity;
+  if (k > kMaxK || num_rows >= (int64_t(1) << 31) || !kl_size_ok(q->T, k)) return DSA_ERR_UNSUPPORTED;
+  if (q->T == 0) return DSA_OK;
+  if (!idx || !target || !loss || !dq || !dw || !dk) return DSA_ERR_INVALID_ARG;
+  if (!aligned(dk, 16) || !aligned(dq, 16)) return DSA_ERR_INVALID_ARG;
+  const size_t need = kl_workspace_bytes(q->T, k);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)) return DSA_ERR_WORKSPACE;
+  return hip_status(launch_kl(q->T, q_fp8, q_scale, w, k_fp8, k_scale, idx, q->seq_id, lay, num_rows, k, target, loss,
+                              dq, dw, dk, workspace, stream));
 }
 
 int dsa_forward(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,

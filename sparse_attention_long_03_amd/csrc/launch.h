@@ -57,6 +57,13 @@ hipError_t launch_dense_attn(int T, int H, const uint16_t* q, const uint16_t* kv
                              const int32_t* seq_id, const int32_t* pos, const Layout& lay, int k, int max_len,
                              float sm_scale, uint16_t* out, float* lse, void* ws, hipStream_t stream);
 
+// scatter-add of bf16 rows (W = 576 or 128 values) into an fp32 table:
+// dst[rows[i]] += src_rows[i] for every i with rows[i] != 0xFFFFFFFF; rows is
+// overwritten (it is the first buffer of the sort); num_rows bounds the ids.
+size_t row_scatter_workspace_bytes(int64_t N);
+hipError_t launch_row_scatter_add(u32* rows, int N, int64_t num_rows, const uint16_t* src_rows, int W, float* dst,
+                                  void* ws, hipStream_t stream);
+
 // (3) backward: dq, and the gradients of the selected rows added into dkv
 // (fp32, 576 per cache row; num_rows = rows of the cache)
 bool attn_bwd_supported(int H);
@@ -67,6 +74,19 @@ hipError_t launch_attn_bwd_dq(int T, int H, const uint16_t* q, const uint16_t* k
                               const float* lse, const uint16_t* dout, float* dq, void* ws, hipStream_t stream);
 hipError_t launch_attn_bwd_dkv(int T, int H, const uint16_t* q, const uint16_t* dout, int64_t num_rows, int k,
                                float* dkv, void* ws, hipStream_t stream);
+
+// indexer KL training signal: target (head-mean attention probabilities of
+// the selected entries) and the loss with its gradients (H_I = 64, D_I = 128)
+bool kl_supported(int H_I, int D_I);
+bool kl_size_ok(int T, int k);
+size_t kl_workspace_bytes(int T, int k);
+hipError_t launch_kl_target(int T, int H, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                            const int32_t* seq_id, const Layout& lay, int k, float sm_scale, const float* lse,
+                            float* target, hipStream_t stream);
+hipError_t launch_kl(int T, const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8, const float* ks,
+                     const int32_t* idx, const int32_t* seq_id, const Layout& lay, int64_t num_rows, int k,
+                     const float* target, float* loss, float* dq, float* dw, float* dk, void* ws,
+                     hipStream_t stream);
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 

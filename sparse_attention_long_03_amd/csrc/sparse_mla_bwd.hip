@@ -12,32 +12,26 @@
 // contraction over heads, and a cache row selected by several queries
 // collects all their contributions.
 //
-// Four steps, chosen for the memory system of the MI355X:
+// Three steps, chosen for the memory system of the MI355X:
 //   1. dq kernel, per (token, 64 heads): the forward's row gather and tile
 //      pipeline; per tile it rebuilds S and dP (the no-rope K fragments feed
 //      both), then P and dS in registers, accumulates dq^T += K^T dS^T with
 //      K^T read through the LDS transpose read, and stores P and scale*dS as
-//      bf16 per (token, head, slot).
-//   2. stable LSD radix sort of the selected cache rows of all (token, slot)
-//      pairs (8-bit digits).
-//   3. slot kernel, per token, all heads: the gradient of each selected slot,
+//      bf16 per (token, head, slot) together with the token's row list.
+//   2. slot kernel, per token, all heads: the gradient of each selected slot,
 //      [scale dS; P]^T [q; dO] -- a contraction over 2H stacked rows -- on
 //      bf16 MFMAs.  q and dO are constant per token, so each wave keeps its
 //      slice of [q; dO]^T in registers (read once through the LDS transpose
 //      read) and streams the P / dS tiles; one bf16 row of 576 per slot.
-//   4. segmented reduction: the sorted (row, slot) list is cut into chunks of
-//      256; a wave sums each run of equal rows of its chunk in fp32 and adds
-//      it to the fp32 dkv row with one atomic per value.
-// fp32 atomics reach only about a fifth of the store bandwidth on this GPU,
-// so adding every slot's gradient straight into dkv (T * k * 576 atomics)
-// would cost several times steps 3 and 4 together; the sort reduces the
-// atomics to one per (run, value).
+//   3. the per-slot rows are added into dkv through a sort of the row list
+//      (row_scatter.hip): one fp32 atomic per (run of equal rows, value)
+//      instead of one per (slot, value).
 #include "attn_tile.h"
 #include "launch.h"
 
 namespace dsa {
 
-constexpr u32 SLOT_NONE = 0xFFFFFFFFu;  // row list entry past a token's selected slots
+constexpr u32 SLOT_NONE = 0xFFFFFFFFu;  // row list entry past a token's selected slots (sorts last)
 constexpr float LOG2E = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
@@ -235,110 +229,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 2. stable LSD radix sort of the row list (8-bit digits)
-// ---------------------------------------------------------------------------
-
-constexpr int RS_NT = 256;
-constexpr int RS_ROUNDS = 16;
-constexpr int RS_BLOCK = RS_NT * RS_ROUNDS;  // elements per block
-
-// per-block digit counts, digit-major: hist[d * nblocks + block]
-__global__ __launch_bounds__(RS_NT) void radix_hist_kernel(const u32* __restrict__ keys, int N, int shift,
-                                                            u32* __restrict__ hist, int nblocks) {
-  __shared__ u32 h[256];
-  const int tid = threadIdx.x;
-  h[tid] = 0;
-  __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * RS_BLOCK;
-#pragma unroll 4
-  for (int r = 0; r < RS_ROUNDS; ++r) {
-    const int64_t i = base + r * RS_NT + tid;
-    if (i < N) atomicAdd(&h[(keys[i] >> shift) & 255u], 1u);
-  }
-  __syncthreads();
-  hist[(int64_t)tid * nblocks + blockIdx.x] = h[tid];
-}
-
-// one workgroup per digit: exclusive scan of its counts over the blocks
-__global__ __launch_bounds__(RS_NT) void radix_scan_kernel(u32* __restrict__ hist, int nblocks,
-                                                            u32* __restrict__ totals) {
-  __shared__ u32 scratch[RS_NT / 64 + 1];
-  u32* row = hist + (int64_t)blockIdx.x * nblocks;
-  u32 carry = 0;
-  for (int i0 = 0; i0 < nblocks; i0 += RS_NT) {
-    const int i = i0 + threadIdx.x;
-    const u32 v = (i < nblocks) ? row[i] : 0u;
-    u32 tot;
-    const u32 incl = block_incl_scan<RS_NT>(v, scratch, &tot);
-    if (i < nblocks) row[i] = carry + incl - v;
-    carry += tot;
-  }
-  if (threadIdx.x == 0) totals[blockIdx.x] = carry;
-}
-
-// Scatter in a stable order: each round takes RS_NT consecutive elements;
-// lanes with equal digits find each other with 8 ballots, and the waves of
-// a round are ranked in order through per-wave digit counts in LDS.
-__global__ __launch_bounds__(RS_NT) void radix_scatter_kernel(const u32* __restrict__ keys_in,
-                                                               const u32* __restrict__ vals_in, int N, int shift,
-                                                               const u32* __restrict__ hist,
-                                                               const u32* __restrict__ totals, int nblocks,
-                                                               u32* __restrict__ keys_out,
-                                                               u32* __restrict__ vals_out) {
-  constexpr int NWV = RS_NT / 64;
-  __shared__ u32 s_base[256];
-  __shared__ u32 s_wcnt[NWV][256];
-  __shared__ u32 scratch[NWV + 1];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wid = tid >> 6;
-  {
-    const u32 tot_d = totals[tid];
-    u32 all;
-    const u32 incl = block_incl_scan<RS_NT>(tot_d, scratch, &all);
-    s_base[tid] = incl - tot_d + hist[(int64_t)tid * nblocks + blockIdx.x];
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) s_wcnt[w][tid] = 0;
-  }
-  __syncthreads();
-  const unsigned long long below = (1ull << lane) - 1ull;
-  const int64_t base = (int64_t)blockIdx.x * RS_BLOCK;
-  for (int r = 0; r < RS_ROUNDS; ++r) {
-    const int64_t i = base + r * RS_NT + tid;
-    const bool valid = i < N;
-    const u32 key = valid ? keys_in[i] : 0u;
-    const u32 val = valid ? (vals_in ? vals_in[i] : (u32)i) : 0u;
-    const u32 dig = (key >> shift) & 255u;
-    unsigned long long peers = __builtin_amdgcn_ballot_w64(valid);
-#pragma unroll
-    for (int bit = 0; bit < 8; ++bit) {
-      const bool set = (dig >> bit) & 1u;
-      const unsigned long long bb = __builtin_amdgcn_ballot_w64(set);
-      peers &= set ? bb : ~bb;
-    }
-    const u32 rank = (u32)__popcll(peers & below);
-    if (valid && rank == 0) s_wcnt[wid][dig] = (u32)__popcll(peers);
-    __syncthreads();
-    if (valid) {
-      u32 pos = s_base[dig] + rank;
-      for (int w = 0; w < wid; ++w) pos += s_wcnt[w][dig];
-      keys_out[pos] = key;
-      vals_out[pos] = val;
-    }
-    __syncthreads();
-    u32 add = 0;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) {
-      add += s_wcnt[w][tid];
-      s_wcnt[w][tid] = 0;
-    }
-    s_base[tid] += add;
-    __syncthreads();
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 3. per-slot gradients
+// 2. per-slot gradients
 // ---------------------------------------------------------------------------
 
 constexpr int XS_STRIDE = AT_ROW_BYTES + 16;  // staged [q; dO] row in LDS (1168 B)
@@ -475,85 +366,6 @@ __global__ __launch_bounds__(256) void sparse_mla_bwd_slot_kernel(const uint16_t
 }
 
 // ---------------------------------------------------------------------------
-// 4. segmented reduction into dkv
-// ---------------------------------------------------------------------------
-
-constexpr int RD_CHUNK = 256;  // sorted entries per wave
-
-__device__ __forceinline__ void add_bf16x8(float* acc, v4i x) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    acc[2 * i] += __uint_as_float((u32)x[i] << 16);
-    acc[2 * i + 1] += __uint_as_float((u32)x[i] & 0xFFFF0000u);
-  }
-}
-
-// Wave: a chunk of the sorted (row, slot) list.  Lane l sums dims 8l..8l+7
-// (and lanes l < 8 also 512+8l..+7) of the slots of a run of equal rows, then
-// adds the run to dkv with fp32 atomics (a run may continue in the next chunk).
-__global__ __launch_bounds__(256) void dkv_reduce_kernel(const u32* __restrict__ keys, const u32* __restrict__ vals,
-                                                         int N, const uint16_t* __restrict__ slot_grad,
-                                                         float* __restrict__ dkv) {
-  const int lane = threadIdx.x & 63;
-  const int64_t base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RD_CHUNK;
-  if (base >= N) return;
-  float a0[8], a1[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) a0[i] = a1[i] = 0.f;
-  u32 cur = SLOT_NONE;
-  bool done = false;
-  auto flush = [&]() {
-    float* dst = dkv + (int64_t)cur * AT_D + 8 * lane;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __hip_atomic_fetch_add(dst + i, a0[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      a0[i] = 0.f;
-    }
-    if (lane < 8) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) __hip_atomic_fetch_add(dst + AT_DV + i, a1[i], __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a1[i] = 0.f;
-  };
-  for (int sub = 0; sub < RD_CHUNK / 64; ++sub) {
-    const int64_t j = base + 64 * sub + lane;
-    const u32 kj = (j < N) ? keys[j] : SLOT_NONE;
-    const u32 vj = (j < N) ? vals[j] : 0u;
-    if (__builtin_amdgcn_readfirstlane(kj) == SLOT_NONE) break;  // the rest of the list is past the end
-#pragma unroll 1
-    for (int e0 = 0; e0 < 64 && !done; e0 += 8) {
-      v4i x0[8], x1[8];
-      u32 ke[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        ke[u] = __builtin_amdgcn_readlane(kj, e0 + u);
-        const u32 ve = __builtin_amdgcn_readlane(vj, e0 + u);
-        const uint16_t* src = slot_grad + (int64_t)(ke[u] == SLOT_NONE ? 0u : ve) * AT_D;
-        x0[u] = *reinterpret_cast<const v4i*>(src + 8 * lane);
-        x1[u] = *reinterpret_cast<const v4i*>(src + AT_DV + 8 * (lane & 7));
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (ke[u] == SLOT_NONE) {
-          done = true;
-          break;
-        }
-        if (ke[u] != cur) {
-          if (cur != SLOT_NONE) flush();
-          cur = ke[u];
-        }
-        add_bf16x8(a0, x0[u]);
-        if (lane < 8) add_bf16x8(a1, x1[u]);
-      }
-    }
-    if (done) break;
-  }
-  if (cur != SLOT_NONE) flush();
-}
-
-// ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
 
@@ -561,29 +373,21 @@ bool attn_bwd_supported(int H) { return H == 16 || H == 32 || H == 64 || H == 12
 
 static int bwd_kp(int k) { return ((k + AT_TILE - 1) / AT_TILE) * AT_TILE; }
 
-static int sort_passes(int64_t num_rows) {
-  int bits = 0;
-  while (bits < 32 && (int64_t(1) << bits) <= num_rows) ++bits;  // bit length of num_rows
-  return (bits + 7) / 8;
-}
-
 struct BwdWorkspace {
   uint16_t* dsp;
   uint16_t* slot_grad;
-  u32 *keys_a, *keys_b, *vals_a, *vals_b;
+  u32* rows;
   int32_t* cnt;
-  u32 *hist, *totals;
+  void* scatter;
 };
 
 // Carves the workspace (base may be null: then only the size is computed).
 static size_t carve_bwd(int T, int H, int k, void* base, BwdWorkspace* w) {
   const size_t kp = (size_t)bwd_kp(k);
   const size_t N = (size_t)T * kp;
-  const size_t nblocks = (N + RS_BLOCK - 1) / RS_BLOCK;
-  const size_t sizes[9] = {N * 2 * H * 2, N * AT_D * 2, N * 4, N * 4, N * 4, N * 4, (size_t)T * 4, 256 * nblocks * 4,
-                           256 * 4};
-  size_t off[9], total = 0;
-  for (int i = 0; i < 9; ++i) {
+  const size_t sizes[5] = {N * 2 * H * 2, N * AT_D * 2, N * 4, (size_t)T * 4, row_scatter_workspace_bytes(N)};
+  size_t off[5], total = 0;
+  for (int i = 0; i < 5; ++i) {
     off[i] = total;
     total += align256(sizes[i]);
   }
@@ -591,13 +395,9 @@ static size_t carve_bwd(int T, int H, int k, void* base, BwdWorkspace* w) {
     char* p = static_cast<char*>(base);
     w->dsp = reinterpret_cast<uint16_t*>(p + off[0]);
     w->slot_grad = reinterpret_cast<uint16_t*>(p + off[1]);
-    w->keys_a = reinterpret_cast<u32*>(p + off[2]);
-    w->keys_b = reinterpret_cast<u32*>(p + off[3]);
-    w->vals_a = reinterpret_cast<u32*>(p + off[4]);
-    w->vals_b = reinterpret_cast<u32*>(p + off[5]);
-    w->cnt = reinterpret_cast<int32_t*>(p + off[6]);
-    w->hist = reinterpret_cast<u32*>(p + off[7]);
-    w->totals = reinterpret_cast<u32*>(p + off[8]);
+    w->rows = reinterpret_cast<u32*>(p + off[2]);
+    w->cnt = reinterpret_cast<int32_t*>(p + off[3]);
+    w->scatter = p + off[4];
   }
   return total;
 }
@@ -620,7 +420,7 @@ hipError_t launch_attn_bwd_dq(int T, int H, const uint16_t* q, const uint16_t* k
   const int blocks = ((T + 7) / 8) * 8 * n_hg;
   hipLaunchKernelGGL(sparse_mla_bwd_dq_kernel<4>, dim3(blocks), dim3(256), 0, stream, q,
                      reinterpret_cast<const uint8_t*>(kv), idx, seq_id, lay, H, k, kp, sm_scale, out, lse, dout, dq,
-                     w.dsp, w.keys_a, w.cnt, T);
+                     w.dsp, w.rows, w.cnt, T);
   return hipGetLastError();
 }
 
@@ -631,22 +431,7 @@ hipError_t launch_attn_bwd_dkv(int T, int H, const uint16_t* q, const uint16_t* 
   carve_bwd(T, H, k, ws, &w);
   const int kp = bwd_kp(k);
   const int N = T * kp;
-  const int nblocks = (N + RS_BLOCK - 1) / RS_BLOCK;
   hipError_t e;
-
-  // sort (row, slot) by row
-  const int passes = sort_passes(num_rows);
-  u32 *kin = w.keys_a, *kout = w.keys_b, *vin = nullptr, *vout = w.vals_a;
-  for (int p = 0; p < passes; ++p) {
-    hipLaunchKernelGGL(radix_hist_kernel, dim3(nblocks), dim3(RS_NT), 0, stream, kin, N, 8 * p, w.hist, nblocks);
-    hipLaunchKernelGGL(radix_scan_kernel, dim3(256), dim3(RS_NT), 0, stream, w.hist, nblocks, w.totals);
-    hipLaunchKernelGGL(radix_scatter_kernel, dim3(nblocks), dim3(RS_NT), 0, stream, kin, vin, N, 8 * p, w.hist,
-                       w.totals, nblocks, kout, vout);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    std::swap(kin, kout);
-    vin = vout;
-    vout = (vout == w.vals_a) ? w.vals_b : w.vals_a;
-  }
 
   // per-slot gradients
   switch (H) {
@@ -662,11 +447,8 @@ hipError_t launch_attn_bwd_dkv(int T, int H, const uint16_t* q, const uint16_t* 
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
-  // reduction into dkv (sorted keys in kin, slots in vin)
-  const int chunks = (N + RD_CHUNK - 1) / RD_CHUNK;
-  hipLaunchKernelGGL(dkv_reduce_kernel, dim3((chunks + 3) / 4), dim3(256), 0, stream, kin, vin, N, w.slot_grad,
-                     dkv);
-  return hipGetLastError();
+  // the per-slot rows into dkv, through the sort of the row list
+  return launch_row_scatter_add(w.rows, N, num_rows, w.slot_grad, AT_D, dkv, w.scatter, stream);
 }
 
 }  // namespace dsa

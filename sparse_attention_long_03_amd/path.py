@@ -116,6 +116,34 @@ class DSAPath:
         B.dsa_sparse_mla_attn_bwd_dkv(self.q, self.layout, c.H, x.q, k, d_out, dkv, ws, stream)
         return dq, dkv
 
+    def kl_target(self, idx: torch.Tensor, lse=None, stream=None) -> torch.Tensor:
+        """Head-mean attention probabilities of the selected entries (the
+        indexer's KL target), from the forward's lse (the last attn() call's
+        by default)."""
+        x, c = self.x, self.cfg
+        lse = self.lse if lse is None else lse
+        target = torch.empty(idx.shape, dtype=torch.float32, device=self.dev)
+        B.dsa_indexer_kl_target(self.q, self.layout, c.H, x.q, x.kv, idx, idx.shape[1], c.scale, lse, target, stream)
+        return target
+
+    def indexer_kl(self, idx: torch.Tensor, target: torch.Tensor, dk=None, stream=None):
+        """KL loss of the indexer against `target` and its gradients:
+        (loss [T], dq [T, H_I, D_I], dw [T, H_I], dk in the key cache's
+        layout, added into `dk` when one is given)."""
+        x, c = self.x, self.cfg
+        k = idx.shape[1]
+        loss = torch.empty((self.T,), dtype=torch.float32, device=self.dev)
+        dq = torch.empty((self.T, c.H_I, c.D_I), dtype=torch.float32, device=self.dev)
+        dw = torch.empty((self.T, c.H_I), dtype=torch.float32, device=self.dev)
+        if dk is None:
+            dk = torch.zeros(x.ik8.shape, dtype=torch.float32, device=self.dev)
+        n = B.dsa_workspace_bytes(B.DSA_OP_INDEXER_KL, self.T, x.max_len, 0, k)
+        if ("kl", n) not in self._ws:
+            self._ws[("kl", n)] = B.workspace(n, self.dev)
+        B.dsa_indexer_kl(self.q, self.layout, c.H_I, c.D_I, x.iq8, x.iqs, x.iw, x.ik8, x.iks, idx, k, target, loss, dq,
+                         dw, dk, self._ws[("kl", n)], stream)
+        return loss, dq, dw, dk
+
     def dense_attn(self, idx: torch.Tensor, out=None, lse=None, stream=None):
         """The masked dense variant over the same selection (contiguous rows)."""
         x, c = self.x, self.cfg

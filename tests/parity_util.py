@@ -152,3 +152,56 @@ def check_bwd(gpu, ref, mag, what=""):
                            f"worst ratio {np.max(err / np.maximum(mag, 1e-30)):.3g}")
     fro = np.linalg.norm(g - o) / max(np.linalg.norm(o), 1e-30)
     assert fro <= BWD_FRO, f"{what}: relative Frobenius error {fro}"
+
+
+# Indexer KL signal.  With indexer inputs whose FP8 values are small integers
+# (exact_indexer_inputs) every q8 . k8 dot product is exact in fp32, so the
+# logits match the oracle's up to the fp32 scaling: loss, dI and dw are
+# compared at 1e-4 relative (plus an absolute floor), and dq / dk -- whose
+# contractions take w*q8 and dI*ks*k8 rounded to bf16, and whose per-entry
+# key gradients are rounded to bf16 -- within 2^-7 of the sum of the absolute
+# values of their terms (the same rule as the attention backward).
+KL_REL = 1e-4
+
+
+def exact_indexer_inputs(x, seed=5):
+    """Overwrite the indexer's FP8 query and key codes with codes of the
+    integers -4..4 and set moderate scales (logits of order 1-10)."""
+    codes = torch.tensor([0x00, 0x38, 0x40, 0x44, 0x48, 0xB8, 0xC0, 0xC4, 0xC8], dtype=torch.uint8)
+    g = torch.Generator().manual_seed(seed)
+    x.iq8.copy_(codes[torch.randint(0, 9, tuple(x.iq8.shape), generator=g)].to(x.iq8.device))
+    x.ik8.copy_(codes[torch.randint(0, 9, tuple(x.ik8.shape), generator=g)].to(x.ik8.device))
+    x.iqs.fill_(0.125)
+    x.iks.copy_((0.0625 + 0.0625 * torch.rand(tuple(x.iks.shape), generator=g)).to(x.iks.device))
+    return x
+
+
+def kl_magnitudes(q8, qs, w, k8, ks, idx, seq_id, dI, block_table=None, page_size=64):
+    """(M_dq [T, H_I, D_I], M_dk in the key cache's shape, M_dw [T, H_I]):
+    sums of the absolute values of the terms of each dq, dk and dw entry."""
+    qd = O.decode_e4m3fn(np.asarray(q8)) * np.asarray(qs, np.float64)[:, None, None]
+    w = np.asarray(w, np.float64)
+    k8 = np.asarray(k8)
+    ks = np.asarray(ks, np.float64)
+    m_dq = np.zeros(qd.shape)
+    m_dk = np.zeros(k8.shape)
+    m_dw = np.zeros(w.shape)
+    for t in range(qd.shape[0]):
+        js = np.nonzero(np.asarray(idx[t]) >= 0)[0]
+        if len(js) == 0:
+            continue
+        b = int(seq_id[t])
+        if block_table is None:
+            where = [(b, int(s)) for s in idx[t, js]]
+        else:
+            where = [(int(block_table[b, int(s) // page_size]), int(s) % page_size) for s in idx[t, js]]
+        kd = np.stack([O.decode_e4m3fn(k8[wh]) * ks[wh] for wh in where])
+        r = qd[t] @ kd.T                                           # [H_I, n]
+        m = (r > 0).astype(np.float64)
+        a = np.abs(dI[t, js])
+        m_dw[t] = np.maximum(r, 0.0) @ a
+        m_dq[t] = np.abs(w[t])[:, None] * ((m * a[None, :]) @ np.abs(kd))
+        gk = a[:, None] * ((m * np.abs(w[t])[:, None]).T @ np.abs(qd[t]))
+        for i, wh in enumerate(where):
+            m_dk[wh] += gk[i]
+    return m_dq, m_dk, m_dw

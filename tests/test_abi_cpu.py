@@ -228,3 +228,32 @@ def test_attention_backward_validation(lib):
     assert fdkv(ctypes.byref(q), ctypes.byref(lay), 48, FAKE, 2048, FAKE, FAKE, FAKE, need, None) == B.DSA_ERR_UNSUPPORTED
     assert fdkv(ctypes.byref(q), ctypes.byref(lay), 128, FAKE, 2048, FAKE, FAKE, FAKE, need - 1, None) == B.DSA_ERR_WORKSPACE
     assert B.dsa_workspace_bytes(B.DSA_OP_ATTN_BWD, 8, 100, 128, 2048) > need
+
+
+def test_indexer_kl_validation(lib):
+    q, lay = _q(T=4), _lay()
+    ft, fk = lib.dsa_indexer_kl_target, lib.dsa_indexer_kl
+    # target: as the attention's arguments, plus lse
+    assert ft(ctypes.byref(q), ctypes.byref(lay), 48, FAKE, FAKE, FAKE, 64, 0.1, FAKE, FAKE, None) == B.DSA_ERR_UNSUPPORTED
+    assert ft(ctypes.byref(q), ctypes.byref(lay), 128, FAKE, FAKE, FAKE, 64, 0.1, None, FAKE, None) == B.DSA_ERR_INVALID_ARG
+    assert ft(ctypes.byref(q), ctypes.byref(lay), 128, FAKE, FAKE, FAKE, 64, 0.1, FAKE, None, None) == B.DSA_ERR_INVALID_ARG
+    assert ft(ctypes.byref(q), ctypes.byref(lay), 128, FAKE, FAKE, FAKE, 4096, 0.1, FAKE, FAKE, None) == B.DSA_ERR_UNSUPPORTED
+    need = B.dsa_workspace_bytes(B.DSA_OP_INDEXER_KL, 4, 100, 0, 2048)
+    assert need >= 4 * 2048 * (128 * 2 + 4)
+
+    def call(H_I=64, D_I=128, k=2048, ptrs=None, ws=FAKE, nbytes=need, q_=None):
+        p = list(ptrs or (FAKE,) * 11)  # q8, qs, w, k8, ks, idx, target, loss, dq, dw, dk
+        return fk(ctypes.byref(q_ or q), ctypes.byref(lay), H_I, D_I, p[0], p[1], p[2], p[3], p[4], p[5], k, p[6],
+                  p[7], p[8], p[9], p[10], ws, nbytes, None)
+
+    assert call(H_I=4) == B.DSA_ERR_UNSUPPORTED      # the KL kernel is built for 64 x 128
+    assert call(D_I=64) == B.DSA_ERR_UNSUPPORTED
+    assert call(k=0) == B.DSA_ERR_INVALID_ARG
+    assert call(k=4096) == B.DSA_ERR_UNSUPPORTED
+    for i in range(5, 11):
+        ptrs = [FAKE] * 11
+        ptrs[i] = None
+        assert call(ptrs=ptrs) == B.DSA_ERR_INVALID_ARG, i
+    assert call(ws=None) == B.DSA_ERR_WORKSPACE
+    assert call(nbytes=need - 1) == B.DSA_ERR_WORKSPACE
+    assert call(q_=_q(T=0, seq=None, pos=None), ptrs=[None] * 11, ws=None, nbytes=0) == B.DSA_OK

@@ -91,3 +91,46 @@ def test_planted_mistakes_fail_and_roundings_pass():
     rdq, rdkv = _variant(x, cfg, idx, dO)
     np.testing.assert_allclose(rdq, dq, rtol=1e-12, atol=1e-15)
     np.testing.assert_allclose(rdkv, dkv, rtol=1e-12, atol=1e-15)
+
+
+def test_kl_check_catches_planted_mistakes():
+    """The KL gradients' check (2^-7 of the term magnitudes, Frobenius 1e-2)
+    fails on plausible mistakes planted in the oracle's result."""
+    from parity_util import kl_magnitudes
+    g = np.random.default_rng(9)
+    T, H_I, D_I, L, k = 3, 64, 128, 200, 40
+    codes = np.array([0x00, 0x38, 0x40, 0x44, 0x48, 0xB8, 0xC0, 0xC4, 0xC8], dtype=np.uint8)
+    q8 = codes[g.integers(0, 9, size=(T, H_I, D_I))]
+    k8 = codes[g.integers(0, 9, size=(1, L, D_I))]
+    qs = np.full(T, 0.125)
+    ks = 0.0625 + 0.0625 * g.uniform(size=(1, L))
+    w = g.uniform(size=(T, H_I))
+    idx = np.stack([g.choice(L, k, replace=False) for _ in range(T)])
+    seq_id = np.zeros(T, int)
+    tgt = g.uniform(size=(T, k))
+    tgt /= tgt.sum(axis=1, keepdims=True)
+    loss, dI, dq, dw, dk = O.indexer_kl(q8, qs, w, k8, ks, idx, seq_id, tgt)
+    m_dq, m_dk, _ = kl_magnitudes(q8, qs, w, k8, ks, idx, seq_id, dI)
+    check_bwd(dq, dq, m_dq)
+    check_bwd(dk, dk, m_dk)
+
+    def fails(fn):
+        try:
+            fn()
+        except AssertionError:
+            return True
+        return False
+
+    # dq without the head weight; dI with the wrong sign
+    assert fails(lambda: check_bwd(dq / w[:, :, None], dq, m_dq))
+    assert fails(lambda: check_bwd(-dq, dq, m_dq))
+    # dk without the query scale
+    assert fails(lambda: check_bwd(dk / 0.125, dk, m_dk))
+    # the ReLU's derivative dropped (every head counts), recomputed from the definition
+    qd = O.decode_e4m3fn(q8) * qs[:, None, None]
+    bad = np.zeros_like(dk)
+    for t in range(T):
+        gk = dI[t][:, None] * (np.ones((H_I, k)) * w[t][:, None]).T @ qd[t]
+        for j, s in enumerate(idx[t]):
+            bad[0, s] += gk[j]
+    assert fails(lambda: check_bwd(bad, dk, m_dk))
