@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--config", default="decode128k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--kl", action="store_true",
+                    help="with --config train64k_chunk4k: time the indexer's KL training signal instead of the "
+                         "attention backward")
     ap.add_argument("--crossover", action="store_true",
                     help="time the masked dense attention against the sparse gather over context lengths")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -338,6 +341,87 @@ def bench_backward(args, cfg):
     print(json.dumps(out), flush=True)
 
 
+def bench_kl(args, cfg):
+    """The indexer's KL training signal on the training chunk: the target
+    (head-mean attention probabilities of each query's top-2048, from the
+    forward's lse) and the KL loss with its gradients into the indexer query,
+    key and head weights.  A step zeroes dk and runs dsa_indexer_kl_target and
+    dsa_indexer_kl.  The target kernel, the larger part, gathers every
+    selected latent row (1152 B) per query, as the forward attention does, and
+    scores it for all heads: it is bound by that gather, so its roofline is
+    HBM bandwidth."""
+    import torch
+    from sparse_attention_long_03_amd import binding as B
+    from sparse_attention_long_03_amd import inputs as I
+    from sparse_attention_long_03_amd.path import DSAPath
+
+    x = I.make_inputs(cfg, "cuda")
+    p = DSAPath(x)
+    _, lse, idx = p.forward()
+    k = cfg.k
+    target = p.kl_target(idx)
+    loss, dq, dw, dk = p.indexer_kl(idx, target)
+    stream = torch.cuda.current_stream()
+    ws = p._ws[("kl", B.dsa_workspace_bytes(B.DSA_OP_INDEXER_KL, x.T, x.max_len, 0, k))]
+    tgt_call = lambda: B.dsa_indexer_kl_target(p.q, p.layout, cfg.H, x.q, x.kv, idx, k, cfg.scale, lse, target)
+    kl_call = lambda: B.dsa_indexer_kl(p.q, p.layout, cfg.H_I, cfg.D_I, x.iq8, x.iqs, x.iw, x.ik8, x.iks, idx, k,
+                                       target, loss, dq, dw, dk, ws)
+
+    def step():
+        dk.zero_()
+        tgt_call()
+        kl_call()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    n_launch = max(args.steps, 5)
+    timed_rotation([tgt_call, kl_call], 2, stream)
+    tgt_avg = mean(timed_rotation([tgt_call], n_launch, stream))
+    kl_avg = mean(timed_rotation([kl_call], n_launch, stream))
+
+    sel = sum(min(int(q) + 1, k) for q in x.pos.tolist())
+    tgt_flops = 2 * sel * cfg.H * cfg.D                       # scores of every head over the selected rows
+    # per selected entry: its latent row, its index, its target value written;
+    # per query: q (H x 576 bf16) and lse
+    tgt_bytes = sel * (cfg.D * 2 + 4 + 4) + x.T * cfg.H * (cfg.D * 2 + 4)
+    # per selected entry: the indexer scores twice (64 heads x 128), and the
+    # dq and dk contractions (64 x 128 each)
+    kl_flops = 2 * sel * cfg.H_I * cfg.D_I * 4
+    tgt_tf = tgt_flops / (tgt_avg * 1e-3) / 1e12
+    tgt_gbs = tgt_bytes / (tgt_avg * 1e-3) / 1e9
+    out = {
+        "metric": "indexer KL training signal query tokens/s @64K ctx, k=2048",
+        "value": round(x.T / (wall_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 attention scores / fp8-e4m3 indexer, fp32 accumulate; bf16 masked products",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: KL target and indexer loss/gradients for {x.T} query tokens at positions "
+                               f"{cfg.L - x.T}..{cfg.L - 1} of one {cfg.L}-token sequence, top-{k} selection each, "
+                               f"{cfg.H} attention heads, indexer {cfg.H_I}x{cfg.D_I}", "L": cfg.L, "T": x.T, "k": k,
+                   "H": cfg.H, "H_I": cfg.H_I, "D_I": cfg.D_I},
+        "roofline": {"bound": "hbm", "kernel": "kl_target_kernel", "achieved": round(tgt_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(tgt_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": tgt_bytes, "avg_launch_us": round(tgt_avg * 1e3, 1)},
+        "kernels": {"target_ms": round(tgt_avg, 3), "target_tflops": round(tgt_tf, 1),
+                    "target_frac_bf16": round(tgt_tf / BF16_PEAK_TFLOPS, 4), "kl_ms": round(kl_avg, 3),
+                    "kl_tflops": round(kl_flops / (kl_avg * 1e-3) / 1e12, 1)},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def bench_crossover(args):
     """Sparse gather vs masked dense attention on the same top-2048 selection,
     prefill (every token a query) and 16-sequence decode, L = 1K .. 16K: the
@@ -393,7 +477,10 @@ def main():
         bench_prefill(args, cfg)
         return
     if cfg.name == "train64k_chunk4k":
-        bench_backward(args, cfg)
+        if args.kl:
+            bench_kl(args, cfg)
+        else:
+            bench_backward(args, cfg)
         return
     x0 = I.make_inputs(cfg, "cuda")
     xs = replicas(x0, REPLICAS)
