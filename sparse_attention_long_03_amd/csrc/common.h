@@ -41,14 +41,18 @@ __device__ __forceinline__ u32 order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Wave-wide inclusive prefix sum of a u32 (64 lanes).
+// Wave-wide inclusive prefix sum of a u32 (64 lanes), on DPP: four row
+// shifts give the sums within each row of 16 lanes, then row_bcast:15 adds row
+// r-1's total to rows 1 and 3 and row_bcast:31 adds the first two rows' total
+// to rows 2 and 3.  Lanes whose DPP source lies outside the row, or whose row
+// is masked off, read 0.
 __device__ __forceinline__ u32 wave_incl_scan(u32 v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    u32 o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
+  v += (u32)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += (u32)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += (u32)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += (u32)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += (u32)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  v += (u32)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
   return v;
 }
 

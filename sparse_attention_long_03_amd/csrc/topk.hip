@@ -167,6 +167,55 @@ __global__ __launch_bounds__(TK_CHUNK_NT) void topk_chunk_kernel(const float* __
   }
 }
 
+// The exact selection among C threshold-bin candidates (their key bits
+// 20..0 and positions, in position order, read through cand_key / cand_pos):
+// the need1-th largest key via two more histogram rounds (bits 20..10, then
+// 9..0), then one ordered sweep that writes to out the candidates above it
+// and the first ties at it, in position order.  `hist` holds TK_BINS words of
+// LDS; every thread of the block takes part.
+template <int NT, class KeyF, class PosF>
+__device__ __forceinline__ void select_candidates(u32 C, u32 need1, int32_t* __restrict__ out, KeyF cand_key,
+                                                  PosF cand_pos, u32* hist, u32* scratch, u32* sh_bin,
+                                                  u32* sh_above) {
+  const int tid = threadIdx.x;
+  for (u32 j = tid; j < C; j += NT) atomicAdd(&hist[cand_key(j) >> 10], 1u);
+  __syncthreads();
+  find_threshold<TK_BINS, NT>(hist, need1, scratch, sh_bin, sh_above);
+  const u32 b2 = *sh_bin;
+  const u32 need2 = need1 - *sh_above;
+  __syncthreads();
+  for (int i = tid; i < 1024; i += NT) hist[i] = 0;
+  __syncthreads();
+  for (u32 j = tid; j < C; j += NT) {
+    const u32 key = cand_key(j);
+    if ((key >> 10) == b2) atomicAdd(&hist[key & 0x3FFu], 1u);
+  }
+  __syncthreads();
+  find_threshold<1024, NT>(hist, need2, scratch, sh_bin, sh_above);
+  const u32 low = (b2 << 10) | *sh_bin;  // bits 20..0 of the k-th key
+  const u32 ties = need2 - *sh_above;    // keys equal to it that are kept (>= 1)
+
+  // ordered sweep of the candidates (their order = position order)
+  u32 gt_base = 0, eq_base = 0;
+  for (u32 j0 = 0; j0 < C; j0 += NT) {
+    const u32 j = j0 + tid;
+    const bool ok = j < C;
+    const u32 key = ok ? cand_key(j) : 0u;
+    const u32 gt = (ok && key > low) ? 1u : 0u;
+    const u32 eq = (ok && key == low) ? 1u : 0u;
+    const u32 packed = (eq << 16) | gt;
+    u32 bt;
+    const u32 bincl = block_incl_scan<NT>(packed, scratch, &bt);
+    const u32 excl = bincl - packed;
+    const u32 gt_before = gt_base + (excl & 0xFFFFu);
+    const u32 eq_before = eq_base + (excl >> 16);
+    if (gt) out[gt_before + min(eq_before, ties)] = cand_pos(j);
+    else if (eq && eq_before < ties) out[gt_before + eq_before] = cand_pos(j);
+    gt_base += bt & 0xFFFFu;
+    eq_base += bt >> 16;
+  }
+}
+
 // Largest c in [0, n) with off[c] <= j (off ascending, off[0] = 0).
 __device__ __forceinline__ int chunk_of(const u32* off, int n, u32 j) {
   int lo = 0, hi = n - 1;
@@ -256,43 +305,7 @@ __global__ __launch_bounds__(TK_RES_NT) void topk_resolve_kernel(const int32_t* 
     return cpos[(slot0 + c) * TK_CH + (j - s_coff[c])];
   };
 
-  // ---- exact k-th key among the candidates: bits 20..10, then 9..0
-  for (u32 j = tid; j < C; j += NT) atomicAdd(&hist[cand_key(j) >> 10], 1u);
-  __syncthreads();
-  find_threshold<TK_BINS, NT>(hist, need1, scratch, &sh_bin, &sh_above);
-  const u32 b2 = sh_bin;
-  const u32 need2 = need1 - sh_above;
-  __syncthreads();
-  for (int i = tid; i < 1024; i += NT) hist[i] = 0;
-  __syncthreads();
-  for (u32 j = tid; j < C; j += NT) {
-    const u32 key = cand_key(j);
-    if ((key >> 10) == b2) atomicAdd(&hist[key & 0x3FFu], 1u);
-  }
-  __syncthreads();
-  find_threshold<1024, NT>(hist, need2, scratch, &sh_bin, &sh_above);
-  const u32 low = (b2 << 10) | sh_bin;  // bits 20..0 of the k-th key
-  const u32 ties = need2 - sh_above;    // keys equal to it that are kept (>= 1)
-
-  // ---- ordered sweep of the candidates (flattened order = position order)
-  u32 gt_base = 0, eq_base = 0;
-  for (u32 j0 = 0; j0 < C; j0 += NT) {
-    const u32 j = j0 + tid;
-    const bool ok = j < C;
-    const u32 key = ok ? cand_key(j) : 0u;
-    const u32 gt = (ok && key > low) ? 1u : 0u;
-    const u32 eq = (ok && key == low) ? 1u : 0u;
-    const u32 packed = (eq << 16) | gt;
-    u32 bt;
-    const u32 bincl = block_incl_scan<NT>(packed, scratch, &bt);
-    const u32 excl = bincl - packed;
-    const u32 gt_before = gt_base + (excl & 0xFFFFu);
-    const u32 eq_before = eq_base + (excl >> 16);
-    if (gt) out[A + gt_before + min(eq_before, ties)] = cand_pos(j);
-    else if (eq && eq_before < ties) out[A + gt_before + eq_before] = cand_pos(j);
-    gt_base += bt & 0xFFFFu;
-    eq_base += bt >> 16;
-  }
+  select_candidates<NT>(C, need1, out + A, cand_key, cand_pos, hist, scratch, &sh_bin, &sh_above);
 }
 
 static int topk_nch(int64_t ld) { return (int)((ld + TK_CH - 1) / TK_CH); }

@@ -286,3 +286,11 @@ def test_full_size_decode32k_sampled():
 def test_full_size_ragged_paged_sampled():
     T = int(I._workload(I.CONFIGS["ragged_paged"])[2].shape[0])
     _sampled_full_size("ragged_paged", [0, T // 2, T - 1])
+
+
+def test_topk_threshold_bin_larger_than_lds():
+    """Logits on 4 levels: the threshold bin holds most of a 128K row, more
+    candidates than the resolve step stages in LDS (they are read from the
+    workspace instead)."""
+    w = np.floor(I.tie_heavy_logits(2, 131072, seed=22).numpy() / 64.0).astype(np.float32)
+    _topk_case(w, [131072, 100000], 2048)
