@@ -43,9 +43,9 @@ REPLICAS = 4
 # device copy in the same pass.  Valid only for the kernel sources they were
 # taken on (hash below); otherwise the field is reported as null.
 TRAFFIC = {
-    "sources_sha256": "65da00adf116d9c766483f6dd491ea606e1950eed4c0c7681bdd2a4199e83623",
-    # FETCH_SIZE 135759.4 KiB/launch x 1.99982 (copy: 131084.0 KiB counted for 262144 KiB read)
-    "fetch_bytes": 278009696,
+    "sources_sha256": "f290bba4c203d278fa17ef80bbda93b3b315d80dcda849e67ffd030e113fe626",
+    # FETCH_SIZE 135758.7 KiB/launch x 1.99982 (copy: 131083.9 KiB counted for 262144 KiB read)
+    "fetch_bytes": 278008591,
     # WRITE_SIZE 8192.0 KiB/launch x 1.0 (copy: 262144 KiB counted for 262144 KiB written)
     "write_bytes": 8388608,
 }
