@@ -20,6 +20,7 @@ constexpr int AT_MAX_SPLIT = 2048;                  // rows per split (k <= 2048
 constexpr u32 ROW_INVALID = 0x80000000u;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
 // s_waitcnt immediates (gfx9 encoding): at most N vector-memory loads of
@@ -73,18 +74,36 @@ struct TileStage {
 // order with the padding entries (-1) dropped: s_row[c] for c < nvalid, then
 // the tail of the last tile filled with a valid row of the sequence flagged
 // ROW_INVALID; s_valid[it] has bit j set when row j of tile it is selected.
-// Returns nvalid.  `scan_scratch` holds NT/64 + 1 words; the caller issues a
-// barrier before reading s_row / s_valid.
-template <int NT>
+// Returns nvalid.  `scan_scratch` holds NT/64 words; the caller issues a
+// barrier before reading s_row / s_valid.  `after_first_load` runs once the
+// first chunk of sel is requested, so the caller can put its own loads in
+// flight beside it: the scan's barriers wait for LDS traffic only, so those
+// loads stay outstanding through it.
+template <int NT, class F>
 __device__ __forceinline__ int compact_selection(const int32_t* __restrict__ sel, int n, const Layout& lay, int b,
-                                                 u32* s_row, u32* s_valid, u32* scan_scratch, int tid) {
+                                                 u32* s_row, u32* s_valid, u32* scan_scratch, int tid,
+                                                 F&& after_first_load) {
+  constexpr int NW = NT / 64;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  int s_next = (tid < n) ? sel[tid] : -1;
+  after_first_load();
   int nvalid = 0;
   for (int i0 = 0; i0 < n; i0 += NT) {
-    const int i = i0 + tid;
-    const int s = (i < n) ? sel[i] : -1;
-    u32 tot;
-    const u32 incl = block_incl_scan<NT>(s >= 0 ? 1u : 0u, scan_scratch, &tot);
-    if (s >= 0) s_row[nvalid + (int)incl - 1] = (u32)token_row(lay, b, s);
+    const int s = s_next;
+    if (i0 + NT < n) s_next = (i0 + NT + tid < n) ? sel[i0 + NT + tid] : -1;
+    const u32 incl = wave_incl_scan(s >= 0 ? 1u : 0u);
+    if (lane == 63) scan_scratch[wid] = incl;
+    lds_barrier();
+    u32 off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const u32 c = scan_scratch[w];
+      off += (w < wid) ? c : 0u;
+      tot += c;
+    }
+    lds_barrier();  // scan_scratch is rewritten by the next chunk
+    if (s >= 0) s_row[nvalid + (int)(off + incl) - 1] = (u32)token_row(lay, b, s);
     nvalid += (int)tot;
   }
   const int ntiles = (nvalid + AT_TILE - 1) / AT_TILE;

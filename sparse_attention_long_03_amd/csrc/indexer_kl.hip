@@ -19,7 +19,6 @@
 
 namespace dsa {
 
-typedef float v2f __attribute__((ext_vector_type(2)));
 
 namespace {
 constexpr u32 SLOT_NONE = 0xFFFFFFFFu;

@@ -38,6 +38,17 @@ namespace dsa {
 // normalisation divides by l accumulated against the same reference.
 constexpr float RESCALE_SLACK = 8.f;
 
+// Maximum over the four lanes n, n+16, n+32, n+48 (one head's lane groups).
+// The row swaps of gfx950 run on the VALU: a ds_bpermute shuffle counts on
+// the LDS counter, and waiting for it also waits for every LDS read issued
+// before it.
+__device__ __forceinline__ float max_over_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Scores, online softmax and value product for one tile held in `buf`.
 // `valid` has bit j set when row j of the tile is a selected row.
 __device__ __forceinline__ void attend_tile(const LDS_AS uint8_t* __restrict__ buf, u32 valid, const v8bf* qf,
@@ -82,8 +93,7 @@ __device__ __forceinline__ void attend_tile(const LDS_AS uint8_t* __restrict__ b
   float mx = z[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  mx = max_over_groups(mx);
   // move the reference only when this tile would exceed the slack
   if (__builtin_amdgcn_ballot_w64(mx > m_ref + RESCALE_SLACK) != 0) {
     const float m_new = (mx > m_ref + RESCALE_SLACK) ? mx : m_ref;
@@ -164,6 +174,16 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(const uint16_t* __r
   const int nrows = max(0, j_end - j_begin);
   int ntiles = (nrows + AT_TILE - 1) / AT_TILE;
 
+  // Q^T operand: head h0+n, dims 32*ks + 8g .. +8 (waves past H read head 0
+  // and discard their results: uniform control flow keeps O in registers);
+  // requested beside the first selection load
+  v8bf qf[AT_D / 32];
+  auto load_q = [&] {
+    const uint16_t* qrow = q + ((int64_t)t * H + (has_heads ? h0 : 0) + n) * AT_D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < AT_D / 32; ++ks) qf[ks] = *reinterpret_cast<const v8bf*>(qrow + 32 * ks);
+  };
+
   // physical rows of this split (padding and the ragged tail load a valid
   // row of the sequence and are masked), and one validity bit per row
   const int64_t safe_row = token_row(lay, b, 0);
@@ -171,9 +191,11 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(const uint16_t* __r
     // selected positions, compacted in order (padding entries -1 dropped:
     // rows shorter than k carry many), then the tail of the last tile masked
     __shared__ u32 scan_scratch[NT / 64 + 1];
-    const int nvalid = compact_selection<NT>(idx_row + j_begin, nrows, lay, b, s_row, s_valid, scan_scratch, tid);
+    const int nvalid =
+        compact_selection<NT>(idx_row + j_begin, nrows, lay, b, s_row, s_valid, scan_scratch, tid, load_q);
     ntiles = (nvalid + AT_TILE - 1) / AT_TILE;
   } else {
+    load_q();
     for (int i = tid; i < ntiles * AT_TILE; i += NT)
       s_row[i] = (i < nrows) ? (u32)token_row(lay, b, j_begin + i) : ((u32)safe_row | ROW_INVALID);
     for (int i = tid; i < AT_MAX_SPLIT / AT_TILE; i += NT) s_valid[i] = 0;
@@ -184,14 +206,6 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(const uint16_t* __r
     }
   }
 
-  // Q^T operand: head h0+n, dims 32*ks + 8g .. +8 (waves past H read head 0
-  // and discard their results: uniform control flow keeps O in registers)
-  v8bf qf[AT_D / 32];
-  {
-    const uint16_t* qrow = q + ((int64_t)t * H + (has_heads ? h0 : 0) + n) * AT_D + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < AT_D / 32; ++ks) qf[ks] = *reinterpret_cast<const v8bf*>(qrow + 32 * ks);
-  }
   float m_ref = -INFINITY;  // reference max (log2 units) of head h0+n
   float l_part = 0.f;       // partial sum over this lane's keys
   v4f o[AT_DV / 16];
@@ -199,7 +213,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(const uint16_t* __r
   for (int mt = 0; mt < AT_DV / 16; ++mt) o[mt] = v4f{0.f, 0.f, 0.f, 0.f};
 
   LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
-  __syncthreads();  // s_row / s_valid visible
+  lds_barrier();  // s_row / s_valid visible; the Q loads stay in flight
   // Two tiles in flight: while a tile is computed from one LDS buffer, the
   // next two load into two register stages (A: odd distance, B: even), so the
   // loop runs over pairs of tiles.  Every path issues the same loads -- tiles
@@ -246,16 +260,23 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(const uint16_t* __r
       lse[(int64_t)t * H + h] = (l > 0.f) ? (m_ref + log2f(l)) * 0.69314718055994531f : -INFINITY;
   } else {
     // split partial: O normalised by its own l, as bf16 (a convex combination
-    // of value rows, so bf16 keeps the range), plus (reference max, l)
+    // of value rows, so bf16 keeps the range), plus (reference max, l).  The
+    // wave's 16 heads x 512 dims are stored in fragment order, [mt/2][lane][8]
+    // (tiles mt and mt+1 of a lane side by side), so each store instruction
+    // writes 1 KB contiguous.
     const int64_t slot_o = ((int64_t)t * n_splits + split) * H + h;
     const float inv = (l > 0.f) ? 1.f / l : 0.f;
-    uint16_t* orow = ws_o + slot_o * AT_DV + 4 * g;
+    uint16_t* orow = ws_o + (slot_o - n) * AT_DV + 8 * lane;
 #pragma unroll
-    for (int mt = 0; mt < AT_DV / 16; ++mt) {
-      v2i pk;
-      pk[0] = (int)((u32)f2bf(o[mt][0] * inv) | ((u32)f2bf(o[mt][1] * inv) << 16));
-      pk[1] = (int)((u32)f2bf(o[mt][2] * inv) | ((u32)f2bf(o[mt][3] * inv) << 16));
-      *reinterpret_cast<v2i*>(orow + 16 * mt) = pk;
+    for (int mp = 0; mp < AT_DV / 32; ++mp) {
+      v4i pk;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const v4f& a = o[2 * mp + i];
+        pk[2 * i] = (int)((u32)f2bf(a[0] * inv) | ((u32)f2bf(a[1] * inv) << 16));
+        pk[2 * i + 1] = (int)((u32)f2bf(a[2] * inv) | ((u32)f2bf(a[3] * inv) << 16));
+      }
+      *reinterpret_cast<v4i*>(orow + 512 * mp) = pk;
     }
     if (g == 0) {
       ws_ml[slot_o * 2 + 0] = m_ref;
@@ -266,58 +287,78 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(const uint16_t* __r
 
 // Merge the splits: with o_s the normalised partial of split s,
 //   O = sum_s w_s o_s / sum_s w_s,   w_s = 2^(m_s - M) l_s,   M = max_s m_s.
-// One wave per (token, head); lane s < n_splits reads split s's (m, l), the
-// weights come out of two wave reductions, and every lane then loads its 8
-// value dims of all splits at once (independent loads, one round trip).
+// The partials are in the attention kernel's fragment order (per 16 heads:
+// [mt/2][lane][8], lane = n + 16g holding head n, dims 16mt + 4g..+3 of tiles
+// mt and mt+1), so a wave takes one token, one group of 16 heads and one pair
+// of dim tiles with the same lane mapping: each load instruction reads 1 KB
+// contiguous of a split.  Each lane derives the split weights of its head.
 constexpr int AT_MAX_SPLITS = 8;
 
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ ws_o,
-                                                      const float* __restrict__ ws_ml, int TH, int H, int n_splits,
+                                                      const float* __restrict__ ws_ml, int T, int H, int n_splits,
                                                       uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int PAIRS = AT_DV / 32;
+  const int n_hg = H / 16;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= TH) return;
+  if (item >= T * n_hg * PAIRS) return;
   const int lane = threadIdx.x & 63;
-  const int t = item / H;
-  const int h = item - t * H;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int mp = item % PAIRS;
+  const int th = item / PAIRS;
+  const int t = th / n_hg;
+  const int h = (th - t * n_hg) * 16 + n;
   const int64_t slot0 = (int64_t)t * n_splits * H + h;  // split s: slot0 + s*H
-  float m = -INFINITY, ls = 0.f;
-  if (lane < n_splits) {
-    m = ws_ml[(slot0 + (int64_t)lane * H) * 2];
-    ls = ws_ml[(slot0 + (int64_t)lane * H) * 2 + 1];
-  }
-  float M = (ls > 0.f) ? m : -INFINITY;
-#pragma unroll
-  for (int d = 1; d < AT_MAX_SPLITS; d <<= 1) M = fmaxf(M, __shfl_xor(M, d, 64));
-  const float wgt = (ls > 0.f) ? exp2f(m - M) * ls : 0.f;
-  float L = wgt;
-#pragma unroll
-  for (int d = 1; d < AT_MAX_SPLITS; d <<= 1) L += __shfl_xor(L, d, 64);
-  // the reductions above ran within groups of 8 lanes: take lane 0's
-  L = __shfl(L, 0, 64);
-  M = __shfl(M, 0, 64);
 
+  // the splits' partials, requested first so they overlap the weights below
+  const uint16_t* src = ws_o + (slot0 - n) * AT_DV + 8 * lane + 512 * mp;
+  const int64_t split_stride = (int64_t)H * AT_DV;
   v4i x[AT_MAX_SPLITS];
 #pragma unroll
-  for (int s = 0; s < AT_MAX_SPLITS; ++s)
-    if (s < n_splits) x[s] = *reinterpret_cast<const v4i*>(ws_o + (slot0 + (int64_t)s * H) * AT_DV + 8 * lane);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < AT_MAX_SPLITS; ++sp)
+    x[sp] = (sp < n_splits) ? *reinterpret_cast<const v4i*>(src + sp * split_stride) : v4i{0, 0, 0, 0};
+
+  // (reference max, l) of every split of head h; M over the non-empty ones
+  float ms[AT_MAX_SPLITS], ls[AT_MAX_SPLITS];
+  float M = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < AT_MAX_SPLITS; ++s) {
-    if (s >= n_splits) break;
-    const float ws = __shfl(wgt, s, 64);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += ws * __uint_as_float((u32)x[s][i] << 16);
-      acc[2 * i + 1] += ws * __uint_as_float((u32)x[s][i] & 0xFFFF0000u);
+  for (int sp = 0; sp < AT_MAX_SPLITS; ++sp) {
+    ms[sp] = -INFINITY;
+    ls[sp] = 0.f;
+    if (sp < n_splits) {
+      const v2f ml = *reinterpret_cast<const v2f*>(ws_ml + (slot0 + (int64_t)sp * H) * 2);
+      ms[sp] = ml[0];
+      ls[sp] = ml[1];
     }
+    if (ls[sp] > 0.f) M = fmaxf(M, ms[sp]);
+  }
+  float wgt[AT_MAX_SPLITS];
+  float L = 0.f;
+#pragma unroll
+  for (int sp = 0; sp < AT_MAX_SPLITS; ++sp) {
+    wgt[sp] = (ls[sp] > 0.f) ? exp2f(ms[sp] - M) * ls[sp] : 0.f;
+    L += wgt[sp];
   }
   const float inv = (L > 0.f) ? 1.f / L : 0.f;
-  v4i pk;
+
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    pk[i] = (int)((u32)f2bf(acc[2 * i] * inv) | ((u32)f2bf(acc[2 * i + 1] * inv) << 16));
-  *reinterpret_cast<v4i*>(out + ((int64_t)t * H + h) * AT_DV + 8 * lane) = pk;
-  if (lse != nullptr && lane == 0)
+  for (int sp = 0; sp < AT_MAX_SPLITS; ++sp) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += wgt[sp] * __uint_as_float((u32)x[sp][i] << 16);
+      acc[2 * i + 1] += wgt[sp] * __uint_as_float((u32)x[sp][i] & 0xFFFF0000u);
+    }
+  }
+  uint16_t* orow = out + ((int64_t)t * H + h) * AT_DV + 4 * g + 32 * mp;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    v2i pk;
+    pk[0] = (int)((u32)f2bf(acc[4 * i] * inv) | ((u32)f2bf(acc[4 * i + 1] * inv) << 16));
+    pk[1] = (int)((u32)f2bf(acc[4 * i + 2] * inv) | ((u32)f2bf(acc[4 * i + 3] * inv) << 16));
+    *reinterpret_cast<v2i*>(orow + 16 * i) = pk;
+  }
+  if (lse != nullptr && mp == 0 && g == 0)
     lse[(int64_t)t * H + h] = (L > 0.f) ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
@@ -387,8 +428,9 @@ static hipError_t launch_attn_t(int T, int H, const uint16_t* q, const uint16_t*
                      lay, H, k, split_len, n_splits, scale_log2, out, lse, ws_o, ws_ml, T);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_splits == 1) return e;
-  const int TH = T * H;
-  hipLaunchKernelGGL(combine_kernel, dim3((TH + 3) / 4), dim3(256), 0, stream, ws_o, ws_ml, TH, H, n_splits, out, lse);
+  const int waves = T * (H / 16) * (AT_DV / 32);
+  hipLaunchKernelGGL(combine_kernel, dim3((waves + 3) / 4), dim3(256), 0, stream, ws_o, ws_ml, T, H, n_splits, out,
+                     lse);
   return hipGetLastError();
 }
 

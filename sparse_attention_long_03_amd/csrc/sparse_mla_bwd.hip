@@ -164,7 +164,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_bwd_dq_kernel(
   const bool has_heads = h0 < H;
   const int b = seq_id[t];
 
-  const int nvalid = compact_selection<NT>(idx + (int64_t)t * k, k, lay, b, s_row, s_valid, scan_scratch, tid);
+  const int nvalid = compact_selection<NT>(idx + (int64_t)t * k, k, lay, b, s_row, s_valid, scan_scratch, tid, [] {});
   const int ntiles = (nvalid + AT_TILE - 1) / AT_TILE;
 
   // Q^T and dO^T operands of head h0+n (dims 32ks + 8g..+8), and D = dO . O
