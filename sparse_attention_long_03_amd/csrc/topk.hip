@@ -195,7 +195,40 @@ __device__ __forceinline__ void select_candidates(u32 C, u32 need1, int32_t* __r
   const u32 low = (b2 << 10) | *sh_bin;  // bits 20..0 of the k-th key
   const u32 ties = need2 - *sh_above;    // keys equal to it that are kept (>= 1)
 
-  // ordered sweep of the candidates (their order = position order)
+  // ordered sweep of the candidates (their order = position order).  Up to
+  // 4 per thread, each thread takes a contiguous run, so one block scan
+  // places them all.
+  if (C <= 4u * NT) {
+    const u32 R = (C + NT - 1) / NT;
+    const u32 j0 = (u32)tid * R;
+    u32 key[4];
+    u32 gt = 0, eq = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const u32 j = j0 + r;
+      key[r] = ((u32)r < R && j < C) ? cand_key(j) : 0u;
+      const bool ok = (u32)r < R && j < C;
+      gt += (ok && key[r] > low) ? 1u : 0u;
+      eq += (ok && key[r] == low) ? 1u : 0u;
+    }
+    u32 bt;
+    const u32 packed = (eq << 16) | gt;
+    const u32 excl = block_incl_scan<NT>(packed, scratch, &bt) - packed;
+    u32 gt_before = excl & 0xFFFFu, eq_before = excl >> 16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const u32 j = j0 + r;
+      if ((u32)r >= R || j >= C) continue;
+      if (key[r] > low) {
+        out[gt_before + min(eq_before, ties)] = cand_pos(j);
+        ++gt_before;
+      } else if (key[r] == low) {
+        if (eq_before < ties) out[gt_before + eq_before] = cand_pos(j);
+        ++eq_before;
+      }
+    }
+    return;
+  }
   u32 gt_base = 0, eq_base = 0;
   for (u32 j0 = 0; j0 < C; j0 += NT) {
     const u32 j = j0 + tid;
@@ -224,6 +257,20 @@ __device__ __forceinline__ int chunk_of(const u32* off, int n, u32 j) {
     if (off[mid] <= j) lo = mid; else hi = mid - 1;
   }
   return lo;
+}
+
+// chunk_of for U indices at once: the same fixed sequence of steps for all,
+// so their LDS reads are in flight together.  `top` is the largest power of
+// two below n (0 when n == 1).
+template <int U>
+__device__ __forceinline__ void chunk_of_n(const u32* off, int n, int top, const u32 (&j)[U], int (&lo)[U]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) lo[u] = 0;
+  for (int step = top; step > 0; step >>= 1) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (lo[u] + step < n && off[lo[u] + step] <= j[u]) lo[u] += step;
+  }
 }
 
 __global__ __launch_bounds__(TK_RES_NT) void topk_resolve_kernel(const int32_t* __restrict__ valid_len, int len_add,
@@ -285,11 +332,31 @@ __global__ __launch_bounds__(TK_RES_NT) void topk_resolve_kernel(const int32_t* 
   // ---- candidates: stage (key bits 20..0, position) in LDS when they fit
   const bool staged = C <= TK_RES_STAGE;
   if (staged) {
-    for (u32 j = tid; j < C; j += NT) {
-      const int c = chunk_of(s_coff, nch, j);
-      const int64_t g = (slot0 + c) * TK_CH + (j - s_coff[c]);
-      s_ckey[j] = ckey[g] & 0x1FFFFFu;
-      s_cpos[j] = cpos[g];
+    // four candidates per thread per round: their chunk lookups share one
+    // search, and all eight loads are in flight before any is used
+    const int top = nch > 1 ? 1 << (31 - __builtin_clz((u32)(nch - 1))) : 0;
+    for (u32 j0 = 0; j0 < C; j0 += 4 * NT) {
+      u32 j[4];
+      int c[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) j[u] = j0 + u * NT + tid;
+      chunk_of_n<4>(s_coff, nch, top, j, c);
+      u32 kv[4];
+      int32_t pv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        // past C the lane reads the row's first slot instead (never out of range)
+        const int64_t g = j[u] < C ? (slot0 + c[u]) * TK_CH + (j[u] - s_coff[c[u]]) : slot0 * TK_CH;
+        kv[u] = ckey[g];
+        pv[u] = cpos[g];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (j[u] < C) {
+          s_ckey[j[u]] = kv[u] & 0x1FFFFFu;
+          s_cpos[j[u]] = pv[u];
+        }
+      }
     }
   }
   for (int i = tid; i < TK_BINS; i += NT) hist[i] = 0;
