@@ -43,9 +43,9 @@ REPLICAS = 4
 # device copy in the same pass.  Valid only for the kernel sources they were
 # taken on (hash below); otherwise the field is reported as null.
 TRAFFIC = {
-    "sources_sha256": "f290bba4c203d278fa17ef80bbda93b3b315d80dcda849e67ffd030e113fe626",
-    # FETCH_SIZE 135758.7 KiB/launch x 1.99982 (copy: 131083.9 KiB counted for 262144 KiB read)
-    "fetch_bytes": 278008591,
+    "sources_sha256": "23a62ccf96890fc35f66d0c9ef4d2dfc1b2033d978fca80c3b7bdaae4bd07e6c",
+    # FETCH_SIZE 135767.5 KiB/launch x 1.99982 (copy: 131083.9 KiB counted for 262144 KiB read)
+    "fetch_bytes": 278026607,
     # WRITE_SIZE 8192.0 KiB/launch x 1.0 (copy: 262144 KiB counted for 262144 KiB written)
     "write_bytes": 8388608,
 }
@@ -550,7 +550,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload_name(cfg), "B": cfg.B, "L": cfg.L, "T": x0.T, "k": cfg.k, "H_I": cfg.H_I,
                    "D_I": cfg.D_I, "H": cfg.H, "paged": cfg.paged},
-        "roofline": {"bound": "hbm", "kernel": f"indexer_kernel<{cfg.H_I},{cfg.D_I}>", "achieved": round(idx_gbs, 1),
+        "roofline": {"bound": "hbm", "kernel": f"indexer_kernel<{cfg.H_I},{cfg.D_I},{'false' if cfg.paged else 'true'}>", "achieved": round(idx_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(idx_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_launch": ab["indexer"],
                      "avg_launch_us": round(idx_avg * 1e3, 2), "median_launch_us": round(median(idx_ts) * 1e3, 2)},
