@@ -457,6 +457,30 @@ def bench_crossover(args):
                       "n_gpus": 1, "data": "synthetic", "series": series}), flush=True)
 
 
+def forward_graph_timing(fwd, steps, stream):
+    """The same decode steps launched from HIP graphs: one graph per replica,
+    each holding one dsa_forward, replayed in rotation for exactly `steps`
+    steps between two synchronisations.  Returns microseconds per step."""
+    import torch
+    graphs = []
+    for f in fwd:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            f()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(2 * len(graphs)):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) * 1e6 / steps
+    stream.synchronize()
+    return us
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -519,6 +543,7 @@ def main():
     attn_ts = timed_rotation(attn_fns, n_launch, stream)
     step_ts = timed_rotation(fwd, n_launch, stream)
     idx_avg, topk_avg, attn_avg = mean(idx_ts), mean(topk_ts), mean(attn_ts)
+    graph_us = forward_graph_timing(fwd, args.steps, stream)
     cw_us, cw_gbs = cache_write_timing(xs[1], n_launch, stream)  # on a replica not used below
 
     if args.copy_calibration:
@@ -563,6 +588,7 @@ def main():
             "attn_gbs": round(ab["attn"] / (attn_avg * 1e-3) / 1e9, 1),
             "attn_tflops": round(ab["attn_flops"] / (attn_avg * 1e-3) / 1e12, 2),
             "forward_event_us": round(mean(step_ts) * 1e3, 2),
+            "forward_graph_us": round(graph_us, 2),
             "cache_write_us": cw_us,
             "cache_write_gbs": cw_gbs,
         },
