@@ -457,6 +457,28 @@ def bench_crossover(args):
                       "n_gpus": 1, "data": "synthetic", "series": series}), flush=True)
 
 
+def stream_copy_gbs():
+    """Measured device-to-device copy bandwidth on this GPU: a 1 GiB buffer
+    (four times the 256 MB MALL) copied with torch, read + written bytes over
+    the mean HIP-event time of 5 copies."""
+    import torch
+    n = 1 << 28  # int32 elements: 1 GiB
+    src = torch.ones(n, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+    for a, b in ev:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    ms = mean([a.elapsed_time(b) for a, b in ev])
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * 4 * n / (ms * 1e-3) / 1e9
+
+
 def forward_graph_timing(fwd, steps, stream):
     """The same decode steps launched from HIP graphs: one graph per replica,
     each holding one dsa_forward, replayed in rotation for exactly `steps`
@@ -544,6 +566,7 @@ def main():
     step_ts = timed_rotation(fwd, n_launch, stream)
     idx_avg, topk_avg, attn_avg = mean(idx_ts), mean(topk_ts), mean(attn_ts)
     graph_us = forward_graph_timing(fwd, args.steps, stream)
+    copy_gbs = stream_copy_gbs()
     cw_us, cw_gbs = cache_write_timing(xs[1], n_launch, stream)  # on a replica not used below
 
     if args.copy_calibration:
@@ -577,7 +600,8 @@ def main():
                    "D_I": cfg.D_I, "H": cfg.H, "paged": cfg.paged},
         "roofline": {"bound": "hbm", "kernel": f"indexer_kernel<{cfg.H_I},{cfg.D_I},{'false' if cfg.paged else 'true'}>", "achieved": round(idx_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(idx_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "bytes_per_launch": ab["indexer"],
+                     "traffic": traffic, "stream_copy_gbs": round(copy_gbs, 1),
+                     "frac_of_stream_copy": round(idx_gbs / copy_gbs, 4), "bytes_per_launch": ab["indexer"],
                      "avg_launch_us": round(idx_avg * 1e3, 2), "median_launch_us": round(median(idx_ts) * 1e3, 2)},
         "kernels": {
             "indexer_us": round(idx_avg * 1e3, 2),
