@@ -26,6 +26,8 @@ SMALL = {
     "idx4x128": I.scaled(I.CONFIGS["decode32k"], B=2, L=3000, H_I=4, H=32, k=512),
     # paged, lengths in [100, 3000], shuffled pages, 1-2 queries per sequence
     "paged_small": I.scaled(I.CONFIGS["ragged_paged"], B=5, L=3000, min_len=100, H=64, k=1024),
+    # paged with the 4x64 indexer (the other key width of the indexer's staging)
+    "paged_4x64": I.scaled(I.CONFIGS["ragged_paged"], B=4, L=2000, min_len=100, H_I=4, D_I=64, H=16, k=256),
 }
 
 
