@@ -156,7 +156,7 @@ int dsa_topk(const float* logits, int64_t ld_logits, const int32_t* valid_len, i
  *               positions ascending, then -1)
  *   workspace : device, 256-byte aligned; it holds a candidate list of `cap`
  *               slots (8 bytes each) per query token, with cap = the largest
- *               multiple of 64 not above 8192 that fits workspace_bytes / T;
+ *               multiple of 64 not above 12288 that fits workspace_bytes / T;
  *               cap >= k + 320 is required (DSA_ERR_WORKSPACE otherwise).
  *               A smaller cap gives the same result with more work;
  *               dsa_workspace_bytes(DSA_OP_INDEXER_TOPK, T, max_len, 0, k) is

@@ -38,7 +38,7 @@ constexpr int FT_QPW = 2;                 // query tokens per wave
 constexpr int FT_QB = FT_WAVES * FT_QPW;  // query tokens per workgroup
 constexpr int FT_TILE = 64;               // keys per tile
 constexpr int FT_AHEAD = 4;               // key tiles in flight (register stages)
-constexpr int FT_CAP_MAX = 8192;          // candidate slots per token
+constexpr int FT_CAP_MAX = 12288;         // candidate slots per token
 constexpr int FT_BINS = 2048;
 
 // Memory fence for one wave's own LDS and global traffic: waits until this

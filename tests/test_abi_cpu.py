@@ -150,7 +150,7 @@ def test_fused_indexer_topk_validation(lib):
     pref = B.dsa_workspace_bytes(B.DSA_OP_INDEXER_TOPK, 16, 100, 0, 256)
     assert pref == 8 * 16 * (256 + 320)
     assert B.dsa_workspace_bytes(B.DSA_OP_INDEXER_TOPK, 16, 5000, 0, 256) == 8 * 16 * (5056 + 256)
-    assert B.dsa_workspace_bytes(B.DSA_OP_INDEXER_TOPK, 16, 1 << 20, 0, 2048) == 8 * 16 * 8192
+    assert B.dsa_workspace_bytes(B.DSA_OP_INDEXER_TOPK, 16, 1 << 20, 0, 2048) == 8 * 16 * 12288
 
 
 def test_forward_workspace_switches_to_fused_selection(lib):
