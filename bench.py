@@ -522,8 +522,8 @@ def forward_graph_timing(fwd, steps, stream):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (multi-GPU sharding is a design "
-                                   "note only)"}))
+        print(json.dumps({"error": "the DSA path runs on one GPU: --gpus must be 1 (how it would shard over several "
+                                   "GPUs is described, not implemented)"}))
         sys.exit(2)
     import torch
     from sparse_attention_long_03_amd import binding as B
