@@ -57,7 +57,11 @@ _E4M3FN_TABLE = np.array([_e4m3fn_value(c) for c in range(256)], dtype=np.float6
 
 
 def decode_e4m3fn(codes) -> np.ndarray:
-    """Decode an array of e4m3fn byte codes (uint8) to float64, exactly."""
+    """Decode an array of e4m3fn byte codes (uint8) to float64, exactly.
+
+    [DSA-article] (1): the indexer computes in FP8, read here as the OCP E4M3
+    ("e4m3fn") format of gfx950 (see _e4m3fn_value).
+    """
     c = np.asarray(codes)
     if c.dtype != np.uint8:
         raise TypeError("e4m3fn codes must be uint8")
@@ -66,6 +70,10 @@ def decode_e4m3fn(codes) -> np.ndarray:
 
 def decode_bf16(bits) -> np.ndarray:
     """Decode bfloat16 bit patterns (uint16) to float64, exactly.
+
+    [DSA-article] "Instantiation": the attention runs on MLA latent rows shared
+    by all query heads; the pages fix no width for them or for the queries, and
+    bfloat16 is the reading taken for both.
 
     bfloat16 is the upper half of an IEEE-754 binary32: the value is the
     binary32 whose bits are ``bits << 16``.
@@ -271,6 +279,9 @@ _E4M3FN_POS = _E4M3FN_TABLE[:0x7F]
 def encode_e4m3fn(y) -> np.ndarray:
     """Nearest e4m3fn code of each value (|y| <= 448), ties to the even code.
 
+    [DSA-article] (1): the index keys are FP8; the pages give no rounding rule,
+    and round to nearest, ties to even, is the reading.
+
     The magnitude is rounded among the 127 non-negative finite values; the
     sign bit is the sign of y (so -0.0, and negative values that round to
     zero, give 0x80).
@@ -290,7 +301,12 @@ def encode_e4m3fn(y) -> np.ndarray:
 
 
 def quantize_index_key(x) -> tuple:
-    """(codes uint8[D], scale float32) of one token's float32 index key."""
+    """(codes uint8[D], scale float32) of one token's float32 index key.
+
+    [DSA-article] (1): index keys are FP8 with one float32 scale per token.  The
+    pages give no recipe; this is the plain one: scale = max(amax / 448,
+    2^-126), x / scale as a float32 division, clamped to +-448, then
+    encode_e4m3fn."""
     x = np.asarray(x, dtype=np.float32)
     amax = np.max(np.abs(x)) if x.size else np.float32(0)
     scale = np.float32(max(np.float32(amax) / np.float32(E4M3FN_MAX), np.float32(SCALE_FLOOR)))
@@ -301,6 +317,10 @@ def quantize_index_key(x) -> tuple:
 def cache_write(k8_cache, ks_cache, kv_cache, seq_id, pos, k_new, kv_new_bits=None, block_table=None,
                 page_size: int = 64):
     """Store new tokens into the caches (returns updated copies).
+
+    [DSA-article] (1) (FP8 index keys) and [mundobytes] "Quick guide to run it
+    locally" (caches in 64-token pages): the step before the indexer, which
+    stores each new token's key and latent row where later queries read them.
 
     Token t goes to logical position pos[t] of sequence seq_id[t] (contiguous
     ``[B, L, ...]`` caches, or physical page ``block_table[b, pos // 64]`` row
@@ -339,7 +359,11 @@ def cache_write(k8_cache, ks_cache, kv_cache, seq_id, pos, k_new, kv_new_bits=No
 def masked_dense_attention(q_bits, kv_bits, idx, seq_id, pos, scale: float, d_v: int = 512, block_table=None,
                            page_size: int = 64):
     """out float64[T, H, d_v], lse float64[T, H] over all s <= pos[t] with the
-    positions absent from idx[t] masked out (empty selection: out 0, lse -inf)."""
+    positions absent from idx[t] masked out (empty selection: out 0, lse -inf).
+
+    [DSA-article] "Lets Discuss it's effectivity and accuracy": at short
+    lengths prefill runs as a masked dense attention.  Over the same selection
+    it equals sparse_mla_attention; only the order of the rows differs."""
     q = decode_bf16(q_bits)
     T, H, D = q.shape
     out = np.zeros((T, H, d_v))
@@ -382,6 +406,10 @@ def masked_dense_attention(q_bits, kv_bits, idx, seq_id, pos, scale: float, d_v:
 def sparse_mla_attention_backward(q_bits, kv_bits, idx, seq_id, scale: float, d_out, d_v: int = 512,
                                   block_table=None, page_size: int = 64):
     """(dq float64[T, H, D], dkv_sel float64[T, k, D], dkv float64[cache shape]).
+
+    [DSA-article] opening paragraph and "Teaching signal": DSA is trained, so
+    the attention of (2) over the selected rows needs its gradient; this is
+    the derivative of sparse_mla_attention.
 
     dkv_sel[t, j] is the gradient reaching the row idx[t, j] from query t
     (zero for padding); dkv adds them up per cache row.
@@ -449,7 +477,11 @@ def sparse_mla_attention_backward(q_bits, kv_bits, idx, seq_id, scale: float, d_
 
 def indexer_kl_target(q_bits, kv_bits, idx, seq_id, scale: float, block_table=None, page_size: int = 64):
     """float64 [T, k]: the head-mean attention probability of each selected
-    entry (0 for padding entries)."""
+    entry (0 for padding entries).
+
+    [DSA-article] "Teaching signal": the indexer learns to imitate the main
+    attention's head-summed distribution; divided by the number of heads it
+    sums to 1 over the selected entries."""
     q = decode_bf16(q_bits)
     kv = decode_bf16(kv_bits)
     T, H, D = q.shape
@@ -474,6 +506,10 @@ def indexer_kl_target(q_bits, kv_bits, idx, seq_id, scale: float, block_table=No
 
 def indexer_kl(q8, qs, w, k8, ks, idx, seq_id, target, block_table=None, page_size: int = 64):
     """KL loss of the indexer against `target` and its gradients.
+
+    [DSA-article] "Teaching signal": the indexer is trained through a KL
+    divergence toward the target distribution, its gradients kept apart from
+    the main model's loss.
 
     Returns (loss [T], dI [T, k], dq [T, H_I, D_I], dw [T, H_I], dk in the
     key cache's shape [..., D_I]), float64; padding entries of idx get dI = 0.
