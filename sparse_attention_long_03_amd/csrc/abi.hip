@@ -1,6 +1,12 @@
 // C ABI of the DSA path: host-side validation, workspace carving, dispatch.
 // Validation runs before any HIP call, so every error path can be exercised
 // without a GPU.  Nothing here allocates memory.
+//
+// dsa_forward chains the method's steps in the order of "DeepSeek V3.2-Exp
+// Cuts Prolonged-Context Costs With DeepSeek Sparse Consideration (DSA)":
+// (1) the lightning indexer's logits, (2) the top-k selection and the
+// attention over the selected entries, under MLA in MQA mode
+// ("Instantiation").
 #include "dsa.h"
 #include "launch.h"
 

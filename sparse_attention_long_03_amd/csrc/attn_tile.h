@@ -2,6 +2,10 @@
 // backward): a tile is 32 latent rows of 576 bf16 gathered from the cache
 // into LDS, the 512 no-rope values of a row stored row-major in padded rows
 // and the 64 rope values with their 16-byte chunks XOR-swizzled by row.
+// The rows are MLA latent entries shared by every query head ("DeepSeek
+// V3.2-Exp Cuts Prolonged-Context Costs With DeepSeek Sparse Consideration
+// (DSA)", "Instantiation"), so one staged tile serves all heads of a
+// workgroup.
 #pragma once
 
 #include "common.h"

@@ -1,5 +1,10 @@
 // Scatter-add of bf16 rows into an fp32 table through a sort.
 //
+// Used by the training side ("DeepSeek V3.2-Exp Cuts Prolonged-Context Costs
+// With DeepSeek Sparse Consideration (DSA)", "Teaching signal"): the sparse
+// attention's key/value gradient and the indexer's key gradient reach each
+// selected cache row once per query that selected it.
+//
 // Many producers (query tokens) each emit one gradient row per selected
 // cache row; a cache row selected by several queries must receive the sum.
 // fp32 atomics reach only about a fifth of the store bandwidth on this GPU,
