@@ -85,12 +85,14 @@ template <typename Sel, typename Bin>
 __device__ __forceinline__ void wave_count(const u32* __restrict__ key, int n, u32* hist, Sel sel, Bin bin) {
   const int lane = threadIdx.x & 63;
   int j = lane;
-  for (; j + 192 < n; j += 256) {
-    const u32 k0 = key[j], k1 = key[j + 64], k2 = key[j + 128], k3 = key[j + 192];
-    if (sel(k0)) atomicAdd(&hist[bin(k0)], 1u);
-    if (sel(k1)) atomicAdd(&hist[bin(k1)], 1u);
-    if (sel(k2)) atomicAdd(&hist[bin(k2)], 1u);
-    if (sel(k3)) atomicAdd(&hist[bin(k3)], 1u);
+  // eight loads in flight per step: the list sits in L2, MALL or HBM
+  for (; j + 448 < n; j += 512) {
+    u32 kk[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) kk[u] = key[j + 64 * u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (sel(kk[u])) atomicAdd(&hist[bin(kk[u])], 1u);
   }
   for (; j < n; j += 64) {
     const u32 k0 = key[j];
@@ -139,23 +141,34 @@ __device__ __forceinline__ void wave_emit(const u32* key, const int32_t* pos, in
                                           u32* okey, int32_t* opos) {
   const int lane = threadIdx.x & 63;
   u32 taken = 0, eq_seen = 0;
-  for (int j0 = 0; j0 < n; j0 += 64) {
-    const int j = j0 + lane;
-    const bool ok = j < n;
-    const u32 kk = ok ? key[j] : 0u;
-    const int32_t pp = ok ? pos[j] : 0;
-    const bool gt = ok && kk > kstar;
-    const bool eq = ok && kk == kstar;
-    const uint64_t meq = __ballot(eq);
-    const bool take = gt || (eq && eq_seen + lanes_below(meq) < ties);
-    const uint64_t mt = __ballot(take);
-    const u32 d = taken + lanes_below(mt);
-    if (take && d < (u32)k) {
-      if (okey != nullptr) okey[d] = kk;
-      opos[d] = pp;
+  // four 64-entry chunks per step, all loaded before any is written: an
+  // entry only moves to a lower or equal index, so in-place compaction
+  // never overwrites an entry that is still to be read
+  for (int j0 = 0; j0 < n; j0 += 256) {
+    u32 kk[4];
+    int32_t pp[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + 64 * u + lane;
+      kk[u] = (j < n) ? key[j] : 0u;
+      pp[u] = (j < n) ? pos[j] : 0;
     }
-    taken += (u32)__popcll(mt);
-    eq_seen += (u32)__popcll(meq);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool ok = j0 + 64 * u + lane < n;
+      const bool gt = ok && kk[u] > kstar;
+      const bool eq = ok && kk[u] == kstar;
+      const uint64_t meq = __ballot(eq);
+      const bool take = gt || (eq && eq_seen + lanes_below(meq) < ties);
+      const uint64_t mt = __ballot(take);
+      const u32 d = taken + lanes_below(mt);
+      if (take && d < (u32)k) {
+        if (okey != nullptr) okey[d] = kk[u];
+        opos[d] = pp[u];
+      }
+      taken += (u32)__popcll(mt);
+      eq_seen += (u32)__popcll(meq);
+    }
   }
 }
 
