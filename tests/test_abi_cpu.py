@@ -59,6 +59,8 @@ def test_topk_validation(lib):
     f = lib.dsa_topk
     assert f(FAKE, 100, FAKE, 4, 100, 0, FAKE, FAKE, 1 << 30, None) == B.DSA_ERR_INVALID_ARG   # k = 0
     assert f(FAKE, 100, FAKE, 4, 100, 4096, FAKE, FAKE, 1 << 30, None) == B.DSA_ERR_UNSUPPORTED  # k > 2048
+    big = 4 * 1024 * 1024  # the longest row the selection handles
+    assert f(FAKE, big + 4, FAKE, 4, big + 1, 64, FAKE, FAKE, 1 << 40, None) == B.DSA_ERR_UNSUPPORTED
     assert f(FAKE, 100, FAKE, 4, 100, 64, FAKE, None, 0, None) == B.DSA_ERR_WORKSPACE
     assert f(FAKE, 100, FAKE, 4, 100, 64, FAKE, FAKE, 16, None) == B.DSA_ERR_WORKSPACE
     assert f(FAKE, 99, FAKE, 4, 100, 64, FAKE, FAKE, 1 << 30, None) == B.DSA_ERR_INVALID_ARG   # ld < max_len

@@ -97,6 +97,15 @@ def test_topk_long_rows_128k_tie_heavy():
     _topk_case(v, [131072, 131071, 65537], 2048)
 
 
+def test_topk_rows_at_the_maximum_length():
+    # the longest supported row (4M positions, 1024 chunks): one row on 256
+    # levels (about 16K candidates tie at the k-th value, more than the LDS
+    # stage holds) and one of distinct-ish uniform values with a ragged tail
+    n = 4 * 1024 * 1024
+    v = torch.cat([I.tie_heavy_logits(1, n, seed=14), torch.rand((1, n), generator=torch.Generator().manual_seed(15))])
+    _topk_case(v.numpy(), [n, n - 3], 2048)
+
+
 def test_topk_signed_zero_and_negatives():
     g = np.random.default_rng(3)
     v = g.choice(np.array([0.0, -0.0, -1.5, 2.0, -3.0, 1e-30], dtype=np.float32), size=(3, 9000))
