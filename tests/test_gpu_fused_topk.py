@@ -163,6 +163,20 @@ def test_forward_many_tokens_uses_fused_selection():
     _check_forward_rows(x, out, lse, idx, [0, 100, 255, 256, 1500, x.T - 1])
 
 
+def test_forward_many_tokens_ignores_workspace_contents():
+    # the fused branch's candidate lists start from whatever the workspace holds
+    x = I.make_inputs(FUSED["prefill_3000"], DEV)
+    p = DSAPath(x)
+    runs = []
+    for fill in (0x00, 0xFF, 0x5A):
+        p.ws(B.DSA_OP_FORWARD).fill_(fill)
+        p.idx.fill_(-5)
+        runs.append([t.clone() for t in p.forward()])
+    o0, l0, i0 = runs[0]
+    for o, l, i in runs[1:]:
+        assert torch.equal(i, i0) and torch.equal(o.view(torch.int16), o0.view(torch.int16)) and torch.equal(l, l0)
+
+
 def test_full_size_prefill64k_sampled():
     x = I.make_inputs(I.CONFIGS["prefill64k"], DEV)
     p = DSAPath(x)

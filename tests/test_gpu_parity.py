@@ -199,6 +199,25 @@ def test_forward_is_deterministic():
     assert torch.equal(i1, i2) and torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
 
 
+def _forward_with_workspace_bytes(p, fill):
+    p.ws(B.DSA_OP_FORWARD).fill_(fill)
+    p.out.fill_(7)
+    p.lse.fill_(-3.0)
+    p.idx.fill_(-5)
+    return [t.clone() for t in p.forward()]
+
+
+def test_forward_ignores_workspace_contents():
+    # the workspace holds nothing on entry: every byte set to 0x00, 0xFF or
+    # 0x5A (and the outputs pre-filled with junk) gives the same result
+    x = _inputs("decode_ragged")
+    p = DSAPath(x)
+    runs = [_forward_with_workspace_bytes(p, f) for f in (0x00, 0xFF, 0x5A)]
+    o0, l0, i0 = runs[0]
+    for o, l, i in runs[1:]:
+        assert torch.equal(i, i0) and torch.equal(o.view(torch.int16), o0.view(torch.int16)) and torch.equal(l, l0)
+
+
 def test_paged_equals_contiguous_bitwise():
     cfg = I.scaled(I.CONFIGS["decode32k"], B=3, L=2500, queries_per_seq=2, k=1024)
     x = I.make_inputs(cfg, DEV)
