@@ -26,6 +26,7 @@ from .dsa_oracle import (  # noqa: F401
     encode_e4m3fn,
     quantize_index_key,
     cache_write,
+    indexer_projection,
     masked_dense_attention,
     sparse_mla_attention_backward,
     indexer_kl_target,

@@ -344,6 +344,42 @@ def cache_write(k8_cache, ks_cache, kv_cache, seq_id, pos, k_new, kv_new_bits=No
 
 
 # ---------------------------------------------------------------------------
+# (f4b) The indexer's inputs from a token's hidden state
+# ---------------------------------------------------------------------------
+#
+# [DSA-article] (1): for each query token h_t in R^d the indexer forms a few
+# small heads q[t, j] and one weight w[t, j] per head, and every earlier token
+# contributes its own index key.  The pages give no formula for these.
+# Reading taken: plain linear maps of the hidden state, without bias,
+#   q[t] = Wq h_t   (H_I * D_I values, head j = rows j*D_I .. j*D_I + D_I - 1)
+#   w[t] = Ww h_t   (H_I values)
+#   k[t] = Wk h_t   (D_I values, the token's own index key)
+# with the query then stored like an index key: FP8 e4m3fn with one float32
+# scale per token over all of its H_I * D_I values (quantize_index_key).  The
+# products are taken exactly (float64 over bf16 inputs, whose products and
+# sums are exact to float64 rounding) and rounded once to float32, the
+# precision from which the query is quantised.
+
+
+def indexer_projection(h_bits, wq_bits, ww_bits, H_I: int, D_I: int, wk_bits=None):
+    """(q8 uint8[T, H_I, D_I], qs float32[T], w float32[T, H_I], k float32[T, D_I]
+    or None) from hidden states h (bf16 bits [T, d]) and bf16 weight bits
+    Wq [H_I*D_I, d], Ww [H_I, d], Wk [D_I, d] (optional)."""
+    h = decode_bf16(h_bits)
+    q = (h @ decode_bf16(wq_bits).T).astype(np.float32)
+    w = (h @ decode_bf16(ww_bits).T).astype(np.float32)
+    T = h.shape[0]
+    q8 = np.zeros((T, H_I, D_I), dtype=np.uint8)
+    qs = np.zeros(T, dtype=np.float32)
+    for t in range(T):
+        codes, scale = quantize_index_key(q[t])
+        q8[t] = codes.reshape(H_I, D_I)
+        qs[t] = scale
+    k = None if wk_bits is None else (h @ decode_bf16(wk_bits).T).astype(np.float32)
+    return q8, qs, w, k
+
+
+# ---------------------------------------------------------------------------
 # (f1) Masked dense variant of the sparse attention (short prefill lengths)
 # ---------------------------------------------------------------------------
 #

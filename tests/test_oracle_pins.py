@@ -655,3 +655,70 @@ def test_kl_zero_when_the_indexer_matches_the_target():
     np.testing.assert_allclose(dI, 0, atol=1e-15)
     np.testing.assert_allclose(dq, 0, atol=1e-13)
     np.testing.assert_allclose(dk, 0, atol=1e-13)
+
+
+# ----------------------------------------------------------------- indexer projection (h_t -> q, w, k)
+
+def _bf16_bits(a):
+    import torch
+    return torch.from_numpy(np.asarray(a, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_indexer_projection_matches_torch_route():
+    """Projection and per-token FP8 quantisation against an independent torch
+    route: fp64 matmul of the bf16 values, rounded to fp32, and torch's own
+    float8_e4m3fn conversion of the clamped quotient."""
+    import torch
+    rng = np.random.default_rng(21)
+    T, d, H_I, D_I = 5, 256, 4, 64
+    h = _bf16_bits(rng.normal(size=(T, d)))
+    wq = _bf16_bits(rng.normal(size=(H_I * D_I, d)) / 16)
+    ww = _bf16_bits(rng.normal(size=(H_I, d)) / 16)
+    wk = _bf16_bits(rng.normal(size=(D_I, d)) / 16)
+    q8, qs, w, k = O.indexer_projection(h, wq, ww, H_I, D_I, wk)
+    tb = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).double()
+    ht = tb(h)
+    qt = (ht @ tb(wq).T).float()
+    s_t = torch.clamp(qt.abs().amax(dim=1) / 448.0, min=2.0 ** -126)
+    c_t = (qt / s_t[:, None]).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(qs, s_t.numpy())
+    assert np.array_equal(q8.reshape(T, -1), c_t)
+    assert np.array_equal(w, (ht @ tb(ww).T).float().numpy())
+    assert np.array_equal(k, (ht @ tb(wk).T).float().numpy())
+
+
+def test_indexer_projection_head_major_layout():
+    """A permutation matrix as Wq puts h's entries into (head, dim) slots:
+    row j*D_I + d of Wq feeds head j, dim d."""
+    rng = np.random.default_rng(22)
+    T, H_I, D_I = 3, 4, 64
+    d = H_I * D_I
+    perm = rng.permutation(d)
+    hv = rng.normal(size=(T, d)).astype(np.float32)
+    h = _bf16_bits(hv)
+    wq = np.zeros((d, d), np.float32)
+    wq[np.arange(d), perm] = 1.0
+    ww = np.zeros((H_I, d), np.float32)
+    ww[np.arange(H_I), perm[:H_I]] = 2.0
+    q8, qs, w, k = O.indexer_projection(h, _bf16_bits(wq), _bf16_bits(ww), H_I, D_I)
+    hb = O.decode_bf16(h).astype(np.float32)
+    assert k is None
+    for t in range(T):
+        codes, scale = O.quantize_index_key(hb[t, perm])
+        assert scale == qs[t]
+        assert np.array_equal(q8[t], codes.reshape(H_I, D_I))
+        assert np.array_equal(w[t], 2.0 * hb[t, perm[:H_I]])
+
+
+def test_indexer_projection_power_of_two_scaling():
+    """Doubling h doubles q's scale, w and k exactly and leaves the codes."""
+    rng = np.random.default_rng(23)
+    T, d, H_I, D_I = 4, 128, 4, 64
+    hv = rng.normal(size=(T, d)).astype(np.float32)
+    wq = _bf16_bits(rng.normal(size=(H_I * D_I, d)))
+    ww = _bf16_bits(rng.normal(size=(H_I, d)))
+    wk = _bf16_bits(rng.normal(size=(D_I, d)))
+    a = O.indexer_projection(_bf16_bits(hv), wq, ww, H_I, D_I, wk)
+    b = O.indexer_projection(_bf16_bits(2 * hv), wq, ww, H_I, D_I, wk)
+    assert np.array_equal(a[0], b[0])
+    assert np.array_equal(2 * a[1], b[1]) and np.array_equal(2 * a[2], b[2]) and np.array_equal(2 * a[3], b[3])
