@@ -60,7 +60,7 @@ size_t forward_ws(int32_t T, int32_t max_len, int32_t H, int32_t k, bool with_id
     s += align256(fused_topk_workspace_bytes(T, fused_topk_cap(max_len, k)));
   } else {
     s += align256((size_t)T * ld * 4);                  // logits
-    s += topk_workspace_bytes(T, ld, k);
+    s += topk_workspace_bytes(T, max_len, k);
   }
   s += align256(attn_workspace_bytes(T, H, k));
   return s;
@@ -126,7 +126,7 @@ size_t dsa_workspace_bytes(int32_t op, int32_t T, int32_t max_len, int32_t H, in
   if (T < 0 || max_len < 0 || H < 0 || k < 0) return 0;
   const int64_t ld = ((int64_t)max_len + 3) & ~int64_t(3);
   switch (op) {
-    case DSA_OP_TOPK: return (k > 0) ? topk_workspace_bytes(T, ld, k) : 0;
+    case DSA_OP_TOPK: return (k > 0) ? topk_workspace_bytes(T, max_len, k) : 0;
     case DSA_OP_ATTN: return (H > 0 && k > 0) ? attn_workspace_bytes(T, H, k) : 0;
     case DSA_OP_FORWARD: return (H > 0 && k > 0) ? forward_ws(T, max_len, H, k, true) : 0;
     case DSA_OP_INDEXER_TOPK: return (k > 0) ? fused_topk_workspace_bytes(T, fused_topk_cap(max_len, k)) : 0;
@@ -160,7 +160,7 @@ int dsa_indexer_topk(const dsa_queries* q, const dsa_kv_layout* layout, int32_t 
   if (idx == nullptr) return DSA_ERR_INVALID_ARG;
   const int cap = fused_topk_cap_from_bytes(q->T, workspace_bytes);
   if (workspace == nullptr || !aligned(workspace, 256) || !fused_topk_cap_ok(cap, k)) return DSA_ERR_WORKSPACE;
-  return hip_status(launch_indexer_topk(q->T, H_I, D_I, q_fp8, q_scale, w, k_fp8, k_scale, q->seq_id, q->pos, lay, k,
+  return hip_status(launch_indexer_topk(q->T, q->max_len, H_I, D_I, q_fp8, q_scale, w, k_fp8, k_scale, q->seq_id, q->pos, lay, k,
                                         cap, idx, workspace, stream));
 }
 
@@ -189,7 +189,7 @@ int dsa_topk(const float* logits, int64_t ld_logits, const int32_t* valid_len, i
   if (T == 0) return DSA_OK;
   if (!logits || !valid_len || !idx) return DSA_ERR_INVALID_ARG;
   if (ld_logits < max_len || (ld_logits & 3) || !aligned(logits, 16)) return DSA_ERR_INVALID_ARG;
-  const size_t need = topk_workspace_bytes(T, ld_logits, k);
+  const size_t need = topk_workspace_bytes(T, max_len, k);
   if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)) return DSA_ERR_WORKSPACE;
   return hip_status(launch_topk(logits, ld_logits, valid_len, 0, T, max_len, k, idx, workspace, false, stream));
 }
@@ -366,14 +366,14 @@ int dsa_forward(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, 
     const int cap = fused_topk_cap(q->max_len, k);
     void* ws_sel = p;
     p += align256(fused_topk_workspace_bytes(q->T, cap));
-    e = launch_indexer_topk(q->T, H_I, D_I, iq_fp8, iq_scale, iw, ik_fp8, ik_scale, q->seq_id, q->pos, lay, k, cap,
+    e = launch_indexer_topk(q->T, q->max_len, H_I, D_I, iq_fp8, iq_scale, iw, ik_fp8, ik_scale, q->seq_id, q->pos, lay, k, cap,
                             idx, ws_sel, stream);
     if (e != hipSuccess) return DSA_ERR_HIP;
   } else {
     float* logits = reinterpret_cast<float*>(p);
     p += align256((size_t)q->T * ld * 4);
     void* ws_topk = p;
-    p += topk_workspace_bytes(q->T, ld, k);
+    p += topk_workspace_bytes(q->T, q->max_len, k);
     e = launch_topk_zero_hist(ws_topk, q->T, stream);
     if (e != hipSuccess) return DSA_ERR_HIP;
     e = launch_indexer(q->T, q->max_len, H_I, D_I, iq_fp8, iq_scale, iw, ik_fp8, ik_scale, q->seq_id, q->pos, lay,

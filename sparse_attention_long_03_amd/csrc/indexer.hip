@@ -94,13 +94,15 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void indexer_kernel(const uint8_t* 
                                                                  const int32_t* __restrict__ seq_id,
                                                                  const int32_t* __restrict__ pos, Layout lay,
                                                                  float* __restrict__ logits, int64_t ld,
-                                                                 u32* __restrict__ hist) {
+                                                                 u32* __restrict__ hist, int max_len) {
   __shared__ __attribute__((aligned(16))) uint8_t slabs[IDX_WAVES][64 * D_I];
   __shared__ u32 h_lds[2048];
   using Stage = GroupStage<H_I, D_I>;
 
   const int t = blockIdx.y;
-  const int p = pos[t];
+  // a position past the stated bound is taken as the last one it allows, so
+  // no store leaves the row or the launched grid
+  const int p = min(pos[t], max_len - 1);
   const int wg_base = blockIdx.x * IDX_KEYS_PER_WG;
   if (wg_base > p) return;
   const int b = seq_id[t];
@@ -172,10 +174,10 @@ static hipError_t launch_t(int T, int max_len, const uint8_t* q8, const float* q
   dim3 grid((max_len + IDX_KEYS_PER_WG - 1) / IDX_KEYS_PER_WG, T);
   if (lay.paged)
     hipLaunchKernelGGL((indexer_kernel<H_I, D_I, false>), grid, dim3(IDX_WAVES * 64), 0, stream, q8, qs, w, k8, ks,
-                       seq_id, pos, lay, logits, ld, hist);
+                       seq_id, pos, lay, logits, ld, hist, max_len);
   else
     hipLaunchKernelGGL((indexer_kernel<H_I, D_I, true>), grid, dim3(IDX_WAVES * 64), 0, stream, q8, qs, w, k8, ks,
-                       seq_id, pos, lay, logits, ld, hist);
+                       seq_id, pos, lay, logits, ld, hist, max_len);
   return hipGetLastError();
 }
 

@@ -45,6 +45,19 @@ constexpr int FT_BINS = 2048;
 // wave's earlier accesses are done, so lanes see each other's writes.
 __device__ __forceinline__ void wave_sync() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup"); }
 
+#ifndef LDS_AS
+#define LDS_AS __attribute__((address_space(3)))
+#endif
+
+// A wave's selection histogram lives in LDS.  Its pointer carries the LDS
+// address space in every signature below, so each access is an LDS
+// instruction whether or not the helpers are inlined.
+typedef LDS_AS u32 lds_u32;
+
+__device__ __forceinline__ void lds_inc(lds_u32* p) {
+  __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 __device__ __forceinline__ u32 lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((u32)(m >> 32), __builtin_amdgcn_mbcnt_lo((u32)m, 0u));
 }
@@ -52,10 +65,10 @@ __device__ __forceinline__ u32 lanes_below(uint64_t m) {
 // Wave-level threshold search over NB bins from the top: the bin holding the
 // need-th largest entry (1 <= need <= total) and the count in higher bins.
 template <int NB>
-__device__ __forceinline__ void wave_threshold(const u32* hist, u32 need, u32& bin, u32& above) {
+__device__ __forceinline__ void wave_threshold(const lds_u32* hist, u32 need, u32& bin, u32& above) {
   constexpr int BPL = NB / 64;
   const int lane = threadIdx.x & 63;
-  const u32* run = hist + NB - 1 - lane * BPL;  // this lane's bins, from the top: run[0], run[-1], ...
+  const lds_u32* run = hist + NB - 1 - lane * BPL;  // this lane's bins, from the top: run[0], run[-1], ...
   u32 mine = 0;
 #pragma unroll 8
   for (int i = 0; i < BPL; ++i) mine += run[-i];
@@ -82,7 +95,7 @@ __device__ __forceinline__ void wave_threshold(const u32* hist, u32 need, u32& b
 
 // Adds 1 to hist[f(key)] for every list entry whose key passes `sel`.
 template <typename Sel, typename Bin>
-__device__ __forceinline__ void wave_count(const u32* __restrict__ key, int n, u32* hist, Sel sel, Bin bin) {
+__device__ __forceinline__ void wave_count(const u32* __restrict__ key, int n, lds_u32* hist, Sel sel, Bin bin) {
   const int lane = threadIdx.x & 63;
   int j = lane;
   // eight loads in flight per step: the list sits in L2, MALL or HBM
@@ -92,17 +105,18 @@ __device__ __forceinline__ void wave_count(const u32* __restrict__ key, int n, u
     for (int u = 0; u < 8; ++u) kk[u] = key[j + 64 * u];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (sel(kk[u])) atomicAdd(&hist[bin(kk[u])], 1u);
+      if (sel(kk[u])) lds_inc(&hist[bin(kk[u])]);
   }
   for (; j < n; j += 64) {
     const u32 k0 = key[j];
-    if (sel(k0)) atomicAdd(&hist[bin(k0)], 1u);
+    if (sel(k0)) lds_inc(&hist[bin(k0)]);
   }
 }
 
 // Exact k-th largest key of a list of n > k entries, by one wave: kstar, and
 // how many entries equal to it are kept (ties >= 1).
-__device__ __forceinline__ void wave_kth(const u32* __restrict__ key, int n, int k, u32* hist, u32& kstar, u32& ties) {
+__device__ __forceinline__ void wave_kth(const u32* __restrict__ key, int n, int k, lds_u32* hist, u32& kstar,
+                                         u32& ties) {
   const int lane = threadIdx.x & 63;
   wave_sync();  // the list entries this wave appended are visible
   for (int i = lane; i < FT_BINS; i += 64) hist[i] = 0;
@@ -200,7 +214,7 @@ template <int H_I, int D_I>
 __global__ __launch_bounds__(FT_WAVES * 64) void indexer_topk_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
     const uint8_t* __restrict__ k8, const float* __restrict__ ks, const int32_t* __restrict__ seq_id,
-    const int32_t* __restrict__ pos, Layout lay, int T, int k, int cap, int32_t* __restrict__ idx,
+    const int32_t* __restrict__ pos, Layout lay, int T, int max_len, int k, int cap, int32_t* __restrict__ idx,
     u32* __restrict__ ckey, int32_t* __restrict__ cpos) {
   constexpr int STRIDE = D_I + 16;  // padded LDS row: rotates banks between rows
   constexpr int CPT = D_I / 4;      // staged bytes per thread
@@ -218,7 +232,7 @@ __global__ __launch_bounds__(FT_WAVES * 64) void indexer_topk_kernel(
   if (tid < FT_QB) {
     const int t = t0 + tid;
     s_seq[tid] = (t < T) ? seq_id[t] : -1;
-    s_pos[tid] = (t < T) ? pos[t] : -1;
+    s_pos[tid] = (t < T) ? min(pos[t], max_len - 1) : -1;  // clamped to the stated bound
   }
   __syncthreads();
 
@@ -244,7 +258,7 @@ __global__ __launch_bounds__(FT_WAVES * 64) void indexer_topk_kernel(
     lkey[qi] = ckey + tt * cap;
     lpos[qi] = cpos + tt * cap;
   }
-  u32* my_hist = hist[wid];
+  lds_u32* my_hist = (lds_u32*)&hist[wid][0];
 
   const int sr = tid >> 2;         // staged key row
   const int sc = (tid & 3) * CPT;  // staged byte offset in the row
@@ -402,24 +416,24 @@ bool fused_topk_cap_ok(int cap, int k) {
 }
 
 template <int H_I, int D_I>
-static hipError_t launch_fused_t(int T, const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8,
+static hipError_t launch_fused_t(int T, int max_len, const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8,
                                  const float* ks, const int32_t* seq_id, const int32_t* pos, const Layout& lay,
                                  int k, int cap, int32_t* idx, void* ws, hipStream_t stream) {
   u32* ckey = static_cast<u32*>(ws);
   int32_t* cpos = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + (size_t)T * cap * 4);
   const int blocks = (T + FT_QB - 1) / FT_QB;
   hipLaunchKernelGGL((indexer_topk_kernel<H_I, D_I>), dim3(blocks), dim3(FT_WAVES * 64), 0, stream, q8, qs, w, k8,
-                     ks, seq_id, pos, lay, T, k, cap, idx, ckey, cpos);
+                     ks, seq_id, pos, lay, T, max_len, k, cap, idx, ckey, cpos);
   return hipGetLastError();
 }
 
-hipError_t launch_indexer_topk(int T, int H_I, int D_I, const uint8_t* q8, const float* qs, const float* w,
+hipError_t launch_indexer_topk(int T, int max_len, int H_I, int D_I, const uint8_t* q8, const float* qs, const float* w,
                                const uint8_t* k8, const float* ks, const int32_t* seq_id, const int32_t* pos,
                                const Layout& lay, int k, int cap, int32_t* idx, void* ws, hipStream_t stream) {
   if (T == 0) return hipSuccess;
 #define DSA_FT_CASE(HH, DD) \
   if (H_I == HH && D_I == DD) \
-    return launch_fused_t<HH, DD>(T, q8, qs, w, k8, ks, seq_id, pos, lay, k, cap, idx, ws, stream);
+    return launch_fused_t<HH, DD>(T, max_len, q8, qs, w, k8, ks, seq_id, pos, lay, k, cap, idx, ws, stream);
   DSA_FT_CASE(64, 128)
   DSA_FT_CASE(64, 64)
   DSA_FT_CASE(4, 128)

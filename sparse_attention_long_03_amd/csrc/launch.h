@@ -23,7 +23,7 @@ int fused_topk_cap(int max_len, int k);              // preferred capacity
 int fused_topk_cap_from_bytes(int T, size_t bytes);  // capacity a workspace holds
 size_t fused_topk_workspace_bytes(int T, int cap);
 bool fused_topk_cap_ok(int cap, int k);
-hipError_t launch_indexer_topk(int T, int H_I, int D_I, const uint8_t* q8, const float* qs, const float* w,
+hipError_t launch_indexer_topk(int T, int max_len, int H_I, int D_I, const uint8_t* q8, const float* qs, const float* w,
                                const uint8_t* k8, const float* ks, const int32_t* seq_id, const int32_t* pos,
                                const Layout& lay, int k, int cap, int32_t* idx, void* ws, hipStream_t stream);
 
@@ -31,7 +31,7 @@ hipError_t launch_indexer_topk(int T, int H_I, int D_I, const uint8_t* q8, const
 // lives at the start of the top-k workspace (topk_hist_buffer); with
 // hist_ready the caller has already filled it (fused indexer epilogue).
 constexpr int64_t kTopkMaxLen = 4 * 1024 * 1024;  // longest row the selection handles
-size_t topk_workspace_bytes(int T, int64_t ld, int k);
+size_t topk_workspace_bytes(int T, int64_t max_len, int k);
 u32* topk_hist_buffer(void* ws);
 hipError_t launch_topk_zero_hist(void* ws, int T, hipStream_t stream);
 hipError_t launch_topk(const float* logits, int64_t ld, const int32_t* valid_len, int len_add, int T, int max_len,

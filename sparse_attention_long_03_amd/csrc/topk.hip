@@ -33,7 +33,11 @@ constexpr int TK_BINS = 2048;
 constexpr int TK_MAX_CHUNKS = TK_RES_NT;  // rows up to 4M positions
 constexpr int TK_RES_STAGE = 12288;       // candidates staged in LDS (96 KB)
 
-__device__ __forceinline__ int row_len(const int32_t* valid_len, int len_add, int t) { return valid_len[t] + len_add; }
+// Valid length of row t, clamped to the stated bound max_len (so a length
+// past it never reaches beyond the launched chunks or the workspace).
+__device__ __forceinline__ int row_len(const int32_t* valid_len, int len_add, int t, int max_len) {
+  return min(valid_len[t] + len_add, max_len);
+}
 
 // Threshold search over NB bins visited from the top with NT threads: the bin
 // holding the `need`-th largest element and the count in higher bins.
@@ -73,10 +77,10 @@ __global__ void zero_u32_kernel(u32* __restrict__ p, int64_t n) {
 // Histogram of the top 11 key bits of each row (standalone selection).
 __global__ __launch_bounds__(TK_CHUNK_NT) void topk_hist_kernel(const float* __restrict__ logits, int64_t ld,
                                                                 const int32_t* __restrict__ valid_len, int len_add,
-                                                                int k, u32* __restrict__ hist) {
+                                                                int max_len, int k, u32* __restrict__ hist) {
   __shared__ u32 h[TK_BINS];
   const int t = blockIdx.y;
-  const int n = row_len(valid_len, len_add, t);
+  const int n = row_len(valid_len, len_add, t, max_len);
   const int c0 = blockIdx.x * TK_CH;
   if (n <= k || c0 >= n) return;
   for (int i = threadIdx.x; i < TK_BINS; i += TK_CHUNK_NT) h[i] = 0;
@@ -102,14 +106,14 @@ struct TopkWs {
 
 __global__ __launch_bounds__(TK_CHUNK_NT) void topk_chunk_kernel(const float* __restrict__ logits, int64_t ld,
                                                                  const int32_t* __restrict__ valid_len, int len_add,
-                                                                 int k, TopkWs ws) {
+                                                                 int max_len, int k, TopkWs ws) {
   constexpr int NT = TK_CHUNK_NT;
   constexpr int E = TK_CH / NT;  // 16 positions per thread
   __shared__ u32 scratch[NT / 64 + 1];
   __shared__ u32 sh_bin, sh_above;
   const int t = blockIdx.y;
   const int c = blockIdx.x;
-  const int n = row_len(valid_len, len_add, t);
+  const int n = row_len(valid_len, len_add, t, max_len);
   const int c0 = c * TK_CH;
   if (n <= k || c0 >= n) return;
   // the chunk's logits are loaded first: their latency overlaps the threshold search
@@ -274,7 +278,8 @@ __device__ __forceinline__ void chunk_of_n(const u32* off, int n, int top, const
 }
 
 __global__ __launch_bounds__(TK_RES_NT) void topk_resolve_kernel(const int32_t* __restrict__ valid_len, int len_add,
-                                                                 int k, int32_t* __restrict__ idx, TopkWs ws) {
+                                                                 int max_len, int k, int32_t* __restrict__ idx,
+                                                                 TopkWs ws) {
   constexpr int NT = TK_RES_NT;
   __shared__ u32 hist[TK_BINS];
   __shared__ u32 scratch[NT / 64 + 1];
@@ -284,7 +289,7 @@ __global__ __launch_bounds__(TK_RES_NT) void topk_resolve_kernel(const int32_t* 
   __shared__ int32_t s_cpos[TK_RES_STAGE];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
-  const int n = row_len(valid_len, len_add, t);
+  const int n = row_len(valid_len, len_add, t, max_len);
   int32_t* __restrict__ out = idx + (int64_t)t * k;
   if (n <= k) {
     for (int i = tid; i < k; i += NT) out[i] = (i < n) ? i : -1;
@@ -375,11 +380,16 @@ __global__ __launch_bounds__(TK_RES_NT) void topk_resolve_kernel(const int32_t* 
   select_candidates<NT>(C, need1, out + A, cand_key, cand_pos, hist, scratch, &sh_bin, &sh_above);
 }
 
-static int topk_nch(int64_t ld) { return (int)((ld + TK_CH - 1) / TK_CH); }
+// Chunk slots per row: enough for the longest valid row (max_len); the row
+// stride of the logits plays no part in the workspace.
+static int topk_nch(int64_t max_len) {
+  const int64_t c = (max_len + TK_CH - 1) / TK_CH;
+  return c > 0 ? (int)c : 1;
+}
 
-static TopkWs carve(void* ws, int T, int64_t ld, int k) {
+static TopkWs carve(void* ws, int T, int64_t max_len, int k) {
   TopkWs w;
-  w.nch = topk_nch(ld);
+  w.nch = topk_nch(max_len);
   w.cap_above = k < TK_CH ? k : TK_CH;
   char* p = static_cast<char*>(ws);
   const size_t slots = (size_t)T * w.nch;
@@ -395,8 +405,8 @@ static TopkWs carve(void* ws, int T, int64_t ld, int k) {
   return w;
 }
 
-size_t topk_workspace_bytes(int T, int64_t ld, int k) {
-  const size_t slots = (size_t)T * topk_nch(ld);
+size_t topk_workspace_bytes(int T, int64_t max_len, int k) {
+  const size_t slots = (size_t)T * topk_nch(max_len);
   return align256((size_t)T * TK_BINS * 4) + align256(slots * 2 * 4) + align256(slots * (size_t)(k < TK_CH ? k : TK_CH) * 4) +
          2 * align256(slots * TK_CH * 4);
 }
@@ -414,18 +424,17 @@ hipError_t launch_topk_zero_hist(void* ws, int T, hipStream_t stream) {
 hipError_t launch_topk(const float* logits, int64_t ld, const int32_t* valid_len, int len_add, int T, int max_len,
                        int k, int32_t* idx, void* ws, bool hist_ready, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  TopkWs w = carve(ws, T, ld, k);
-  const int nch_need = (max_len + TK_CH - 1) / TK_CH;
-  const int nch = nch_need > 0 ? nch_need : 1;
+  TopkWs w = carve(ws, T, max_len, k);
+  const int nch = w.nch;
   if (!hist_ready) {
     hipError_t e = launch_topk_zero_hist(ws, T, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_hist_kernel, dim3(nch, T), dim3(TK_CHUNK_NT), 0, stream, logits, ld, valid_len, len_add, k,
-                       w.hist);
+    hipLaunchKernelGGL(topk_hist_kernel, dim3(nch, T), dim3(TK_CHUNK_NT), 0, stream, logits, ld, valid_len, len_add,
+                       max_len, k, w.hist);
   }
-  hipLaunchKernelGGL(topk_chunk_kernel, dim3(nch, T), dim3(TK_CHUNK_NT), 0, stream, logits, ld, valid_len, len_add, k,
-                     w);
-  hipLaunchKernelGGL(topk_resolve_kernel, dim3(T), dim3(TK_RES_NT), 0, stream, valid_len, len_add, k, idx, w);
+  hipLaunchKernelGGL(topk_chunk_kernel, dim3(nch, T), dim3(TK_CHUNK_NT), 0, stream, logits, ld, valid_len, len_add,
+                     max_len, k, w);
+  hipLaunchKernelGGL(topk_resolve_kernel, dim3(T), dim3(TK_RES_NT), 0, stream, valid_len, len_add, max_len, k, idx, w);
   return hipGetLastError();
 }
 

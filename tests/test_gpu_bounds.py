@@ -1,0 +1,152 @@
+"""Every entry point stays inside the buffers it is given.
+
+Each workspace is allocated at exactly the size dsa_workspace_bytes states
+(or the smallest the call accepts), followed by a guard region; each output
+is followed by one too; the logit rows carry a guard pattern past pos[t] (the
+header leaves those entries unwritten).  After the call every guard must hold
+its pattern.  The cases cover the decode and many-token branches of
+dsa_forward, the standalone steps, the fused selection at its minimum
+workspace, the masked dense variant, the backward and the KL signal.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from sparse_attention_long_03_amd import binding as B
+from sparse_attention_long_03_amd import inputs as I
+from sparse_attention_long_03_amd.path import DSAPath
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+GUARD = 1 << 16          # bytes of guard after each buffer
+PATTERN = 0xA5
+
+
+class Guarded:
+    """A device buffer of `nbytes` followed by a guard region."""
+
+    def __init__(self, nbytes):
+        self.n = int(nbytes)
+        self.raw = torch.full((self.n + GUARD,), PATTERN, dtype=torch.uint8, device=DEV)
+
+    def bytes(self):
+        return self.raw[:self.n]
+
+    def view(self, dtype, shape):
+        return self.raw[:self.n].view(dtype).view(shape)
+
+    def intact(self):
+        return bool(torch.all(self.raw[self.n:] == PATTERN))
+
+
+def _nbytes(dtype, shape):
+    return int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+
+
+def _guarded(dtype, shape):
+    g = Guarded(_nbytes(dtype, shape))
+    return g, g.view(dtype, shape)
+
+
+CASES = {
+    "decode_ragged": I.scaled(I.CONFIGS["decode32k"], B=3, L=5000, queries_per_seq=2),
+    "paged": I.scaled(I.CONFIGS["ragged_paged"], B=5, L=3000, min_len=100, H=64, k=1024),
+    "prefill_2500": I.scaled(I.CONFIGS["prefill64k"], L=2500, H=16, k=256),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_forward_stays_in_its_buffers(name):
+    x = I.make_inputs(CASES[name], DEV)
+    c = x.cfg
+    p = DSAPath(x)
+    ws = Guarded(B.dsa_workspace_bytes(B.DSA_OP_FORWARD, x.T, x.max_len, c.H, c.k))
+    go, out = _guarded(torch.bfloat16, (x.T, c.H, c.d_v))
+    gl, lse = _guarded(torch.float32, (x.T, c.H))
+    gi, idx = _guarded(torch.int32, (x.T, c.k))
+    B.dsa_forward(p.q, p.layout, c.H_I, c.D_I, x.iq8, x.iqs, x.iw, x.ik8, x.iks, c.H, x.q, x.kv, c.k, c.scale, out,
+                  lse, idx, ws.bytes())
+    torch.cuda.synchronize()
+    assert ws.intact() and go.intact() and gl.intact() and gi.intact()
+
+
+@pytest.mark.parametrize("name", ["decode_ragged", "paged"])
+def test_steps_stay_in_their_buffers(name):
+    x = I.make_inputs(CASES[name], DEV)
+    c = x.cfg
+    p = DSAPath(x)
+    ld = p.ld
+    # logits: rows guarded past pos[t] and the whole buffer followed by a guard
+    gl, logits = _guarded(torch.float32, (x.T, ld))
+    B.dsa_indexer_logits(p.q, p.layout, c.H_I, c.D_I, x.iq8, x.iqs, x.iw, x.ik8, x.iks, logits)
+    torch.cuda.synchronize()
+    assert gl.intact()
+    raw = logits.view(torch.int32)
+    for t in range(x.T):
+        n = int(x.pos[t]) + 1
+        assert torch.all(raw[t, n:] == np.int32(np.uint32(0xA5A5A5A5).view(np.int32))), f"row {t} written past pos"
+    # top-k in exactly its stated workspace
+    ws = Guarded(B.dsa_workspace_bytes(B.DSA_OP_TOPK, x.T, x.max_len, 0, c.k))
+    gi, idx = _guarded(torch.int32, (x.T, c.k))
+    B.dsa_topk(logits, p.valid_len, x.max_len, c.k, idx, ws.bytes())
+    torch.cuda.synchronize()
+    assert ws.intact() and gi.intact()
+    # attention
+    ws = Guarded(max(B.dsa_workspace_bytes(B.DSA_OP_ATTN, x.T, x.max_len, c.H, c.k), 256))
+    go, out = _guarded(torch.bfloat16, (x.T, c.H, c.d_v))
+    gs, lse = _guarded(torch.float32, (x.T, c.H))
+    B.dsa_sparse_mla_attn(p.q, p.layout, c.H, x.q, x.kv, idx, c.k, c.scale, out, lse, ws.bytes())
+    torch.cuda.synchronize()
+    assert ws.intact() and go.intact() and gs.intact()
+    # masked dense variant over the same selection
+    ws = Guarded(max(B.dsa_workspace_bytes(B.DSA_OP_DENSE_ATTN, x.T, x.max_len, c.H, c.k), 256))
+    go, out = _guarded(torch.bfloat16, (x.T, c.H, c.d_v))
+    gs, lse2 = _guarded(torch.float32, (x.T, c.H))
+    B.dsa_masked_dense_attn(p.q, p.layout, c.H, x.q, x.kv, idx, c.k, c.scale, out, lse2, ws.bytes())
+    torch.cuda.synchronize()
+    assert ws.intact() and go.intact() and gs.intact()
+
+
+def test_fused_selection_at_its_minimum_workspace():
+    x = I.make_inputs(CASES["prefill_2500"], DEV)
+    c = x.cfg
+    p = DSAPath(x)
+    ws = Guarded(8 * x.T * (c.k + 320))   # the smallest list capacity the call accepts
+    gi, idx = _guarded(torch.int32, (x.T, c.k))
+    B.dsa_indexer_topk(p.q, p.layout, c.H_I, c.D_I, x.iq8, x.iqs, x.iw, x.ik8, x.iks, c.k, idx, ws.bytes())
+    torch.cuda.synchronize()
+    assert ws.intact() and gi.intact()
+
+
+def test_backward_and_kl_stay_in_their_buffers():
+    cfg = I.scaled(I.CONFIGS["ragged_paged"], B=4, L=2500, min_len=100, H=64, k=512)
+    x = I.make_inputs(cfg, DEV)
+    p = DSAPath(x)
+    idx = I.random_selection(cfg, x.pos, cfg.k, DEV)
+    out, lse = p.attn(idx)
+    dO = I.output_grad(cfg, x.T, DEV)
+    ws = Guarded(B.dsa_workspace_bytes(B.DSA_OP_ATTN_BWD, x.T, x.max_len, cfg.H, cfg.k))
+    gq, dq = _guarded(torch.float32, (x.T, cfg.H, cfg.D))
+    gk, dkv = _guarded(torch.float32, tuple(x.kv.shape))
+    dkv.zero_()
+    B.dsa_sparse_mla_attn_bwd(p.q, p.layout, cfg.H, x.q, x.kv, idx, cfg.k, cfg.scale, out, lse, dO, dq, dkv,
+                              ws.bytes())
+    torch.cuda.synchronize()
+    assert ws.intact() and gq.intact() and gk.intact()
+    target = I.random_distribution(cfg, idx)
+    ws = Guarded(B.dsa_workspace_bytes(B.DSA_OP_INDEXER_KL, x.T, x.max_len, 0, cfg.k))
+    gl, loss = _guarded(torch.float32, (x.T,))
+    gq, dqi = _guarded(torch.float32, (x.T, cfg.H_I, cfg.D_I))
+    gw, dw = _guarded(torch.float32, (x.T, cfg.H_I))
+    gk, dk = _guarded(torch.float32, tuple(x.ik8.shape))
+    dk.zero_()
+    B.dsa_indexer_kl(p.q, p.layout, cfg.H_I, cfg.D_I, x.iq8, x.iqs, x.iw, x.ik8, x.iks, idx, cfg.k, target, loss, dqi,
+                     dw, dk, ws.bytes())
+    torch.cuda.synchronize()
+    assert ws.intact() and gl.intact() and gq.intact() and gw.intact() and gk.intact()
+    gt, tgt = _guarded(torch.float32, (x.T, cfg.k))
+    B.dsa_indexer_kl_target(p.q, p.layout, cfg.H, x.q, x.kv, idx, cfg.k, cfg.scale, lse, tgt)
+    torch.cuda.synchronize()
+    assert gt.intact()
