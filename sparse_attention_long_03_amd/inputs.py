@@ -23,7 +23,7 @@ FP8_MAX = 448.0
 _MIN_SCALE = 2.0 ** -126
 
 # tensor ids used to derive per-tensor seeds
-_T_IQ, _T_IK, _T_W, _T_Q, _T_KV, _T_LEN, _T_PAGES, _T_PLANT, _T_NQ, _T_DOUT = range(10)
+_T_IQ, _T_IK, _T_W, _T_Q, _T_KV, _T_LEN, _T_PAGES, _T_PLANT, _T_NQ, _T_DOUT, _T_SEL, _T_DIST = range(12)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -246,6 +246,35 @@ def output_grad(cfg: DSAConfig, T: int, device="cpu") -> torch.Tensor:
     N(0, 1) entries (seeded per config)."""
     dev = torch.device(device)
     return _randn_bf16_scaled((T, cfg.H, cfg.d_v), _gen(cfg.seed, _T_DOUT, dev), dev, 1.0)
+
+
+def random_selection(cfg: DSAConfig, pos: torch.Tensor, k: int, device="cpu") -> torch.Tensor:
+    """int32 [T, k]: per query t, min(k, pos[t] + 1) distinct positions drawn
+    uniformly from 0..pos[t], in random order, the rest -1 (seeded per
+    config).  A stand-in selection for steps that take any selection."""
+    dev = torch.device(device)
+    pos = pos.to(dev).long()
+    T = int(pos.shape[0])
+    L = int(pos.max()) + 1 if T else 1
+    g = _gen(cfg.seed, _T_SEL, dev)
+    out = torch.full((T, k), -1, dtype=torch.int32, device=dev)
+    for r0 in range(0, T, 256):
+        r1 = min(T, r0 + 256)
+        u = torch.rand((r1 - r0, L), generator=g, device=dev)
+        u[torch.arange(L, device=dev)[None, :] > pos[r0:r1, None]] = -1.0
+        kk = min(k, L)
+        val, sel = torch.topk(u, kk, dim=1)
+        sel = torch.where(val >= 0, sel, torch.full_like(sel, -1))
+        out[r0:r1, :kk] = sel.to(torch.int32)
+    return out
+
+
+def random_distribution(cfg: DSAConfig, idx: torch.Tensor) -> torch.Tensor:
+    """float32 [T, k]: a random probability distribution over each row's
+    entries != -1 (0 on padding), seeded per config."""
+    g = _gen(cfg.seed, _T_DIST, idx.device)
+    v = torch.rand(idx.shape, generator=g, device=idx.device) * (idx >= 0)
+    return (v / v.sum(dim=1, keepdim=True).clamp_min(1e-30)).float()
 
 
 def tie_heavy_logits(T: int, n: int, levels: int = 256, seed: int = 7, device="cpu") -> torch.Tensor:

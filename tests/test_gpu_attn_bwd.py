@@ -11,7 +11,7 @@ import oracle as O
 from sparse_attention_long_03_amd import inputs as I
 from sparse_attention_long_03_amd.path import DSAPath
 
-from parity_util import attn_bwd_magnitudes, check_bwd, np_
+from parity_util import attn_bwd_magnitudes, check_bwd, np_, oracle_selection
 
 pytestmark = pytest.mark.gpu
 
@@ -30,11 +30,11 @@ CASES = {
 
 
 def _run(x, idx=None):
+    """Forward (the attention kernel) and backward over a selection: the
+    given one, else the oracle's own top-k of its own logits."""
     p = DSAPath(x)
-    out, lse, sel = p.forward()
-    if idx is not None:
-        p.attn(idx)
-        sel = idx
+    sel = torch.from_numpy(oracle_selection(x)).to(DEV) if idx is None else idx
+    p.attn(sel)
     dO = I.output_grad(x.cfg, x.T, DEV)
     dq, dkv = p.attn_bwd(sel, dO)
     torch.cuda.synchronize()
@@ -129,7 +129,7 @@ def test_full_size_train_chunk_sampled():
     cfg = I.CONFIGS["train64k_chunk4k"]
     x = I.make_inputs(cfg, DEV)
     print(f"backward full size: T={x.T} L={cfg.L}", flush=True)
-    p, idx, dO, dq, dkv = _run(x)
+    p, idx, dO, dq, dkv = _run(x, I.random_selection(cfg, x.pos, cfg.k, DEV))
     idx_h = np_(idx)
     dO64 = dO.float().cpu().numpy().astype(np.float64)
     kv0 = x.kv[0]

@@ -32,7 +32,7 @@ CASES = {
 def test_dense_matches_sparse_and_oracle(name):
     x = I.make_inputs(CASES[name], DEV)
     p = DSAPath(x)
-    idx = p.topk(p.indexer())
+    idx = I.random_selection(x.cfg, x.pos, x.cfg.k, DEV)
     o_s, l_s = (t.clone() for t in p.attn(idx))
     o_d, l_d = p.dense_attn(idx)
     torch.cuda.synchronize()

@@ -16,7 +16,7 @@ from sparse_attention_long_03_amd import binding as B
 from sparse_attention_long_03_amd import inputs as I
 from sparse_attention_long_03_amd.path import DSAPath
 
-from parity_util import bf16_to_np, check_attn, check_selection_valid, indexer_magnitude, np_
+from parity_util import bf16_to_np, check_attn, check_selection_valid, indexer_tolerance, np_
 
 pytestmark = pytest.mark.gpu
 
@@ -125,7 +125,7 @@ def _oracle_row(x, t):
     n = int(x.pos[t]) + 1
     k8, ks = np_(x.ik8[b, :n]), np_(x.iks[b, :n]).astype(np.float64)
     qt, qst, wt = np_(x.iq8[t]), float(x.iqs[t]), np_(x.iw[t]).astype(np.float64)
-    return n, O.indexer_logits_row(qt, qst, wt, k8, ks), indexer_magnitude(qt, qst, wt, k8, ks)
+    return n, O.indexer_logits_row(qt, qst, wt, k8, ks), indexer_tolerance(qt, qst, wt, k8, ks)
 
 
 @pytest.mark.parametrize("name", ["prefill_3000", "three_sequences", "idx4x64"])
@@ -137,30 +137,39 @@ def test_fused_selection_matches_oracle(name):
         check_selection_valid(got[t], ref, n, x.cfg.k, mag)
 
 
-def _check_forward_rows(x, out, lse, idx, rows):
+def _check_forward_rows(x, p, idx, rows):
+    """Sampled rows of a many-token forward: its selection is a valid top-k
+    of the oracle's logits, and the attention kernel on the oracle's own
+    selection of those rows matches the oracle's attention (no GPU value is
+    fed to the oracle)."""
+    sel_o = np.full((x.T, x.cfg.k), -1, dtype=np.int32)
+    for t in rows:
+        n, ref, tol = _oracle_row(x, t)
+        check_selection_valid(np_(idx[t]), ref, n, x.cfg.k, tol)
+        sel_o[t] = O.topk_select(ref, n, x.cfg.k)
+    out_o, lse_o = p.attn(torch.from_numpy(sel_o).to(DEV))
+    torch.cuda.synchronize()
     for t in rows:
         b = int(x.seq_id[t])
-        n, ref, mag = _oracle_row(x, t)
-        sel = np_(idx[t])
-        check_selection_valid(sel, ref, n, x.cfg.k, mag)
-        got = sel[sel >= 0]
+        got = sel_o[t][sel_o[t] >= 0]
         kv = I.bf16_bits(x.kv[b][torch.as_tensor(got, dtype=torch.int64, device=DEV)])
         ro, rl = O.sparse_mla_attention(I.bf16_bits(x.q[t:t + 1]), kv[None], np.arange(len(got))[None],
                                         np.zeros(1, int), x.cfg.scale)
-        check_attn(bf16_to_np(out[t:t + 1]), ro, f"{x.cfg.name} query {t}")
-        np.testing.assert_allclose(np_(lse[t]), rl[0], rtol=1e-4, atol=1e-4)
+        check_attn(bf16_to_np(out_o[t:t + 1]), ro, f"{x.cfg.name} query {t}")
+        np.testing.assert_allclose(np_(lse_o[t]), rl[0], rtol=1e-4, atol=1e-4)
 
 
 def test_forward_many_tokens_uses_fused_selection():
     x = I.make_inputs(FUSED["prefill_3000"], DEV)
     assert x.T >= 2048  # dsa_forward takes the fused branch
     p = DSAPath(x)
-    out, lse, idx = p.forward()
+    out, lse, idx = [t.clone() for t in p.forward()]
     fused = p.indexer_topk()
     assert np.array_equal(np_(idx), np_(fused))
-    out_a, _ = p.attn(fused)
+    out_a, lse_a = p.attn(fused)
     assert torch.equal(out.view(torch.int16), out_a.view(torch.int16))
-    _check_forward_rows(x, out, lse, idx, [0, 100, 255, 256, 1500, x.T - 1])
+    assert torch.equal(lse.view(torch.int32), lse_a.view(torch.int32))
+    _check_forward_rows(x, p, idx, [0, 100, 255, 256, 1500, x.T - 1])
 
 
 def test_forward_many_tokens_ignores_workspace_contents():
@@ -180,6 +189,9 @@ def test_forward_many_tokens_ignores_workspace_contents():
 def test_full_size_prefill64k_sampled():
     x = I.make_inputs(I.CONFIGS["prefill64k"], DEV)
     p = DSAPath(x)
-    out, lse, idx = p.forward()
+    out, lse, idx = [t.clone() for t in p.forward()]
     torch.cuda.synchronize()
-    _check_forward_rows(x, out, lse, idx, [0, 2046, 2047, 2048, 40000, x.T - 1])
+    _check_forward_rows(x, p, idx, [0, 2046, 2047, 2048, 40000, x.T - 1])
+    # the forward is the fused selection followed by the attention kernel
+    out_a, lse_a = p.attn(idx)
+    assert torch.equal(out.view(torch.int16), out_a.view(torch.int16))

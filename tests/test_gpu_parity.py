@@ -10,7 +10,7 @@ from sparse_attention_long_03_amd import inputs as I
 from sparse_attention_long_03_amd.path import DSAPath
 
 from parity_util import (bf16_to_np, check_attn, check_logits, check_selection_valid, host_inputs,
-                         indexer_magnitude, np_)
+                         indexer_tolerance, np_)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,16 +39,16 @@ def _oracle_logits(h):
     return O.indexer_logits(h["iq8"], h["iqs"], h["iw"], h["ik8"], h["iks"], h["seq_id"], h["pos"], h["bt"])
 
 
-def _magnitudes(h):
-    """Per-query term magnitudes M (tolerance floor of the indexer)."""
-    mags = []
+def _tolerances(h):
+    """Per-query logit tolerances (from the FP8 accumulation bound)."""
+    tols = []
     for t in range(len(h["pos"])):
         n = int(h["pos"][t]) + 1
         b = int(h["seq_id"][t])
         k8 = O.logical_rows(h["ik8"], b, n, h["bt"])
         ks = O.logical_rows(h["iks"], b, n, h["bt"])
-        mags.append(indexer_magnitude(h["iq8"][t], h["iqs"][t], h["iw"][t], k8, ks))
-    return mags
+        tols.append(indexer_tolerance(h["iq8"][t], h["iqs"][t], h["iw"][t], k8, ks))
+    return tols
 
 
 # ----------------------------------------------------------------- indexer
@@ -61,10 +61,10 @@ def test_indexer_matches_oracle(name):
     torch.cuda.synchronize()
     h = host_inputs(x)
     ref = _oracle_logits(h)
-    mags = _magnitudes(h)
+    tols = _tolerances(h)
     for t in range(x.T):
         n = int(h["pos"][t]) + 1
-        check_logits(lg[t, :n], ref[t, :n], mags[t], f"{name} row {t}")
+        check_logits(lg[t, :n], ref[t, :n], tols[t], f"{name} row {t}")
 
 
 # ----------------------------------------------------------------- top-k
@@ -175,20 +175,44 @@ def test_attention_padding_and_empty_rows():
 
 # ----------------------------------------------------------------- whole path
 
+def _check_forward_against_parts(p, out, lse, idx):
+    """dsa_forward equals its separate GPU calls: its selection is dsa_topk's
+    on dsa_indexer_logits' logits (same order), and its output and lse are
+    dsa_sparse_mla_attn's on that selection, bit for bit."""
+    sep = p.topk(p.indexer())
+    out_s, lse_s = p.attn(sep)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, sep)
+    assert torch.equal(out.view(torch.int16), out_s.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse_s.view(torch.int32))
+
+
 @pytest.mark.parametrize("name", ["tiny", "decode_ragged", "paged_small"])
 def test_forward_end_to_end(name):
+    """The whole path against the oracle, with no GPU value fed to the
+    oracle: the forward's selection is a valid top-k of the oracle's logits,
+    the attention kernel on the oracle's own selection matches the oracle's
+    attention, and the forward is the composition of its GPU parts."""
     x = _inputs(name)
     h = host_inputs(x)
     p = DSAPath(x)
-    out, lse, idx = p.forward()
-    out, idx = bf16_to_np(out), np_(idx)
+    out, lse, idx = [t.clone() for t in p.forward()]
+    idx_h = np_(idx)
     ref = _oracle_logits(h)
-    mags = _magnitudes(h)
+    tols = _tolerances(h)
+    sel_o = np.full((x.T, x.cfg.k), -1, dtype=np.int32)
+    same = 0
     for t in range(x.T):
         n = int(h["pos"][t]) + 1
-        check_selection_valid(idx[t], ref[t], n, x.cfg.k, mags[t])
-    ro, _ = O.sparse_mla_attention(h["q"], h["kv"], idx, h["seq_id"], x.cfg.scale, 512, h["bt"])
-    check_attn(out, ro, name)
+        check_selection_valid(idx_h[t], ref[t], n, x.cfg.k, tols[t])
+        sel_o[t] = O.topk_select(ref[t, :n], n, x.cfg.k)
+        same += int(np.array_equal(np.sort(idx_h[t]), np.sort(sel_o[t])))
+    print(f"{name}: {same} of {x.T} forward selections equal the oracle's", flush=True)
+    out_o, lse_o = p.attn(torch.from_numpy(sel_o).to(DEV))
+    ro, rl = O.sparse_mla_attention(h["q"], h["kv"], sel_o, h["seq_id"], x.cfg.scale, 512, h["bt"])
+    check_attn(bf16_to_np(out_o), ro, name)
+    np.testing.assert_allclose(np_(lse_o), rl, rtol=1e-4, atol=1e-4)
+    _check_forward_against_parts(p, out, lse, idx)
 
 
 def test_forward_is_deterministic():
@@ -277,24 +301,31 @@ def _sampled_full_size(cfg_name, sample_t):
     x = I.make_inputs(I.CONFIGS[cfg_name], DEV)
     p = DSAPath(x)
     logits = p.indexer()
-    out, lse, idx = p.forward()
+    out, lse, idx = [t.clone() for t in p.forward()]
     torch.cuda.synchronize()
+    sel_o = np.full((x.T, x.cfg.k), -1, dtype=np.int32)
     for t in sample_t:
         b = int(x.seq_id[t])
         n = int(x.pos[t]) + 1
         k8, ks = _key_rows_host(x, b, n)
         qt, qst, wt = np_(x.iq8[t]), float(x.iqs[t]), np_(x.iw[t]).astype(np.float64)
         ref = O.indexer_logits_row(qt, qst, wt, k8, ks)
-        mag = indexer_magnitude(qt, qst, wt, k8, ks)
-        check_logits(np_(logits[t, :n]), ref, mag, f"{cfg_name} row {t}")
-        sel = np_(idx[t])
-        check_selection_valid(sel, ref, n, x.cfg.k, mag)
-        got = sel[sel >= 0]
+        tol = indexer_tolerance(qt, qst, wt, k8, ks)
+        check_logits(np_(logits[t, :n]), ref, tol, f"{cfg_name} row {t}")
+        check_selection_valid(np_(idx[t]), ref, n, x.cfg.k, tol)
+        sel_o[t] = O.topk_select(ref, n, x.cfg.k)
+    # the attention kernel on the oracle's selections of the sampled queries
+    out_o, lse_o = p.attn(torch.from_numpy(sel_o).to(DEV))
+    torch.cuda.synchronize()
+    for t in sample_t:
+        b = int(x.seq_id[t])
+        got = sel_o[t][sel_o[t] >= 0]
         rows = _gather_rows_host(x, b, got)
         ro, rl = O.sparse_mla_attention(I.bf16_bits(x.q[t:t + 1]), rows[None], np.arange(len(got))[None],
                                         np.zeros(1, int), x.cfg.scale)
-        check_attn(bf16_to_np(out[t:t + 1]), ro, f"{cfg_name} query {t}")
-        np.testing.assert_allclose(np_(lse[t]), rl[0], rtol=1e-4, atol=1e-4)
+        check_attn(bf16_to_np(out_o[t:t + 1]), ro, f"{cfg_name} query {t}")
+        np.testing.assert_allclose(np_(lse_o[t]), rl[0], rtol=1e-4, atol=1e-4)
+    _check_forward_against_parts(p, out, lse, idx)
     return x, idx
 
 
@@ -324,3 +355,71 @@ def test_topk_threshold_bin_larger_than_lds():
     workspace instead)."""
     w = np.floor(I.tie_heavy_logits(2, 131072, seed=22).numpy() / 64.0).astype(np.float32)
     _topk_case(w, [131072, 100000], 2048)
+
+
+# ----------------------------------------------------------------- forward's own selection
+
+def _repeat_key_rows(x, period):
+    """Index-key rows repeat with the given period along each sequence, so
+    the logits of a row repeat and most rows tie at the k-th value."""
+    if x.block_table is None:
+        s = torch.arange(x.ik8.shape[1], device=DEV) % period
+        x.ik8[:] = x.ik8[:, s]
+        x.iks[:] = x.iks[:, s]
+        return x
+    bt = x.block_table.long()
+    for b in range(bt.shape[0]):
+        n = int(x.seq_lens[b])
+        npg = -(-n // 64)
+        s = torch.arange(npg * 64, device=DEV)
+        src = s % period
+        pages, rows = bt[b, s // 64], s % 64
+        x.ik8[pages, rows] = x.ik8[bt[b, src // 64], src % 64]
+        x.iks[pages, rows] = x.iks[bt[b, src // 64], src % 64]
+    return x
+
+
+@pytest.mark.parametrize("name,period", [("decode_ragged", None), ("paged_small", None), ("paged_small", 37),
+                                         ("decode_ragged", 61)])
+def test_forward_selection_equals_separate_calls(name, period):
+    """dsa_forward's decode branch builds the first radix level in the
+    indexer's epilogue; its selection must equal dsa_topk (which builds its
+    own histogram) on dsa_indexer_logits' logits, bit for bit and in the same
+    order, also when the forward's own logits tie at the k-th value."""
+    x = _inputs(name)
+    if period is not None:
+        x = _repeat_key_rows(x, period)
+    p = DSAPath(x)
+    out, lse, idx = [t.clone() for t in p.forward()]
+    _check_forward_against_parts(p, out, lse, idx)
+    if period is not None:
+        lg = np_(p.indexer())
+        ties = 0
+        for t in range(x.T):
+            n = int(x.pos[t]) + 1
+            if n > x.cfg.k:
+                kth = np.sort(lg[t, :n])[::-1][x.cfg.k - 1]
+                ties += int((lg[t, :n] == kth).sum() > 1)
+        assert ties > 0, "no row ties at the k-th value"
+
+
+def test_topk_workspace_sized_by_max_len():
+    """The top-k workspace is sized from the longest valid row, whatever the
+    row stride: rows of 4097 values stored 8196 apart run in exactly
+    dsa_workspace_bytes(DSA_OP_TOPK, T, 4097, 0, k) bytes."""
+    T, n, ld, k = 3, 4097, 8196, 2048
+    v = I.tie_heavy_logits(T, n, seed=21).numpy()
+    lg = torch.full((T, ld), 1e30, dtype=torch.float32)   # past the valid length: never read
+    lg[:, :n] = torch.from_numpy(v)
+    lg = lg.to(DEV)
+    valid = [n, n - 1, 3000]
+    vl = torch.tensor(valid, dtype=torch.int32, device=DEV)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    nbytes = B.dsa_workspace_bytes(B.DSA_OP_TOPK, T, n, 0, k)
+    assert nbytes < B.dsa_workspace_bytes(B.DSA_OP_TOPK, T, ld, 0, k)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    B.dsa_topk(lg, vl, n, k, idx, ws)
+    got = np_(idx)
+    for t in range(T):
+        ref = O.topk_select(v[t], valid[t], k)
+        assert np.array_equal(np.sort(got[t]), np.sort(ref)), f"row {t}"
