@@ -18,13 +18,17 @@
  *   before the call returns.
  * - The caller owns every buffer, including workspaces.  The library
  *   allocates no memory and keeps no state between calls, so it is
- *   re-entrant; calls on one stream run in order.
+ *   re-entrant; calls on one stream run in order.  The one exception is
+ *   dsa_forward_noalloc, whose workspace is a static array of the library
+ *   (one per GPU; see there).
  * - Every call only enqueues work on `stream` and returns; nothing waits.
  * - Errors: each call returns DSA_OK (0) or a negative DSA_ERR_* code and
  *   enqueues nothing when it fails validation.  Validation covers host-side
  *   scalars, null pointers, alignment and workspace size.  The contents of
  *   device index arrays (seq_id, pos, valid_len, idx, block_table) are
- *   trusted: out-of-range values there are undefined behaviour.
+ *   trusted: out-of-range values there are undefined behaviour (the indexer
+ *   and the selection clamp pos[t] and valid lengths to max_len, so those
+ *   never write past their rows).
  * - All tensors are dense, row-major, with the strides stated per argument.
  * - Key positions are logical token positions within a sequence (0-based),
  *   so results do not depend on whether the caches are paged.
@@ -49,6 +53,7 @@ extern "C" {
 #define DSA_ERR_UNSUPPORTED (-2) /* valid request outside the built shapes       */
 #define DSA_ERR_WORKSPACE (-3)   /* workspace missing or smaller than required    */
 #define DSA_ERR_HIP (-4)         /* a HIP launch reported an error                */
+#define DSA_ERR_SCRATCH_LIMIT (-5) /* dsa_forward_noalloc: request larger than its static scratch */
 
 /* Query tokens.  Query t belongs to sequence seq_id[t] and sits at logical
  * position pos[t]; it sees the tokens 0..pos[t] of its sequence (its own
@@ -315,6 +320,27 @@ int dsa_forward(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, 
                 const float* ik_scale, int32_t H, const void* q_bf16, const void* kv_bf16, int32_t k,
                 float sm_scale, void* out_bf16, float* lse, int32_t* idx_out, void* workspace,
                 size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * dsa_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Arguments, results and errors as for dsa_forward;
+ * the workspace is a static device array inside the library, one copy per GPU
+ * of DSA_NOALLOC_SCRATCH_BYTES (64 MiB), held from the first call on that GPU
+ * until the process ends.  The call allocates nothing; it returns
+ * DSA_ERR_SCRATCH_LIMIT, enqueuing nothing, when the request needs more than
+ * the scratch holds (dsa_workspace_bytes(DSA_OP_FORWARD, ...) bytes, less
+ * T * k * 4 when idx_out is given) -- in practice decode batches below 2048
+ * query tokens, e.g. 16 queries of 128K positions (about 45 MB).  Every call
+ * on a GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams, other host threads) race and must be serialised by the caller.
+ * The current device must be the one the stream and buffers belong to.
+ * ------------------------------------------------------------------------- */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int dsa_forward_noalloc(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,
+                        const uint8_t* iq_fp8, const float* iq_scale, const float* iw, const uint8_t* ik_fp8,
+                        const float* ik_scale, int32_t H, const void* q_bf16, const void* kv_bf16, int32_t k,
+                        float sm_scale, void* out_bf16, float* lse, int32_t* idx_out, hipStream_t stream);
 
 /* Workspace sizes (bytes) for an operation; 0 when none is needed. */
 #define DSA_OP_TOPK 1

@@ -22,6 +22,7 @@ DSA_ERR_INVALID_ARG = -1
 DSA_ERR_UNSUPPORTED = -2
 DSA_ERR_WORKSPACE = -3
 DSA_ERR_HIP = -4
+DSA_ERR_SCRATCH_LIMIT = -5
 DSA_OP_TOPK, DSA_OP_ATTN, DSA_OP_FORWARD, DSA_OP_INDEXER_TOPK, DSA_OP_DENSE_ATTN, DSA_OP_ATTN_BWD = 1, 2, 3, 4, 5, 6
 DSA_OP_INDEXER_KL = 7
 
@@ -44,7 +45,8 @@ class dsa_kv_layout(ctypes.Structure):
 
 EXPORTS = ("dsa_cache_write", "dsa_indexer_logits", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_attn",
            "dsa_sparse_mla_attn_bwd", "dsa_sparse_mla_attn_bwd_dq", "dsa_sparse_mla_attn_bwd_dkv",
-           "dsa_indexer_kl_target", "dsa_indexer_kl", "dsa_masked_dense_attn", "dsa_forward", "dsa_workspace_bytes",
+           "dsa_indexer_kl_target", "dsa_indexer_kl", "dsa_masked_dense_attn", "dsa_forward", "dsa_forward_noalloc",
+           "dsa_workspace_bytes",
            "dsa_status_str", "dsa_abi_version")
 
 _lib = None
@@ -72,13 +74,15 @@ def lib() -> ctypes.CDLL:
     L.dsa_indexer_kl.argtypes = [Q, KV, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_masked_dense_attn.argtypes = [Q, KV, i32, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
     L.dsa_forward.argtypes = [Q, KV, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]
+    L.dsa_forward_noalloc.argtypes = [Q, KV, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, i32, f32, vp, vp, vp, vp]
     L.dsa_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     L.dsa_workspace_bytes.restype = sz
     L.dsa_status_str.argtypes = [i32]
     L.dsa_status_str.restype = ctypes.c_char_p
     L.dsa_abi_version.restype = i32
     for name in ("dsa_cache_write", "dsa_indexer_logits", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_attn",
-                 "dsa_sparse_mla_attn_bwd", "dsa_sparse_mla_attn_bwd_dq", "dsa_sparse_mla_attn_bwd_dkv", "dsa_masked_dense_attn", "dsa_forward"):
+                 "dsa_sparse_mla_attn_bwd", "dsa_sparse_mla_attn_bwd_dq", "dsa_sparse_mla_attn_bwd_dkv", "dsa_masked_dense_attn", "dsa_forward",
+                 "dsa_forward_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -244,3 +248,12 @@ def dsa_forward(q: dsa_queries, layout: dsa_kv_layout, H_I: int, D_I: int, iq_fp
                            _ptr(ik_fp8), _ptr(ik_scale), H, _ptr(q_bf16), _ptr(kv_bf16), int(k), float(sm_scale),
                            _ptr(out_bf16), _ptr(lse), _ptr(idx_out), _ptr(ws), nbytes, _stream(stream))
     _check(st, "dsa_forward")
+
+
+def dsa_forward_noalloc(q: dsa_queries, layout: dsa_kv_layout, H_I: int, D_I: int, iq_fp8, iq_scale, iw, ik_fp8,
+                        ik_scale, H: int, q_bf16, kv_bf16, k: int, sm_scale: float, out_bf16, lse=None, idx_out=None,
+                        stream=None):
+    st = lib().dsa_forward_noalloc(ctypes.byref(q), ctypes.byref(layout), H_I, D_I, _ptr(iq_fp8), _ptr(iq_scale),
+                                   _ptr(iw), _ptr(ik_fp8), _ptr(ik_scale), H, _ptr(q_bf16), _ptr(kv_bf16), int(k),
+                                   float(sm_scale), _ptr(out_bf16), _ptr(lse), _ptr(idx_out), _stream(stream))
+    _check(st, "dsa_forward_noalloc")

@@ -7,6 +7,8 @@
 // (1) the lightning indexer's logits, (2) the top-k selection and the
 // attention over the selected entries, under MLA in MQA mode
 // ("Instantiation").
+#include <mutex>
+
 #include "dsa.h"
 #include "launch.h"
 
@@ -118,6 +120,7 @@ const char* dsa_status_str(int32_t status) {
     case DSA_ERR_UNSUPPORTED: return "unsupported shape or option";
     case DSA_ERR_WORKSPACE: return "workspace missing or too small";
     case DSA_ERR_HIP: return "HIP launch error";
+    case DSA_ERR_SCRATCH_LIMIT: return "request exceeds the no-allocation entry point's static scratch (64 MiB per GPU)";
     default: return "unknown status";
   }
 }
@@ -332,15 +335,24 @@ int dsa_indexer_kl(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_
                               dq, dw, dk, workspace, stream));
 }
 
-int dsa_forward(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,
-                const uint8_t* iq_fp8, const float* iq_scale, const float* iw, const uint8_t* ik_fp8,
-                const float* ik_scale, int32_t H, const void* q_bf16, const void* kv_bf16, int32_t k,
-                float sm_scale, void* out_bf16, float* lse, int32_t* idx_out, void* workspace,
-                size_t workspace_bytes, hipStream_t stream) {
-  Layout lay;
+}  // extern "C"
+
+// The static scratch of dsa_forward_noalloc: one copy per GPU, held until the
+// process ends.  Host code never uses the symbol's name as an address: the
+// device address of each GPU's copy comes from hipGetSymbolAddress, taken once
+// per device with that device current, and kept per device below.
+static __device__ __align__(256) unsigned char scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// dsa_forward's argument checks, shared with dsa_forward_noalloc.  Fills lay.
+int validate_forward(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,
+                     const uint8_t* iq_fp8, const float* iq_scale, const float* iw, const uint8_t* ik_fp8,
+                     const float* ik_scale, int32_t H, const void* q_bf16, const void* kv_bf16, int32_t k,
+                     float sm_scale, const void* out_bf16, Layout* lay) {
   int st = check_queries(q);
   if (st) return st;
-  if ((st = check_layout(layout, q, &lay))) return st;
+  if ((st = check_layout(layout, q, lay))) return st;
   if (H_I < 1 || D_I < 1 || H < 1 || k < 1) return DSA_ERR_INVALID_ARG;
   if (!(sm_scale > 0.f)) return DSA_ERR_INVALID_ARG;
   if (!indexer_supported(H_I, D_I) || !attn_supported(H) || k > kMaxK) return DSA_ERR_UNSUPPORTED;
@@ -350,10 +362,16 @@ int dsa_forward(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, 
   if (!aligned(iq_fp8, 16) || !aligned(ik_fp8, 16) || !aligned(q_bf16, 16) || !aligned(kv_bf16, 16) ||
       !aligned(out_bf16, 16))
     return DSA_ERR_INVALID_ARG;
-  const int64_t ld = ((int64_t)q->max_len + 3) & ~int64_t(3);
-  const size_t need = forward_ws(q->T, q->max_len, H, k, idx_out == nullptr);
-  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)) return DSA_ERR_WORKSPACE;
+  return DSA_OK;
+}
 
+// (1) -> (2) -> (3) over a workspace of at least forward_ws(...) bytes
+// (validated arguments).
+int run_forward(const dsa_queries* q, const Layout& lay, int32_t H_I, int32_t D_I, const uint8_t* iq_fp8,
+                const float* iq_scale, const float* iw, const uint8_t* ik_fp8, const float* ik_scale, int32_t H,
+                const void* q_bf16, const void* kv_bf16, int32_t k, float sm_scale, void* out_bf16, float* lse,
+                int32_t* idx_out, void* workspace, hipStream_t stream) {
+  const int64_t ld = ((int64_t)q->max_len + 3) & ~int64_t(3);
   char* p = static_cast<char*>(workspace);
   int32_t* idx = idx_out;
   if (idx == nullptr) {
@@ -366,8 +384,8 @@ int dsa_forward(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, 
     const int cap = fused_topk_cap(q->max_len, k);
     void* ws_sel = p;
     p += align256(fused_topk_workspace_bytes(q->T, cap));
-    e = launch_indexer_topk(q->T, q->max_len, H_I, D_I, iq_fp8, iq_scale, iw, ik_fp8, ik_scale, q->seq_id, q->pos, lay, k, cap,
-                            idx, ws_sel, stream);
+    e = launch_indexer_topk(q->T, q->max_len, H_I, D_I, iq_fp8, iq_scale, iw, ik_fp8, ik_scale, q->seq_id, q->pos,
+                            lay, k, cap, idx, ws_sel, stream);
     if (e != hipSuccess) return DSA_ERR_HIP;
   } else {
     float* logits = reinterpret_cast<float*>(p);
@@ -386,6 +404,58 @@ int dsa_forward(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, 
   e = launch_attn(q->T, H, static_cast<const uint16_t*>(q_bf16), static_cast<const uint16_t*>(kv_bf16), idx, q->seq_id,
                   lay, k, sm_scale, static_cast<uint16_t*>(out_bf16), lse, ws_attn, stream);
   return hip_status(e);
+}
+
+constexpr size_t kScratchBytes = DSA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DSA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return DSA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_forward(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,
+                const uint8_t* iq_fp8, const float* iq_scale, const float* iw, const uint8_t* ik_fp8,
+                const float* ik_scale, int32_t H, const void* q_bf16, const void* kv_bf16, int32_t k,
+                float sm_scale, void* out_bf16, float* lse, int32_t* idx_out, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  Layout lay;
+  int st = validate_forward(q, layout, H_I, D_I, iq_fp8, iq_scale, iw, ik_fp8, ik_scale, H, q_bf16, kv_bf16, k,
+                            sm_scale, out_bf16, &lay);
+  if (st || q->T == 0) return st;
+  const size_t need = forward_ws(q->T, q->max_len, H, k, idx_out == nullptr);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)) return DSA_ERR_WORKSPACE;
+  return run_forward(q, lay, H_I, D_I, iq_fp8, iq_scale, iw, ik_fp8, ik_scale, H, q_bf16, kv_bf16, k, sm_scale,
+                     out_bf16, lse, idx_out, workspace, stream);
+}
+
+int dsa_forward_noalloc(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,
+                        const uint8_t* iq_fp8, const float* iq_scale, const float* iw, const uint8_t* ik_fp8,
+                        const float* ik_scale, int32_t H, const void* q_bf16, const void* kv_bf16, int32_t k,
+                        float sm_scale, void* out_bf16, float* lse, int32_t* idx_out, hipStream_t stream) {
+  Layout lay;
+  int st = validate_forward(q, layout, H_I, D_I, iq_fp8, iq_scale, iw, ik_fp8, ik_scale, H, q_bf16, kv_bf16, k,
+                            sm_scale, out_bf16, &lay);
+  if (st || q->T == 0) return st;
+  if (forward_ws(q->T, q->max_len, H, k, idx_out == nullptr) > kScratchBytes) return DSA_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  if ((st = scratch_for_current_device(&ws))) return st;
+  return run_forward(q, lay, H_I, D_I, iq_fp8, iq_scale, iw, ik_fp8, ik_scale, H, q_bf16, kv_bf16, k, sm_scale,
+                     out_bf16, lse, idx_out, ws, stream);
 }
 
 }  // extern "C"

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert B.dsa_abi_version() == 1
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert B.dsa_status_str(code) != "unknown status"
     assert B.dsa_status_str(-99) == "unknown status"
 
@@ -259,3 +259,24 @@ def test_indexer_kl_validation(lib):
     assert call(ws=None) == B.DSA_ERR_WORKSPACE
     assert call(nbytes=need - 1) == B.DSA_ERR_WORKSPACE
     assert call(q_=_q(T=0, seq=None, pos=None), ptrs=[None] * 11, ws=None, nbytes=0) == B.DSA_OK
+
+
+def test_forward_noalloc_validation(lib):
+    """The no-allocation forward checks its arguments like dsa_forward and
+    rejects a request larger than its static scratch before any HIP call."""
+    f = lib.dsa_forward_noalloc
+    lay = _lay(1 << 17)
+
+    def call(q_=None, H_I=64, H=128, k=2048, out=FAKE, **kw):
+        q_ = q_ or _q(T=4, max_len=1000)
+        return f(ctypes.byref(q_), ctypes.byref(lay), H_I, 128, FAKE, FAKE, FAKE, FAKE, FAKE, H, FAKE, FAKE, k, 0.04,
+                 out, None, None, None)
+
+    assert call(H_I=8) == B.DSA_ERR_UNSUPPORTED
+    assert call(k=0) == B.DSA_ERR_INVALID_ARG
+    assert call(out=None) == B.DSA_ERR_INVALID_ARG
+    assert call(q_=_q(T=0, seq=None, pos=None)) == B.DSA_OK
+    # 64 decode queries of 128K positions need more than the 64 MiB scratch
+    assert B.dsa_workspace_bytes(B.DSA_OP_FORWARD, 64, 1 << 17, 128, 2048) > (64 << 20)
+    assert call(q_=_q(T=64, max_len=1 << 17)) == B.DSA_ERR_SCRATCH_LIMIT
+    assert "static scratch" in B.dsa_status_str(B.DSA_ERR_SCRATCH_LIMIT)
