@@ -73,6 +73,8 @@ def parse():
     ap.add_argument("--kl", action="store_true",
                     help="with --config train64k_chunk4k: time the indexer's KL training signal instead of the "
                          "attention backward")
+    ap.add_argument("--proj", action="store_true",
+                    help="time the indexer projection (hidden states -> FP8 query + scale, head weights, index key)")
     ap.add_argument("--crossover", action="store_true",
                     help="time the masked dense attention against the sparse gather over context lengths")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -473,6 +475,63 @@ def bench_crossover(args):
                       "n_gpus": 1, "data": "synthetic", "series": series}), flush=True)
 
 
+def bench_projection(args):
+    """The indexer's inputs from hidden states (dsa_indexer_project): per
+    token, q = Wq h (64 heads x 128, then FP8 with a per-token scale),
+    w = Ww h and the token's index key k = Wk h, from bf16 h and weights.
+    The hidden width is 7168 (the pages leave d open; this is the width of
+    the model family they describe).  Decode (16 tokens) streams the 120 MB
+    of weights: bound by HBM, with four weight replicas in rotation so that no
+    launch finds them in the 256 MB MALL (one per layer in a model).  A
+    4096-token chunk is bound by the bf16 matrix cores."""
+    import torch
+    from sparse_attention_long_03_amd import binding as B
+
+    d, H_I, D_I = 7168, 64, 128
+    N = H_I * D_I + H_I + D_I
+    stream = torch.cuda.current_stream()
+    g = torch.Generator(device="cuda").manual_seed(5)
+    mk = lambda *shape, s=1.0: (torch.randn(shape, generator=g, device="cuda") * s).to(torch.bfloat16)
+    weights = [(mk(H_I * D_I, d, s=d ** -0.5), mk(H_I, d, s=d ** -0.5), mk(D_I, d, s=d ** -0.5))
+               for _ in range(REPLICAS)]
+    res = {}
+    n_launch = max(args.steps, 20)
+    for T in (16, 4096):
+        h = mk(T, d)
+        q8 = torch.empty((T, H_I, D_I), dtype=torch.uint8, device="cuda")
+        qs = torch.empty((T,), dtype=torch.float32, device="cuda")
+        w = torch.empty((T, H_I), dtype=torch.float32, device="cuda")
+        k = torch.empty((T, D_I), dtype=torch.float32, device="cuda")
+        ws = B.workspace(B.dsa_workspace_bytes(B.DSA_OP_INDEXER_PROJ, T, d, H_I, D_I))
+        fns = [(lambda wq=wq, ww=ww, wk=wk: B.dsa_indexer_project(d, H_I, D_I, h, wq, ww, wk, q8, qs, w, k, ws))
+               for wq, ww, wk in weights]
+        timed_rotation(fns, 2 * REPLICAS, stream)
+        avg = batch_rotation(fns, n_launch, stream)
+        ts = timed_rotation(fns, n_launch, stream)
+        nbytes = N * d * 2 + T * d * 2 + T * (H_I * D_I + 4 + 4 * H_I + 4 * D_I)
+        flops = 2 * T * d * N
+        res[f"T{T}"] = {"us": round(avg * 1e3, 2), "p10_us": round(sorted(ts)[len(ts) // 10] * 1e3, 2),
+                        "p90_us": round(sorted(ts)[(9 * len(ts)) // 10] * 1e3, 2),
+                        "gbs": round(nbytes / (avg * 1e-3) / 1e9, 1),
+                        "frac_hbm": round(nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "tflops": round(flops / (avg * 1e-3) / 1e12, 1),
+                        "frac_bf16": round(flops / (avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                        "bytes_per_launch": nbytes, "flops_per_launch": flops}
+        del h, q8, qs, w, k, ws, fns
+    dec = res["T16"]
+    out = {"metric": "indexer projection tokens/s (hidden 7168 -> FP8 query 64x128 + scale, 64 weights, 128-wide key)",
+           "value": round(16 / (dec["us"] * 1e-6), 1), "unit": "tokens/s", "n_gpus": 1, "steps": n_launch,
+           "warmup": 2 * REPLICAS, "higher_is_better": True, "dtype": "bf16 MFMA, fp32 accumulate; FP8 query codes",
+           "data": "synthetic",
+           "config": {"workload": "decode step of 16 tokens (4 weight replicas in rotation) and a 4096-token chunk",
+                      "d": d, "H_I": H_I, "D_I": D_I},
+           "roofline": {"bound": "hbm", "kernel": "proj_gemm_kernel<16> + proj_finish_kernel<32>",
+                        "achieved": dec["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec["frac_hbm"],
+                        "traffic": None, "bytes_per_launch": dec["bytes_per_launch"], "avg_launch_us": dec["us"]},
+           "points": res}
+    print(json.dumps(out), flush=True)
+
+
 def stream_copy_gbs():
     """Measured device-to-device copy bandwidth on this GPU: a 1 GiB buffer
     (four times the 256 MB MALL) copied with torch, read + written bytes over
@@ -533,6 +592,9 @@ def main():
     torch.cuda.set_device(0)
     if args.crossover:
         bench_crossover(args)
+        return
+    if args.proj:
+        bench_projection(args)
         return
     cfg = I.CONFIGS[args.config]
     if cfg.kind == "prefill":

@@ -107,6 +107,36 @@ int dsa_cache_write(const dsa_queries* q, const dsa_kv_layout* layout, int32_t D
                     const void* kv_new_bf16, uint8_t* k_fp8, float* k_scale, void* kv_bf16, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * (0b) The indexer's inputs from the tokens' hidden states ("... Sparse
+ * Consideration (DSA)", part (1): for each query token h_t the indexer forms
+ * a few small heads and one weight per head; each token also has its own
+ * index key).  The pages give no formula; the reading is plain linear maps
+ * without bias, accumulated in fp32 on the matrix cores from bf16 inputs:
+ *     q[t, j, c] = sum_i Wq[j * D_I + c, i] * h[t, i]     (head-major rows)
+ *     w[t, j]    = sum_i Ww[j, i] * h[t, i]
+ *     k[t, c]    = sum_i Wk[c, i] * h[t, i]                (optional)
+ * The query is then quantised per token exactly as dsa_cache_write quantises
+ * a key, over all of its H_I * D_I values: q_scale[t] = max(amax / 448,
+ * 2^-126), q_fp8 = e4m3fn(clamp(q / q_scale, +-448)), ties to even -- the
+ * q_fp8 / q_scale that dsa_indexer_logits takes.  k is the float32 key that
+ * dsa_cache_write stores.
+ *
+ *   T, d      : tokens >= 0; hidden width d, a multiple of 64, <= 65536
+ *   H_I, D_I  : as for dsa_indexer_logits
+ *   h_bf16    : device bf16[T, d]                 (16-byte aligned)
+ *   wq_bf16   : device bf16[H_I * D_I, d]         (16-byte aligned)
+ *   ww_bf16   : device bf16[H_I, d]               (16-byte aligned)
+ *   wk_bf16   : device bf16[D_I, d] or NULL       (16-byte aligned)
+ *   q_fp8     : device uint8[T, H_I, D_I] (16-byte aligned); q_scale : device float[T]
+ *   w         : device float[T, H_I];  k_new : device float[T, D_I], NULL iff wk_bf16 is
+ *   workspace : device, >= dsa_workspace_bytes(DSA_OP_INDEXER_PROJ, T, d, H_I, D_I),
+ *               256-byte aligned (fp32 partial sums of the projection)
+ * ------------------------------------------------------------------------- */
+int dsa_indexer_project(int32_t T, int32_t d, int32_t H_I, int32_t D_I, const void* h_bf16, const void* wq_bf16,
+                        const void* ww_bf16, const void* wk_bf16, uint8_t* q_fp8, float* q_scale, float* w,
+                        float* k_new, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * (1) Lightning indexer logits.
  *   logits[t * ld_logits + s] =
  *       q_scale[t] * k_scale[s] * sum_j w[t,j] * ReLU( sum_d q[t,j,d] * k[s,d] )
@@ -350,6 +380,7 @@ int dsa_forward_noalloc(const dsa_queries* q, const dsa_kv_layout* layout, int32
 #define DSA_OP_DENSE_ATTN 5
 #define DSA_OP_ATTN_BWD 6
 #define DSA_OP_INDEXER_KL 7
+#define DSA_OP_INDEXER_PROJ 8 /* arguments (T, d, H_I, D_I) in place of (T, max_len, H, k) */
 size_t dsa_workspace_bytes(int32_t op, int32_t T, int32_t max_len, int32_t H, int32_t k);
 
 /* Static string for a status code (never NULL). */

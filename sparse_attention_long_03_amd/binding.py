@@ -25,6 +25,7 @@ DSA_ERR_HIP = -4
 DSA_ERR_SCRATCH_LIMIT = -5
 DSA_OP_TOPK, DSA_OP_ATTN, DSA_OP_FORWARD, DSA_OP_INDEXER_TOPK, DSA_OP_DENSE_ATTN, DSA_OP_ATTN_BWD = 1, 2, 3, 4, 5, 6
 DSA_OP_INDEXER_KL = 7
+DSA_OP_INDEXER_PROJ = 8
 
 
 class DSAError(RuntimeError):
@@ -43,7 +44,7 @@ class dsa_kv_layout(ctypes.Structure):
                 ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("seq_capacity", ctypes.c_int64)]
 
 
-EXPORTS = ("dsa_cache_write", "dsa_indexer_logits", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_attn",
+EXPORTS = ("dsa_cache_write", "dsa_indexer_project", "dsa_indexer_logits", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_attn",
            "dsa_sparse_mla_attn_bwd", "dsa_sparse_mla_attn_bwd_dq", "dsa_sparse_mla_attn_bwd_dkv",
            "dsa_indexer_kl_target", "dsa_indexer_kl", "dsa_masked_dense_attn", "dsa_forward", "dsa_forward_noalloc",
            "dsa_workspace_bytes",
@@ -63,6 +64,7 @@ def lib() -> ctypes.CDLL:
     vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
     Q, KV = ctypes.POINTER(dsa_queries), ctypes.POINTER(dsa_kv_layout)
     L.dsa_cache_write.argtypes = [Q, KV, i32, vp, vp, vp, vp, vp, vp]
+    L.dsa_indexer_project.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_indexer_logits.argtypes = [Q, KV, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp]
     L.dsa_indexer_topk.argtypes = [Q, KV, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
     L.dsa_topk.argtypes = [vp, i64, vp, i32, i32, i32, vp, vp, sz, vp]
@@ -80,7 +82,7 @@ def lib() -> ctypes.CDLL:
     L.dsa_status_str.argtypes = [i32]
     L.dsa_status_str.restype = ctypes.c_char_p
     L.dsa_abi_version.restype = i32
-    for name in ("dsa_cache_write", "dsa_indexer_logits", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_attn",
+    for name in ("dsa_cache_write", "dsa_indexer_project", "dsa_indexer_logits", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_attn",
                  "dsa_sparse_mla_attn_bwd", "dsa_sparse_mla_attn_bwd_dq", "dsa_sparse_mla_attn_bwd_dkv", "dsa_masked_dense_attn", "dsa_forward",
                  "dsa_forward_noalloc"):
         getattr(L, name).restype = ctypes.c_int
@@ -156,6 +158,14 @@ def dsa_cache_write(q: dsa_queries, layout: dsa_kv_layout, D_I: int, k_new, kv_n
     st = lib().dsa_cache_write(ctypes.byref(q), ctypes.byref(layout), D_I, _ptr(k_new), _ptr(kv_new_bf16),
                                _ptr(k_fp8), _ptr(k_scale), _ptr(kv_bf16), _stream(stream))
     _check(st, "dsa_cache_write")
+
+
+def dsa_indexer_project(d: int, H_I: int, D_I: int, h_bf16, wq_bf16, ww_bf16, wk_bf16, q_fp8, q_scale, w, k_new,
+                        ws: torch.Tensor, stream=None):
+    st = lib().dsa_indexer_project(int(h_bf16.shape[0]), int(d), int(H_I), int(D_I), _ptr(h_bf16), _ptr(wq_bf16),
+                                   _ptr(ww_bf16), _ptr(wk_bf16), _ptr(q_fp8), _ptr(q_scale), _ptr(w), _ptr(k_new),
+                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "dsa_indexer_project")
 
 
 def dsa_indexer_logits(q: dsa_queries, layout: dsa_kv_layout, H_I: int, D_I: int, q_fp8, q_scale, w, k_fp8, k_scale,

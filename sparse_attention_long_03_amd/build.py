@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
-SOURCES = ["abi.hip", "cache_write.hip", "indexer.hip", "indexer_topk.hip", "topk.hip", "sparse_mla.hip",
+SOURCES = ["abi.hip", "cache_write.hip", "indexer_proj.hip", "indexer.hip", "indexer_topk.hip", "topk.hip", "sparse_mla.hip",
            "sparse_mla_bwd.hip", "row_scatter.hip", "indexer_kl.hip"]
 ARCH = "gfx950"
 

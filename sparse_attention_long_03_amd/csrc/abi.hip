@@ -136,6 +136,8 @@ size_t dsa_workspace_bytes(int32_t op, int32_t T, int32_t max_len, int32_t H, in
     case DSA_OP_DENSE_ATTN: return (H > 0) ? dense_attn_workspace_bytes(T, H, max_len) : 0;
     case DSA_OP_ATTN_BWD: return (H > 0 && k > 0 && attn_bwd_size_ok(T, k)) ? attn_bwd_workspace_bytes(T, H, k) : 0;
     case DSA_OP_INDEXER_KL: return (k > 0 && kl_size_ok(T, k)) ? kl_workspace_bytes(T, k) : 0;
+    case DSA_OP_INDEXER_PROJ:  // (T, d, H_I, D_I)
+      return proj_supported(H, k, max_len) ? proj_workspace_bytes(T, max_len, H, k) : 0;
     default: return 0;
   }
 }
@@ -183,6 +185,25 @@ int dsa_cache_write(const dsa_queries* q, const dsa_kv_layout* layout, int32_t D
   return hip_status(launch_cache_write(q->T, D_I, q->seq_id, q->pos, lay, k_new,
                                       static_cast<const uint16_t*>(kv_new_bf16), k_fp8, k_scale,
                                       static_cast<uint16_t*>(kv_bf16), stream));
+}
+
+int dsa_indexer_project(int32_t T, int32_t d, int32_t H_I, int32_t D_I, const void* h_bf16, const void* wq_bf16,
+                        const void* ww_bf16, const void* wk_bf16, uint8_t* q_fp8, float* q_scale, float* w,
+                        float* k_new, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (T < 0 || d < 1 || H_I < 1 || D_I < 1) return DSA_ERR_INVALID_ARG;
+  if (!proj_supported(H_I, D_I, d)) return DSA_ERR_UNSUPPORTED;
+  if ((wk_bf16 == nullptr) != (k_new == nullptr)) return DSA_ERR_INVALID_ARG;
+  if (T == 0) return DSA_OK;
+  if (!h_bf16 || !wq_bf16 || !ww_bf16 || !q_fp8 || !q_scale || !w) return DSA_ERR_INVALID_ARG;
+  if (!aligned(h_bf16, 16) || !aligned(wq_bf16, 16) || !aligned(ww_bf16, 16) || !aligned(q_fp8, 16) ||
+      (wk_bf16 && !aligned(wk_bf16, 16)))
+    return DSA_ERR_INVALID_ARG;
+  const size_t need = proj_workspace_bytes(T, d, H_I, D_I);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)) return DSA_ERR_WORKSPACE;
+  return hip_status(launch_indexer_project(T, d, H_I, D_I, static_cast<const uint16_t*>(h_bf16),
+                                           static_cast<const uint16_t*>(wq_bf16), static_cast<const uint16_t*>(ww_bf16),
+                                           static_cast<const uint16_t*>(wk_bf16), q_fp8, q_scale, w, k_new, workspace,
+                                           stream));
 }
 
 int dsa_topk(const float* logits, int64_t ld_logits, const int32_t* valid_len, int32_t T, int32_t max_len,

@@ -7,32 +7,12 @@
 // with round to nearest, ties to even.  The latent row (576 bf16) is copied
 // as is.  One wave per token: the key's amax is a wave reduction, each lane
 // encodes D_I/64 elements, and the row copy is 72 chunks of 16 bytes.
+#include "fp8_encode.h"
 #include "launch.h"
 
 namespace dsa {
 
 constexpr int CW_WAVES = 4;
-
-// float32 -> e4m3fn code, round to nearest even, for |y| <= 448 (finite).
-// Normal range (|y| >= 2^-6, exponent e): the magnitude in units of the
-// code step 2^(e-3) rounds to an integer m in [8, 16], and the code is
-// (e + 7) * 8 + (m - 8) -- m = 16 carries into the next exponent by itself.
-// Below 2^-6 the step is 2^-9 and the code is the rounded count m in [0, 8]
-// (m = 8 is the smallest normal, code 0x08).  rintf rounds ties to even.
-__device__ __forceinline__ u32 e4m3fn_code(float y) {
-  const u32 u = __float_as_uint(y);
-  const u32 sign = (u >> 31) << 7;
-  const float a = __uint_as_float(u & 0x7FFFFFFFu);
-  u32 mag;
-  if (a < 0.015625f) {  // 2^-6
-    mag = (u32)rintf(a * 512.f);
-  } else {
-    const int e = (int)((u >> 23) & 0xFF) - 127;                      // floor(log2 a), in [-6, 8]
-    const float m = rintf(a * __uint_as_float((u32)(127 + 3 - e) << 23));  // a * 2^(3-e), exact
-    mag = (u32)((e + 7) * 8) + (u32)m - 8u;
-  }
-  return sign | mag;
-}
 
 template <int D_I>
 __global__ __launch_bounds__(CW_WAVES * 64) void cache_write_kernel(const int32_t* __restrict__ seq_id,
@@ -55,14 +35,11 @@ __global__ __launch_bounds__(CW_WAVES * 64) void cache_write_kernel(const int32_
   for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 64));
-  const float scale = fmaxf(amax / 448.f, 1.17549435e-38f);  // floor 2^-126
+  const float scale = e4m3fn_scale(amax);
 
   u32 packed = 0;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const float y = fminf(fmaxf(x[e] / scale, -448.f), 448.f);
-    packed |= e4m3fn_code(y) << (8 * e);
-  }
+  for (int e = 0; e < EPL; ++e) packed |= e4m3fn_quantise(x[e], scale) << (8 * e);
   uint8_t* krow = k8 + row * D_I + EPL * lane;
   if (EPL == 2)
     *reinterpret_cast<uint16_t*>(krow) = (uint16_t)packed;

@@ -50,6 +50,15 @@ hipError_t launch_cache_write(int T, int D_I, const int32_t* seq_id, const int32
                               const float* k_new, const uint16_t* kv_new, uint8_t* k8, float* ks, uint16_t* kv,
                               hipStream_t stream);
 
+// the indexer's inputs from hidden states: q (FP8 + per-token scale), w and
+// optionally k, from bf16 h [T, d] and weights Wq [H_I*D_I, d], Ww [H_I, d],
+// Wk [D_I, d]; fp32 partial sums in the workspace
+bool proj_supported(int H_I, int D_I, int d);
+size_t proj_workspace_bytes(int T, int d, int H_I, int D_I);
+hipError_t launch_indexer_project(int T, int d, int H_I, int D_I, const uint16_t* h, const uint16_t* wq,
+                                  const uint16_t* ww, const uint16_t* wk, uint8_t* q8, float* qs, float* w,
+                                  float* k_new, void* ws, hipStream_t stream);
+
 // (3') masked dense variant of (3): all positions 0..pos[t], unselected masked
 bool dense_attn_supported(int max_len);
 size_t dense_attn_workspace_bytes(int T, int H, int max_len);

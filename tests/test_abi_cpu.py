@@ -280,3 +280,22 @@ def test_forward_noalloc_validation(lib):
     assert B.dsa_workspace_bytes(B.DSA_OP_FORWARD, 64, 1 << 17, 128, 2048) > (64 << 20)
     assert call(q_=_q(T=64, max_len=1 << 17)) == B.DSA_ERR_SCRATCH_LIMIT
     assert "static scratch" in B.dsa_status_str(B.DSA_ERR_SCRATCH_LIMIT)
+
+
+def test_indexer_project_validation(lib):
+    f = lib.dsa_indexer_project
+
+    def call(T=4, d=512, H_I=64, D_I=128, wk=FAKE, kn=FAKE, ws=FAKE, nbytes=0, h=FAKE):
+        return f(T, d, H_I, D_I, h, FAKE, FAKE, wk, FAKE, FAKE, FAKE, kn, ws, nbytes, None)
+
+    need = B.dsa_workspace_bytes(B.DSA_OP_INDEXER_PROJ, 4, 512, 64, 128)
+    assert need >= 4 * (64 * 128 + 64 + 128) * 4
+    assert call(d=500) == B.DSA_ERR_UNSUPPORTED            # not a multiple of 64
+    assert call(H_I=8) == B.DSA_ERR_UNSUPPORTED
+    assert call(wk=None) == B.DSA_ERR_INVALID_ARG            # key weights without a key output
+    assert call(kn=None) == B.DSA_ERR_INVALID_ARG
+    assert call(h=None) == B.DSA_ERR_INVALID_ARG
+    assert call(nbytes=need - 1) == B.DSA_ERR_WORKSPACE
+    assert call(ws=None, nbytes=need) == B.DSA_ERR_WORKSPACE
+    assert call(T=0) == B.DSA_OK
+    assert B.dsa_workspace_bytes(B.DSA_OP_INDEXER_PROJ, 4, 500, 64, 128) == 0

@@ -1,0 +1,107 @@
+"""GPU parity of the indexer projection (dsa_indexer_project): the FP8 query
+with its per-token scale, the head weights and the token's own index key,
+from bf16 hidden states and weights, against the float64 oracle.
+
+Exact case: hidden states and weights whose values are small integers
+(times 2^-3), so every product and every partial sum is exact in fp32 in any
+order; the GPU's projection then equals the oracle's, and the codes and
+scales must match bit for bit (w and k exactly).  Natural case: N(0,1)
+hidden states and N(0, 1/d) weights; the projection is within the bf16
+matrix cores' accumulation bound of the oracle's, and each dequantised query
+value within half an FP8 step of it plus that bound.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_attention_long_03_amd import binding as B
+from sparse_attention_long_03_amd import inputs as I
+
+from parity_util import np_
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+# |matrix-core sum - exact sum| / sum |products| for the bf16 projection,
+# checked on the natural case below
+PROJ_ACC_BOUND = 2.0 ** -15
+
+
+def _gen(seed, shape, kind, d=1):
+    g = torch.Generator().manual_seed(seed)
+    if kind == "int":
+        v = torch.randint(-3, 4, shape, generator=g).float()
+    elif kind == "int8th":
+        v = torch.randint(-2, 3, shape, generator=g).float() / 8.0
+    else:
+        v = torch.randn(shape, generator=g) / (d ** 0.5 if kind == "w" else 1.0)
+    return v.to(torch.bfloat16).to(DEV)
+
+
+def _run(T, d, H_I, D_I, with_k, exact, seed=0):
+    h = _gen(seed, (T, d), "int" if exact else "h")
+    wq = _gen(seed + 1, (H_I * D_I, d), "int8th" if exact else "w", d)
+    ww = _gen(seed + 2, (H_I, d), "int8th" if exact else "w", d)
+    wk = _gen(seed + 3, (D_I, d), "int8th" if exact else "w", d) if with_k else None
+    q8 = torch.empty((T, H_I, D_I), dtype=torch.uint8, device=DEV)
+    qs = torch.empty((T,), dtype=torch.float32, device=DEV)
+    w = torch.empty((T, H_I), dtype=torch.float32, device=DEV)
+    k = torch.empty((T, D_I), dtype=torch.float32, device=DEV) if with_k else None
+    ws = B.workspace(B.dsa_workspace_bytes(B.DSA_OP_INDEXER_PROJ, T, d, H_I, D_I))
+    B.dsa_indexer_project(d, H_I, D_I, h, wq, ww, wk, q8, qs, w, k, ws)
+    torch.cuda.synchronize()
+    ref = O.indexer_projection(I.bf16_bits(h), I.bf16_bits(wq), I.bf16_bits(ww), H_I, D_I,
+                               None if wk is None else I.bf16_bits(wk))
+    mags = [np.abs(O.decode_bf16(I.bf16_bits(h))) @ np.abs(O.decode_bf16(I.bf16_bits(m))).T
+            for m in (wq, ww) + ((wk,) if with_k else ())]
+    return (np_(q8), np_(qs), np_(w), None if k is None else np_(k)), ref, mags
+
+
+EXACT = [
+    # (T, d, H_I, D_I, with_k): a decode batch at the model's width (hidden
+    # dims split over the grid), ragged token tiles, every indexer shape
+    (16, 7168, 64, 128, True),
+    (70, 512, 64, 128, True),
+    (5, 256, 4, 64, False),
+    (33, 384, 64, 64, True),
+    (100, 1024, 4, 128, False),
+]
+
+
+@pytest.mark.parametrize("T,d,H_I,D_I,with_k", EXACT)
+def test_projection_bit_exact_on_exact_inputs(T, d, H_I, D_I, with_k):
+    (q8, qs, w, k), (rq8, rqs, rw, rk), _ = _run(T, d, H_I, D_I, with_k, exact=True)
+    assert np.array_equal(qs, rqs)
+    assert np.array_equal(q8, rq8)
+    assert np.array_equal(w, rw)
+    if with_k:
+        assert np.array_equal(k, rk)
+
+
+@pytest.mark.parametrize("T,d,H_I,D_I", [(16, 7168, 64, 128), (70, 1024, 64, 128), (9, 512, 4, 64)])
+def test_projection_natural_inputs(T, d, H_I, D_I):
+    (q8, qs, w, k), (rq8, rqs, rw, rk), (mq, mw, mk) = _run(T, d, H_I, D_I, True, exact=False, seed=7)
+    # w and k: within the accumulation bound of their exact values
+    for what, g, r, m in (("w", w, rw, mw), ("k", k, rk, mk)):
+        err = np.abs(g.astype(np.float64) - r.astype(np.float64))
+        ratio = err / np.maximum(m, 1e-300)
+        print(f"projection {what}: worst |err| / sum|h*W| = {ratio.max():.3e}", flush=True)
+        assert np.all(err <= PROJ_ACC_BOUND * m + 2.0 ** -24 * np.abs(r)), what
+    # q: the exact projection, its per-token scale and the dequantised codes
+    qx = (O.decode_bf16(I.bf16_bits(_gen(7, (T, d), "h"))) @
+          O.decode_bf16(I.bf16_bits(_gen(8, (H_I * D_I, d), "w", d))).T)
+    eq = PROJ_ACC_BOUND * mq + 2.0 ** -24 * np.abs(qx)           # bound on the GPU's fp32 projection
+    amax_tol = eq.max(axis=1)
+    assert np.all(np.abs(qs.astype(np.float64) * 448 - np.abs(qx).max(axis=1)) <= amax_tol * (1 + 1e-6) + 448 * 2.0 ** -23 * qs)
+    # a code is the nearest FP8 value of the GPU's q / scale: within half a step
+    # of it (2^-4 relative for normals, 2^-10 of the scale below), and the
+    # GPU's q is within eq of the exact one
+    deq = O.decode_e4m3fn(q8).reshape(T, -1) * qs.astype(np.float64)[:, None]
+    half_step = np.maximum(2.0 ** -4 * (np.abs(qx) + eq), 2.0 ** -10 * qs.astype(np.float64)[:, None])
+    err = np.abs(deq - qx)
+    assert np.all(err <= half_step * (1 + 1e-6) + eq)
+    same = float((q8.reshape(T, -1) == rq8.reshape(T, -1)).mean())
+    print(f"projection q: {same:.5f} of the codes equal the oracle's", flush=True)
+    assert same > 0.99
