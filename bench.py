@@ -73,6 +73,8 @@ def parse():
     ap.add_argument("--kl", action="store_true",
                     help="with --config train64k_chunk4k: time the indexer's KL training signal instead of the "
                          "attention backward")
+    ap.add_argument("--kl-dense", action="store_true",
+                    help="with a decode config: time the dense warm-up's KL target over every position")
     ap.add_argument("--proj", action="store_true",
                     help="time the indexer projection (hidden states -> FP8 query + scale, head weights, index key)")
     ap.add_argument("--crossover", action="store_true",
@@ -440,6 +442,50 @@ def bench_kl(args, cfg):
     print(json.dumps(out), flush=True)
 
 
+def bench_kl_dense(args, cfg):
+    """The dense warm-up's KL target (dsa_indexer_kl_target_dense) over every
+    position 0..pos[t] of each decode query: the dense attention's lse (first
+    pass over the rows) and the head-mean probabilities (second pass).  Each
+    pass reads every latent row of the query's sequence (1152 B) once, so the
+    kernels are bound by HBM; four replicas of the caches rotate so that no
+    launch finds its rows in the MALL."""
+    import torch
+    from sparse_attention_long_03_amd import binding as B
+    from sparse_attention_long_03_amd import inputs as I
+    from sparse_attention_long_03_amd.path import DSAPath
+
+    x0 = I.make_inputs(I.scaled(cfg, planted_frac=0.0), "cuda")
+    xs = replicas(x0, REPLICAS)
+    paths = [DSAPath(x) for x in xs]
+    target = torch.empty((x0.T, paths[0].ld), dtype=torch.float32, device="cuda")
+    lse = torch.empty((x0.T, cfg.H), dtype=torch.float32, device="cuda")
+    ws = B.workspace(B.dsa_workspace_bytes(B.DSA_OP_KL_TARGET_DENSE, x0.T, x0.max_len, cfg.H, 0))
+    fns = [(lambda p=p, x=x: B.dsa_indexer_kl_target_dense(p.q, p.layout, cfg.H, x.q, x.kv, cfg.scale, target, lse,
+                                                           ws)) for p, x in zip(paths, xs)]
+    stream = torch.cuda.current_stream()
+    timed_rotation(fns, 2 * REPLICAS, stream)
+    n_launch = max(args.steps, 20)
+    avg = batch_rotation(fns, n_launch, stream)
+    ts = timed_rotation(fns, n_launch, stream)
+    n = (x0.pos.long() + 1).sum().item()
+    nbytes = 2 * n * cfg.D * 2 + n * 4 + 2 * x0.T * cfg.H * cfg.D * 2
+    flops = 2 * 2 * n * cfg.H * cfg.D
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    out = {"metric": "dense warm-up KL target query tokens/s @128K ctx (every position)",
+           "value": round(x0.T / (avg * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": n_launch,
+           "warmup": 2 * REPLICAS, "ms_per_step": round(avg, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16 scores, fp32 softmax", "data": "synthetic",
+           "config": {"workload": f"{cfg.name}: {x0.T} decode queries, target over all {x0.max_len} positions each, "
+                                  f"{cfg.H} heads x 576", "T": x0.T, "L": cfg.L, "H": cfg.H},
+           "roofline": {"bound": "hbm", "kernel": "kl_target_kernel<1> + kl_target_kernel<2>", "achieved": round(gbs, 1),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                        "bytes_per_launch": nbytes, "avg_launch_us": round(avg * 1e3, 1),
+                        "p10_us": round(sorted(ts)[len(ts) // 10] * 1e3, 1),
+                        "p90_us": round(sorted(ts)[(9 * len(ts)) // 10] * 1e3, 1)},
+           "kernels": {"tflops": round(flops / (avg * 1e-3) / 1e12, 1)}}
+    print(json.dumps(out), flush=True)
+
+
 def bench_crossover(args):
     """Sparse gather vs masked dense attention on the same top-2048 selection,
     prefill (every token a query) and 16-sequence decode, L = 1K .. 16K: the
@@ -605,6 +651,9 @@ def main():
             bench_kl(args, cfg)
         else:
             bench_backward(args, cfg)
+        return
+    if args.kl_dense:
+        bench_kl_dense(args, cfg)
         return
     x0 = I.make_inputs(cfg, "cuda")
     xs = replicas(x0, REPLICAS)

@@ -280,7 +280,7 @@ int dsa_sparse_mla_attn_bwd_dkv(const dsa_queries* q, const dsa_kv_layout* layou
  * distribution through a KL divergence; the target takes no gradient).
  *
  * dsa_indexer_kl_target: for the entries j of idx[t, :] (the sparse stage's
- * selection; the dense warm-up passes every position 0..pos[t]),
+ * selection; for the dense warm-up see dsa_indexer_kl_target_dense),
  *     target[t, j] = (1/H) sum_h exp(z[t,h,j] - lse[t,h]),
  *     z = sm_scale * <q[t,h,:], kv_row_j>,
  * the head-summed attention probabilities normalised to total 1; 0 for
@@ -292,6 +292,24 @@ int dsa_sparse_mla_attn_bwd_dkv(const dsa_queries* q, const dsa_kv_layout* layou
 int dsa_indexer_kl_target(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H, const void* q_bf16,
                           const void* kv_bf16, const int32_t* idx, int32_t k, float sm_scale, const float* lse,
                           float* target, hipStream_t stream);
+
+/* dsa_indexer_kl_target_dense: the dense warm-up's target ("Teaching signal":
+ * first a short dense warm-up, the main model frozen), over every position
+ * s = 0..pos[t] of the query's sequence at any context length:
+ *     target[t * ld_target + s] = (1/H) sum_h exp(z[t,h,s] - lse[t,h]),
+ *     lse[t,h] = ln sum_{s <= pos[t]} exp(z[t,h,s])   (the dense attention's),
+ * with z as above.  The lse is computed here from every position (two passes
+ * over the rows) and written to lse_out when it is not NULL.  Entries past
+ * pos[t] of a row are left unwritten.  The rows sum to 1 up to rounding.
+ *   arguments : q, layout, H, q_bf16, kv_bf16, sm_scale as for dsa_sparse_mla_attn
+ *   target    : device float[T, ld_target], ld_target >= max_len
+ *   lse_out   : device float[T, H] or NULL
+ *   workspace : device, >= dsa_workspace_bytes(DSA_OP_KL_TARGET_DENSE, T, max_len, H, 0),
+ *               256-byte aligned (8 bytes per query, head and 2048 positions)
+ * ------------------------------------------------------------------------- */
+int dsa_indexer_kl_target_dense(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H, const void* q_bf16,
+                                const void* kv_bf16, float sm_scale, float* target, int64_t ld_target, float* lse_out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* dsa_indexer_kl: with the indexer logits I (as dsa_indexer_logits) at the
  * selected entries, q[t, j] = softmax_j I[t, idx[t, j]] over the entries != -1:
@@ -381,6 +399,7 @@ int dsa_forward_noalloc(const dsa_queries* q, const dsa_kv_layout* layout, int32
 #define DSA_OP_ATTN_BWD 6
 #define DSA_OP_INDEXER_KL 7
 #define DSA_OP_INDEXER_PROJ 8 /* arguments (T, d, H_I, D_I) in place of (T, max_len, H, k) */
+#define DSA_OP_KL_TARGET_DENSE 9
 size_t dsa_workspace_bytes(int32_t op, int32_t T, int32_t max_len, int32_t H, int32_t k);
 
 /* Static string for a status code (never NULL). */

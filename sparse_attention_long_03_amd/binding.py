@@ -26,6 +26,7 @@ DSA_ERR_SCRATCH_LIMIT = -5
 DSA_OP_TOPK, DSA_OP_ATTN, DSA_OP_FORWARD, DSA_OP_INDEXER_TOPK, DSA_OP_DENSE_ATTN, DSA_OP_ATTN_BWD = 1, 2, 3, 4, 5, 6
 DSA_OP_INDEXER_KL = 7
 DSA_OP_INDEXER_PROJ = 8
+DSA_OP_KL_TARGET_DENSE = 9
 
 
 class DSAError(RuntimeError):
@@ -46,7 +47,7 @@ class dsa_kv_layout(ctypes.Structure):
 
 EXPORTS = ("dsa_cache_write", "dsa_indexer_project", "dsa_indexer_logits", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_attn",
            "dsa_sparse_mla_attn_bwd", "dsa_sparse_mla_attn_bwd_dq", "dsa_sparse_mla_attn_bwd_dkv",
-           "dsa_indexer_kl_target", "dsa_indexer_kl", "dsa_masked_dense_attn", "dsa_forward", "dsa_forward_noalloc",
+           "dsa_indexer_kl_target", "dsa_indexer_kl_target_dense", "dsa_indexer_kl", "dsa_masked_dense_attn", "dsa_forward", "dsa_forward_noalloc",
            "dsa_workspace_bytes",
            "dsa_status_str", "dsa_abi_version")
 
@@ -73,6 +74,8 @@ def lib() -> ctypes.CDLL:
     L.dsa_sparse_mla_attn_bwd_dq.argtypes = [Q, KV, i32, vp, vp, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_sparse_mla_attn_bwd_dkv.argtypes = [Q, KV, i32, vp, i32, vp, vp, vp, sz, vp]
     L.dsa_indexer_kl_target.argtypes = [Q, KV, i32, vp, vp, vp, i32, f32, vp, vp, vp]
+    L.dsa_indexer_kl_target_dense.argtypes = [Q, KV, i32, vp, vp, f32, vp, i64, vp, vp, sz, vp]
+    L.dsa_indexer_kl_target_dense.restype = ctypes.c_int
     L.dsa_indexer_kl.argtypes = [Q, KV, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_masked_dense_attn.argtypes = [Q, KV, i32, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
     L.dsa_forward.argtypes = [Q, KV, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]
@@ -231,6 +234,15 @@ def dsa_indexer_kl_target(q: dsa_queries, layout: dsa_kv_layout, H: int, q_bf16,
     st = lib().dsa_indexer_kl_target(ctypes.byref(q), ctypes.byref(layout), H, _ptr(q_bf16), _ptr(kv_bf16), _ptr(idx),
                                      int(k), float(sm_scale), _ptr(lse), _ptr(target), _stream(stream))
     _check(st, "dsa_indexer_kl_target")
+
+
+def dsa_indexer_kl_target_dense(q: dsa_queries, layout: dsa_kv_layout, H: int, q_bf16, kv_bf16, sm_scale: float,
+                                target: torch.Tensor, lse_out=None, ws: Optional[torch.Tensor] = None, stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib().dsa_indexer_kl_target_dense(ctypes.byref(q), ctypes.byref(layout), H, _ptr(q_bf16), _ptr(kv_bf16),
+                                           float(sm_scale), _ptr(target), int(target.shape[-1]), _ptr(lse_out),
+                                           _ptr(ws), nbytes, _stream(stream))
+    _check(st, "dsa_indexer_kl_target_dense")
 
 
 def dsa_indexer_kl(q: dsa_queries, layout: dsa_kv_layout, H_I: int, D_I: int, q_fp8, q_scale, w, k_fp8, k_scale,

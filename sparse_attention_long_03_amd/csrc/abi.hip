@@ -136,6 +136,7 @@ size_t dsa_workspace_bytes(int32_t op, int32_t T, int32_t max_len, int32_t H, in
     case DSA_OP_DENSE_ATTN: return (H > 0) ? dense_attn_workspace_bytes(T, H, max_len) : 0;
     case DSA_OP_ATTN_BWD: return (H > 0 && k > 0 && attn_bwd_size_ok(T, k)) ? attn_bwd_workspace_bytes(T, H, k) : 0;
     case DSA_OP_INDEXER_KL: return (k > 0 && kl_size_ok(T, k)) ? kl_workspace_bytes(T, k) : 0;
+    case DSA_OP_KL_TARGET_DENSE: return (H > 0 && max_len > 0) ? kl_target_dense_workspace_bytes(T, H, max_len) : 0;
     case DSA_OP_INDEXER_PROJ:  // (T, d, H_I, D_I)
       return proj_supported(H, k, max_len) ? proj_workspace_bytes(T, max_len, H, k) : 0;
     default: return 0;
@@ -334,6 +335,26 @@ int dsa_indexer_kl_target(const dsa_queries* q, const dsa_kv_layout* layout, int
   return hip_status(launch_kl_target(q->T, H, static_cast<const uint16_t*>(q_bf16),
                                      static_cast<const uint16_t*>(kv_bf16), idx, q->seq_id, lay, k, sm_scale, lse,
                                      target, stream));
+}
+
+int dsa_indexer_kl_target_dense(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H, const void* q_bf16,
+                                const void* kv_bf16, float sm_scale, float* target, int64_t ld_target, float* lse_out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Layout lay;
+  int st = check_queries(q);
+  if (st) return st;
+  if ((st = check_layout(layout, q, &lay))) return st;
+  if (H < 1 || !(sm_scale > 0.f)) return DSA_ERR_INVALID_ARG;
+  if (!attn_supported(H)) return DSA_ERR_UNSUPPORTED;
+  if (q->T == 0) return DSA_OK;
+  if (!q_bf16 || !kv_bf16 || !target || !aligned(q_bf16, 16) || !aligned(kv_bf16, 16) || !aligned(target, 4))
+    return DSA_ERR_INVALID_ARG;
+  if (ld_target < q->max_len) return DSA_ERR_INVALID_ARG;
+  const size_t need = kl_target_dense_workspace_bytes(q->T, H, q->max_len);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)) return DSA_ERR_WORKSPACE;
+  return hip_status(launch_kl_target_dense(q->T, H, q->max_len, static_cast<const uint16_t*>(q_bf16),
+                                           static_cast<const uint16_t*>(kv_bf16), q->seq_id, q->pos, lay, sm_scale,
+                                           target, ld_target, lse_out, workspace, stream));
 }
 
 int dsa_indexer_kl(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,

@@ -36,14 +36,29 @@ constexpr float LOG2E = 1.4426950408889634f;
 // S^T = K Q^T for its heads, P = exp(z - lse), and sums P over its 16 heads
 // with four xor steps; the waves' sums meet in LDS and the next tile's first
 // 32 threads write their total / H.
+//
+// The dense warm-up (every position 0..pos[t] of the sequence) runs the same
+// tile loop over contiguous positions, split into chunks of up to 2048 per
+// workgroup (blockIdx.y), in two launches:
+//   KT_DENSE_LSE     per chunk and head, the running maximum m (log2 units)
+//                    and the sum l of exp2(z - m) over the chunk's positions;
+//   KT_DENSE_TARGET  every lane first merges the chunks' (m, l) of its head
+//                    into the dense lse (the warm-up's attention runs over
+//                    every position), then the target of each position.
 constexpr int KT_NW = 8;
+enum KtMode { KT_SELECTED = 0, KT_DENSE_LSE = 1, KT_DENSE_TARGET = 2 };
 
+template <int MODE>
 __global__ __launch_bounds__(KT_NW * 64) void kl_target_kernel(const uint16_t* __restrict__ q,
                                                              const uint8_t* __restrict__ kv,
                                                              const int32_t* __restrict__ idx,
-                                                             const int32_t* __restrict__ seq_id, Layout lay, int H,
+                                                             const int32_t* __restrict__ seq_id,
+                                                             const int32_t* __restrict__ pos, Layout lay, int H,
                                                              int k, float scale_log2, const float* __restrict__ lse,
-                                                             float* __restrict__ target, int n_tokens) {
+                                                             float* __restrict__ target, int64_t ld_target,
+                                                             float* __restrict__ ml, int n_chunks,
+                                                             float* __restrict__ lse_out, int n_tokens) {
+  constexpr bool DENSE = MODE != KT_SELECTED;
   constexpr int NT = KT_NW * 64;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF_BYTES];
   __shared__ u32 s_row[AT_MAX_SPLIT];
@@ -60,12 +75,20 @@ __global__ __launch_bounds__(KT_NW * 64) void kl_target_kernel(const uint16_t* _
   const bool has_heads = h0 < H;
   const int nw_heads = H / 16;
   const int b = seq_id[t];
-  const int32_t* __restrict__ idx_row = idx + (int64_t)t * k;
-  const int ntiles = (k + AT_TILE - 1) / AT_TILE;
+  const int32_t* __restrict__ idx_row = DENSE ? nullptr : idx + (int64_t)t * k;
+  // the entries of this workgroup: the selection, or one chunk of positions
+  const int j_begin = DENSE ? blockIdx.y * AT_MAX_SPLIT : 0;
+  const int n_ent = DENSE ? min(pos[t] + 1 - j_begin, AT_MAX_SPLIT) : k;
+  if (n_ent <= 0) return;  // (dense) the chunk lies past the query's position
+  const int ntiles = (n_ent + AT_TILE - 1) / AT_TILE;
 
   const u32 safe_row = (u32)token_row(lay, b, 0);
   for (int i = tid; i < ntiles * AT_TILE; i += NT) {
-    const int s = (i < k) ? idx_row[i] : -1;
+    int s;
+    if constexpr (DENSE)
+      s = (i < n_ent) ? j_begin + i : -1;
+    else
+      s = (i < k) ? idx_row[i] : -1;
     s_row[i] = (s >= 0) ? (u32)token_row(lay, b, s) : (safe_row | ROW_INVALID);
   }
   __syncthreads();
@@ -82,13 +105,30 @@ __global__ __launch_bounds__(KT_NW * 64) void kl_target_kernel(const uint16_t* _
 #pragma unroll
     for (int ks = 0; ks < AT_D / 32; ++ks) qf[ks] = *reinterpret_cast<const v8bf*>(qrow + 32 * ks);
   }
-  const float lse2 = lse[(int64_t)t * H + hq] * LOG2E;
+  // lse of head hq in log2 units: given (the forward's), or merged from the
+  // dense chunks' (m, l)
+  float lse2 = 0.f;
+  if constexpr (MODE == KT_SELECTED) {
+    lse2 = lse[(int64_t)t * H + hq] * LOG2E;
+  } else if constexpr (MODE == KT_DENSE_TARGET) {
+    const int nch = min(n_chunks, (pos[t] + AT_MAX_SPLIT) / AT_MAX_SPLIT);
+    const float* mlq = ml + ((int64_t)t * n_chunks * H + hq) * 2;
+    float M = -INFINITY;
+    for (int c = 0; c < nch; ++c) M = fmaxf(M, mlq[(int64_t)c * H * 2]);
+    float L = 0.f;
+    for (int c = 0; c < nch; ++c) L += mlq[(int64_t)c * H * 2 + 1] * exp2f(mlq[(int64_t)c * H * 2] - M);
+    lse2 = M + log2f(L);
+    if (lse_out != nullptr && blockIdx.y == 0 && g == 0 && has_heads)
+      lse_out[(int64_t)t * H + hq] = lse2 * 0.69314718055994531f;
+  }
   const float inv_h = 1.f / (float)H;
+  float m_run = -INFINITY, l_run = 0.f;  // KT_DENSE_LSE: this lane's keys of head hq
 
   LDS_AS uint8_t* lds = (LDS_AS uint8_t*)smem;
   __syncthreads();  // s_row / s_valid visible
 
-  // Scores and head sum of one tile; the sums go to s_part[it & 1].
+  // Scores of one tile; then the head sum (to s_part[it & 1]) or the lane's
+  // running (m, l).
   auto tile = [&](const LDS_AS uint8_t* buf, int it) {
     constexpr int SPIPE = 4;
     auto frag = [&](int ks, int r) -> v8bf {
@@ -114,31 +154,58 @@ __global__ __launch_bounds__(KT_NW * 64) void kl_target_kernel(const uint16_t* _
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    float p[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(s0[i] * scale_log2 - lse2);
-      p[4 + i] = __builtin_amdgcn_exp2f(s1[i] * scale_log2 - lse2);
-    }
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] += __shfl_xor(p[i], d, 64);
-    if (n == 0 && has_heads) {
+    if constexpr (MODE == KT_DENSE_LSE) {
+      // lane holds head n: s0[i] -> key 4g+i, s1[i] -> key 16+4g+i
+      const u32 valid = s_valid[it];
+      float z[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        s_part[it & 1][wid][4 * g + i] = p[i];
-        s_part[it & 1][wid][16 + 4 * g + i] = p[4 + i];
+        z[i] = ((valid >> (4 * g + i)) & 1u) ? s0[i] * scale_log2 : -INFINITY;
+        z[4 + i] = ((valid >> (16 + 4 * g + i)) & 1u) ? s1[i] * scale_log2 : -INFINITY;
+      }
+      float mx = m_run;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mx = fmaxf(mx, z[i]);
+      if (mx > -INFINITY) {
+        float add = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) add += exp2f(z[i] - mx);
+        l_run = l_run * exp2f(m_run - mx) + add;  // exp2(-inf) = 0 on the first tile
+        m_run = mx;
+      }
+    } else {
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(s0[i] * scale_log2 - lse2);
+        p[4 + i] = __builtin_amdgcn_exp2f(s1[i] * scale_log2 - lse2);
+      }
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] += __shfl_xor(p[i], d, 64);
+      if (n == 0 && has_heads) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s_part[it & 1][wid][4 * g + i] = p[i];
+          s_part[it & 1][wid][16 + 4 * g + i] = p[4 + i];
+        }
       }
     }
   };
   // the sums of tile it, written once every wave has stored its part
   auto finish = [&](int it) {
-    if (tid < AT_TILE && it >= 0 && it < ntiles) {
-      float v = 0.f;
-      for (int w = 0; w < nw_heads; ++w) v += s_part[it & 1][w][tid];
-      const int j = it * AT_TILE + tid;
-      if (j < k) target[(int64_t)t * k + j] = ((s_valid[it] >> tid) & 1u) ? v * inv_h : 0.f;
+    if constexpr (MODE != KT_DENSE_LSE) {
+      if (tid < AT_TILE && it >= 0 && it < ntiles) {
+        float v = 0.f;
+        for (int w = 0; w < nw_heads; ++w) v += s_part[it & 1][w][tid];
+        const int j = it * AT_TILE + tid;
+        if constexpr (DENSE) {
+          if (j < n_ent) target[(int64_t)t * ld_target + j_begin + j] = v * inv_h;
+        } else {
+          if (j < k) target[(int64_t)t * k + j] = ((s_valid[it] >> tid) & 1u) ? v * inv_h : 0.f;
+        }
+      }
     }
   };
 
@@ -163,6 +230,23 @@ __global__ __launch_bounds__(KT_NW * 64) void kl_target_kernel(const uint16_t* _
   }
   __syncthreads();
   finish(ntiles - 1);  // (with an odd tile count already written once: the same values)
+
+  if constexpr (MODE == KT_DENSE_LSE) {
+    // merge the four lane groups of head hq (lanes n, n+16, n+32, n+48)
+#pragma unroll
+    for (int d = 16; d < 64; d <<= 1) {
+      const float mo = __shfl_xor(m_run, d, 64);
+      const float lo = __shfl_xor(l_run, d, 64);
+      const float mm = fmaxf(m_run, mo);
+      l_run = (mm == -INFINITY) ? 0.f : l_run * exp2f(m_run - mm) + lo * exp2f(mo - mm);
+      m_run = mm;
+    }
+    if (g == 0 && has_heads) {
+      float* o = ml + (((int64_t)t * n_chunks + blockIdx.y) * H + hq) * 2;
+      o[0] = m_run;
+      o[1] = l_run;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -469,8 +553,31 @@ hipError_t launch_kl_target(int T, int H, const uint16_t* q, const uint16_t* kv,
                             const int32_t* seq_id, const Layout& lay, int k, float sm_scale, const float* lse,
                             float* target, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(kl_target_kernel, dim3(T), dim3(KT_NW * 64), 0, stream, q, reinterpret_cast<const uint8_t*>(kv),
-                     idx, seq_id, lay, H, k, sm_scale * LOG2E, lse, target, T);
+  hipLaunchKernelGGL(kl_target_kernel<KT_SELECTED>, dim3(T), dim3(KT_NW * 64), 0, stream, q,
+                     reinterpret_cast<const uint8_t*>(kv), idx, seq_id, nullptr, lay, H, k, sm_scale * LOG2E, lse,
+                     target, (int64_t)k, nullptr, 0, nullptr, T);
+  return hipGetLastError();
+}
+
+static int dense_target_chunks(int max_len) { return (max_len + AT_MAX_SPLIT - 1) / AT_MAX_SPLIT; }
+
+size_t kl_target_dense_workspace_bytes(int T, int H, int max_len) {
+  return align256((size_t)T * dense_target_chunks(max_len) * H * 2 * 4);
+}
+
+hipError_t launch_kl_target_dense(int T, int H, int max_len, const uint16_t* q, const uint16_t* kv,
+                                  const int32_t* seq_id, const int32_t* pos, const Layout& lay, float sm_scale,
+                                  float* target, int64_t ld, float* lse_out, void* ws, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int nch = dense_target_chunks(max_len);
+  float* ml = static_cast<float*>(ws);
+  const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv);
+  hipLaunchKernelGGL(kl_target_kernel<KT_DENSE_LSE>, dim3(T, nch), dim3(KT_NW * 64), 0, stream, q, kvb, nullptr,
+                     seq_id, pos, lay, H, 0, sm_scale * LOG2E, nullptr, nullptr, (int64_t)0, ml, nch, nullptr, T);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kl_target_kernel<KT_DENSE_TARGET>, dim3(T, nch), dim3(KT_NW * 64), 0, stream, q, kvb, nullptr,
+                     seq_id, pos, lay, H, 0, sm_scale * LOG2E, nullptr, target, ld, ml, nch, lse_out, T);
   return hipGetLastError();
 }
 

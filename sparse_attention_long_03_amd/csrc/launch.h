@@ -92,6 +92,13 @@ size_t kl_workspace_bytes(int T, int k);
 hipError_t launch_kl_target(int T, int H, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                             const int32_t* seq_id, const Layout& lay, int k, float sm_scale, const float* lse,
                             float* target, hipStream_t stream);
+// the dense warm-up's target over every position 0..pos[t] (T x ld fp32),
+// with the dense attention's lse computed on the way (workspace: per chunk of
+// 2048 positions and head, a running max and sum)
+size_t kl_target_dense_workspace_bytes(int T, int H, int max_len);
+hipError_t launch_kl_target_dense(int T, int H, int max_len, const uint16_t* q, const uint16_t* kv,
+                                  const int32_t* seq_id, const int32_t* pos, const Layout& lay, float sm_scale,
+                                  float* target, int64_t ld, float* lse_out, void* ws, hipStream_t stream);
 hipError_t launch_kl(int T, const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8, const float* ks,
                      const int32_t* idx, const int32_t* seq_id, const Layout& lay, int64_t num_rows, int k,
                      const float* target, float* loss, float* dq, float* dw, float* dk, void* ws,

@@ -299,3 +299,21 @@ def test_indexer_project_validation(lib):
     assert call(ws=None, nbytes=need) == B.DSA_ERR_WORKSPACE
     assert call(T=0) == B.DSA_OK
     assert B.dsa_workspace_bytes(B.DSA_OP_INDEXER_PROJ, 4, 500, 64, 128) == 0
+
+
+def test_kl_target_dense_validation(lib):
+    f = lib.dsa_indexer_kl_target_dense
+    lay = _lay(5000)
+
+    def call(q_=None, H=128, ld=5000, target=FAKE, ws=FAKE, nbytes=0, scale=0.04):
+        q_ = q_ or _q(T=4, max_len=5000)
+        return f(ctypes.byref(q_), ctypes.byref(lay), H, FAKE, FAKE, scale, target, ld, None, ws, nbytes, None)
+
+    need = B.dsa_workspace_bytes(B.DSA_OP_KL_TARGET_DENSE, 4, 5000, 128, 0)
+    assert need == 256 * ((4 * 3 * 128 * 8 + 255) // 256)   # 3 chunks of 2048 positions
+    assert call(H=24) == B.DSA_ERR_UNSUPPORTED
+    assert call(scale=0.0) == B.DSA_ERR_INVALID_ARG
+    assert call(ld=4999) == B.DSA_ERR_INVALID_ARG
+    assert call(target=None) == B.DSA_ERR_INVALID_ARG
+    assert call(nbytes=need - 1) == B.DSA_ERR_WORKSPACE
+    assert call(q_=_q(T=0, seq=None, pos=None)) == B.DSA_OK

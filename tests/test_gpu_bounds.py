@@ -150,3 +150,15 @@ def test_backward_and_kl_stay_in_their_buffers():
     B.dsa_indexer_kl_target(p.q, p.layout, cfg.H, x.q, x.kv, idx, cfg.k, cfg.scale, lse, tgt)
     torch.cuda.synchronize()
     assert gt.intact()
+
+
+def test_dense_warmup_target_stays_in_its_buffers():
+    cfg = I.scaled(I.CONFIGS["ragged_paged"], B=4, L=5000, min_len=100, H=64, k=512)
+    x = I.make_inputs(cfg, DEV)
+    p = DSAPath(x)
+    ws = Guarded(B.dsa_workspace_bytes(B.DSA_OP_KL_TARGET_DENSE, x.T, x.max_len, cfg.H, 0))
+    gt, tgt = _guarded(torch.float32, (x.T, p.ld))
+    gl, lse = _guarded(torch.float32, (x.T, cfg.H))
+    B.dsa_indexer_kl_target_dense(p.q, p.layout, cfg.H, x.q, x.kv, cfg.scale, tgt, lse, ws.bytes())
+    torch.cuda.synchronize()
+    assert ws.intact() and gt.intact() and gl.intact()
