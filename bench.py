@@ -153,38 +153,72 @@ def median(xs):
     return sorted(xs)[len(xs) // 2]
 
 
-def cpu_baseline(x, budget_s):
-    """Float64 oracle on host cores, one query at a time (cycling over the
-    batch) until the time budget is spent."""
+def _host_rows(x, b, n, cache):
+    """Logical rows 0..n-1 of sequence b of a cache (contiguous or paged), on the host."""
+    import torch
+    if x.block_table is None:
+        return cache[b, :n].cpu()
+    pos = torch.arange(n, device=cache.device)
+    pages = x.block_table[b].long()[pos // 64]
+    return cache[pages, pos % 64].cpu()
+
+
+def cpu_baseline(x, budget_s, rows=None, extrapolate_to=None):
+    """Float64 oracle on the host cores, one query at a time (cycling over
+    `rows`, by default every query of the batch) until the time budget is
+    spent.  BLAS threads are set to the process's CPU affinity count, which is
+    what `cores` reports.  With `extrapolate_to` (prefill), the rows are a
+    uniform sample of the queries and the rate is extrapolated: the sample's
+    mean time per query stands for every query's.  A sequence's caches are
+    copied to the host (untimed) the first time one of its queries runs."""
     import numpy as np
     import oracle as O
     from sparse_attention_long_03_amd import inputs as I
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_limits
     except Exception:
-        cores = 1
+        threadpool_limits = None
     c = x.cfg
-    host = []
-    for t in range(x.T):  # host copies of every query's inputs (not timed)
-        b = int(x.seq_id[t])
-        n = int(x.pos[t]) + 1
-        host.append((n, x.iq8[t].cpu().numpy(), float(x.iqs[t]), x.iw[t].cpu().numpy().astype(np.float64),
-                     x.ik8[b, :n].cpu().numpy(), x.iks[b, :n].cpu().numpy().astype(np.float64),
-                     I.bf16_bits(x.kv[b, :n])[None], I.bf16_bits(x.q[t:t + 1])))
-    done = 0
-    dt = 0.0
-    while dt <= budget_s:
-        n, q8, qs, w, k8, ks, kv, q = host[done % x.T]
-        ts = time.perf_counter()
-        lg = O.indexer_logits_row(q8, qs, w, k8, ks)
-        sel = O.topk_select(lg.astype(np.float32), n, c.k)
-        O.sparse_mla_attention(q, kv, sel[None], np.zeros(1, int), c.scale, c.d_v)
-        dt += time.perf_counter() - ts
-        done += 1
-    return {"value": round(done / dt, 3), "unit": "queries/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} queries of the same workload, cycling over its {x.T} full-length query rows "
-                      f"(indexer over all {x.max_len} keys, top-k, attention), float64 NumPy oracle, {dt:.1f} s"}
+    rows = list(range(x.T)) if rows is None else list(rows)
+    seq_cache = {}
+
+    def host_seq(b, n):
+        if b not in seq_cache or seq_cache[b][0] < n:
+            L = max(n, int(x.seq_lens[b]))
+            seq_cache[b] = (L, _host_rows(x, b, L, x.ik8).numpy(), _host_rows(x, b, L, x.iks).numpy().astype(np.float64),
+                            I.bf16_bits(_host_rows(x, b, L, x.kv)))
+        return seq_cache[b]
+
+    done, dt = 0, 0.0
+    ctx = threadpool_limits(cores) if threadpool_limits is not None else None
+    try:
+        while dt <= budget_s:
+            t = rows[done % len(rows)]
+            b, n = int(x.seq_id[t]), int(x.pos[t]) + 1
+            _, k8, ks, kv = host_seq(b, n)
+            q8, qs, w = x.iq8[t].cpu().numpy(), float(x.iqs[t]), x.iw[t].cpu().numpy().astype(np.float64)
+            q = I.bf16_bits(x.q[t:t + 1])
+            ts = time.perf_counter()
+            lg = O.indexer_logits_row(q8, qs, w, k8[:n], ks[:n])
+            sel = O.topk_select(lg.astype(np.float32), n, c.k)
+            O.sparse_mla_attention(q, kv[None, :n], sel[None], np.zeros(1, int), c.scale, c.d_v)
+            dt += time.perf_counter() - ts
+            done += 1
+    finally:
+        if ctx is not None:
+            ctx.restore_original_limits()
+    rate = done / dt
+    if extrapolate_to is None:
+        sample = (f"{done} queries of the same workload, cycling over its {len(rows)} query rows (indexer over all "
+                  f"of each row's keys, top-k, attention), float64 NumPy oracle, {dt:.1f} s")
+        unit = "queries/s"
+    else:
+        sample = (f"{done} query rows of a uniform sample of {len(rows)} of the workload's {extrapolate_to} (indexer "
+                  f"over all of each row's keys, top-k, attention), float64 NumPy oracle, {dt:.1f} s; extrapolated: "
+                  f"the sample's mean time per row stands for every row's")
+        unit = "tokens/s"
+    return {"value": round(rate, 3), "unit": unit, "cores": cores, "kind": "oracle", "sample": sample}
 
 
 def cache_write_timing(x, n_launch, stream):
@@ -251,6 +285,7 @@ def bench_prefill(args, cfg):
     fused_ts = timed_rotation([fused], n_launch, stream)
     attn_ts = timed_rotation([lambda: p.attn(idx)], n_launch, stream)
     fused_avg, attn_avg = mean(fused_ts), mean(attn_ts)
+    step_ts = timed_rotation([p.forward], max(args.steps, 5), stream)
     cw_us, cw_gbs = cache_write_timing(x, n_launch, stream)  # last: it overwrites the caches
 
     pairs = (x.pos.long() + 1).sum().item()
@@ -280,11 +315,17 @@ def bench_prefill(args, cfg):
                      "achieved": round(idx_tf, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(idx_tf / FP8_PEAK_TFLOPS, 4), "traffic": None,
                      "flops_per_launch": idx_flops, "avg_launch_us": round(fused_avg * 1e3, 1)},
+        "p10_ms": round(sorted(step_ts)[len(step_ts) // 10], 3),
+        "p90_ms": round(sorted(step_ts)[(9 * len(step_ts)) // 10], 3),
         "kernels": {"indexer_topk_ms": round(fused_avg, 3), "indexer_tflops": round(idx_tf, 1),
                     "attn_ms": round(attn_avg, 3), "attn_tflops": round(attn_tf, 1),
                     "attn_frac_bf16": round(attn_tf / BF16_PEAK_TFLOPS, 4),
                     "cache_write_us": cw_us, "cache_write_gbs": cw_gbs},
     }
+    if not args.no_cpu:
+        import random
+        rows = random.Random(7).sample(range(x.T), 256)  # random order: any prefix is a uniform sample
+        out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds, rows=rows, extrapolate_to=x.T)
     print(json.dumps(out), flush=True)
 
 
@@ -694,6 +735,7 @@ def main():
     attn_avg = batch_rotation(attn_fns, n_launch, stream)
     step_avg = batch_rotation(fwd, n_launch, stream)
     idx_ts = timed_rotation(idx_fns, n_launch, stream)
+    step_ts = timed_rotation(fwd, n_launch, stream)
     graph_us = forward_graph_timing(fwd, args.steps, stream)
     copy_gbs = stream_copy_gbs()
     cw_us, cw_gbs = cache_write_timing(xs[1], n_launch, stream)  # on a replica not used below
@@ -720,6 +762,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(wall_ms, 4),
+        "p10_ms": round(sorted(step_ts)[len(step_ts) // 10], 4),
+        "p90_ms": round(sorted(step_ts)[(9 * len(step_ts)) // 10], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
