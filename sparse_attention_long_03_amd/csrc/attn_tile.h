@@ -61,17 +61,16 @@ struct TileStage {
       if (72 % TPR == 0 || c0 + TPR * r < 72) v[r] = *reinterpret_cast<const v4i*>(src + 16 * TPR * r);
   }
   // no-rope chunks row-major (padded rows); rope chunk cc of row r in slot cc^(r&7)
-  __device__ __forceinline__ void store_one(LDS_AS uint8_t* buf, int tid, int r) const {
-    const int row = tid / TPR, c0 = tid % TPR;
-    const int c = c0 + TPR * r;
-    if (c < 64)
-      *reinterpret_cast<LDS_AS v4i*>(buf + row * NOPE_STRIDE + 16 * c) = v[r];
-    else if (c < 72)
-      *reinterpret_cast<LDS_AS v4i*>(buf + NOPE_BYTES + row * 128 + 16 * ((c - 64) ^ (row & 7))) = v[r];
-  }
   __device__ __forceinline__ void store(LDS_AS uint8_t* buf, int tid) const {
+    const int row = tid / TPR, c0 = tid % TPR;
 #pragma unroll
-    for (int r = 0; r < PER; ++r) store_one(buf, tid, r);
+    for (int r = 0; r < PER; ++r) {
+      const int c = c0 + TPR * r;
+      if (c < 64)
+        *reinterpret_cast<LDS_AS v4i*>(buf + row * NOPE_STRIDE + 16 * c) = v[r];
+      else if (c < 72)
+        *reinterpret_cast<LDS_AS v4i*>(buf + NOPE_BYTES + row * 128 + 16 * ((c - 64) ^ (row & 7))) = v[r];
+    }
   }
 };
 

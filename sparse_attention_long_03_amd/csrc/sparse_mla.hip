@@ -49,22 +49,41 @@ __device__ __forceinline__ float max_over_groups(float v) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// K fragment for the score product: key r of the tile, dims 32ks + 8g..+8
-// (no-rope rows for ks < 16, the swizzled rope block after).
-__device__ __forceinline__ v8bf k_frag(const LDS_AS uint8_t* __restrict__ buf, int ks, int r, int g) {
-  if (ks < 16) return *reinterpret_cast<const LDS_AS v8bf*>(buf + r * NOPE_STRIDE + 64 * ks + 16 * g);
-  const int c = 4 * (ks - 16) + g;  // rope chunk
-  return *reinterpret_cast<const LDS_AS v8bf*>(buf + NOPE_BYTES + r * 128 + 16 * (c ^ (r & 7)));
-}
-
-// Online softmax of one tile from its scores S^T (lane: head n, keys
-// 4g..4g+3 in s0 and 16+4g.. in s1).  `valid` has bit j set when row j of
-// the tile is a selected row.  Returns P (bf16) in the B-operand layout of
-// the value product; when a head's reference maximum moves, `corr` (per
-// lane: its head's factor) is the factor the accumulators of that head must
-// take first, and `rescaled` (wave-uniform) is set.
-__device__ __forceinline__ v8bf softmax_from_scores(v4f s0, v4f s1, u32 valid, float scale_log2, int g, float& m_ref,
-                                                    float& l_part, float& corr, bool& rescaled) {
+// Scores, online softmax and value product for one tile held in `buf`.
+// `valid` has bit j set when row j of the tile is a selected row.
+__device__ __forceinline__ void attend_tile(const LDS_AS uint8_t* __restrict__ buf, u32 valid, const v8bf* qf,
+                                           float scale_log2, int n, int g, float& m_ref, float& l_part, v4f* o) {
+  const LDS_AS uint8_t* nope = buf;
+  const LDS_AS uint8_t* rope = buf + NOPE_BYTES;
+  // ---- scores S^T (keys x heads): K fragments of keys n and 16+n, dims
+  // 32ks + 8g..+8 (no-rope rows for ks < 16, the swizzled rope block after).
+  // The reads run SPIPE steps ahead of the MFMAs that use them, in a ring of
+  // registers, so LDS latency overlaps the matrix work.
+  constexpr int SPIPE = 4;
+  auto frag = [&](int ks, int r) -> v8bf {
+    if (ks < 16) return *reinterpret_cast<const LDS_AS v8bf*>(nope + r * NOPE_STRIDE + 64 * ks + 16 * g);
+    const int c = 4 * (ks - 16) + g;  // rope chunk
+    return *reinterpret_cast<const LDS_AS v8bf*>(rope + r * 128 + 16 * (c ^ (r & 7)));
+  };
+  v8bf ra0[SPIPE], ra1[SPIPE];
+#pragma unroll
+  for (int j = 0; j < SPIPE; ++j) {
+    ra0[j] = frag(j, n);
+    ra1[j] = frag(j, 16 + n);
+  }
+  v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < AT_D / 32; ++ks) {
+    const int slot = ks % SPIPE;
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra0[slot], qf[ks], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra1[slot], qf[ks], s1, 0, 0, 0);
+    if (ks + SPIPE < AT_D / 32) {
+      ra0[slot] = frag(ks + SPIPE, n);
+      ra1[slot] = frag(ks + SPIPE, 16 + n);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the ring order
+  }
+  // lane holds head n: s0[i] -> key 4g+i, s1[i] -> key 16+4g+i
   float z[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -76,12 +95,12 @@ __device__ __forceinline__ v8bf softmax_from_scores(v4f s0, v4f s1, u32 valid, f
   for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
   mx = max_over_groups(mx);
   // move the reference only when this tile would exceed the slack
-  corr = 1.f;
-  rescaled = __builtin_amdgcn_ballot_w64(mx > m_ref + RESCALE_SLACK) != 0;
-  if (rescaled) {
+  if (__builtin_amdgcn_ballot_w64(mx > m_ref + RESCALE_SLACK) != 0) {
     const float m_new = (mx > m_ref + RESCALE_SLACK) ? mx : m_ref;
-    corr = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
+    const float corr = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
     l_part *= corr;
+#pragma unroll
+    for (int mt = 0; mt < AT_DV / 16; ++mt) o[mt] *= corr;
     m_ref = m_new;
   }
   const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
@@ -92,96 +111,17 @@ __device__ __forceinline__ v8bf softmax_from_scores(v4f s0, v4f s1, u32 valid, f
     l_part += p;
     pb[i] = (__bf16)p;
   }
-  return pb;
-}
 
-// The same softmax without branches (so that the scheduler can interleave it
-// with independent matrix work): the reference moves per lane exactly as
-// above; lanes whose reference stays get corr = exp2(0) = 1, and a lane with
-// no reference yet has l_part = 0, so the unconditional l_part *= corr leaves
-// every value as the branching form does.
-__device__ __forceinline__ v8bf softmax_from_scores_nb(v4f s0, v4f s1, u32 valid, float scale_log2, int g,
-                                                       float& m_ref, float& l_part, float& corr, bool& rescaled) {
-  float z[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    z[i] = ((valid >> (4 * g + i)) & 1u) ? s0[i] * scale_log2 : -INFINITY;
-    z[4 + i] = ((valid >> (16 + 4 * g + i)) & 1u) ? s1[i] * scale_log2 : -INFINITY;
-  }
-  float mx = z[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
-  mx = max_over_groups(mx);
-  const bool move = mx > m_ref + RESCALE_SLACK;
-  rescaled = __builtin_amdgcn_ballot_w64(move) != 0;
-  const float m_new = move ? mx : m_ref;
-  corr = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
-  l_part *= corr;
-  m_ref = m_new;
-  const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-  v8bf pb;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float p = __builtin_amdgcn_exp2f(z[i] - m_use);
-    l_part += p;
-    pb[i] = (__bf16)p;
-  }
-  return pb;
-}
-
-// Scores S^T = K Q^T of one tile held in `buf` for the wave's 16 heads, then
-// its online softmax.  The K reads run SPIPE steps ahead of the MFMAs that
-// use them, in a ring of registers, so LDS latency overlaps the matrix work.
-__device__ __forceinline__ v8bf tile_softmax(const LDS_AS uint8_t* __restrict__ buf, u32 valid, const v8bf* qf,
-                                             float scale_log2, int n, int g, float& m_ref, float& l_part,
-                                             float& corr, bool& rescaled) {
-  constexpr int SPIPE = 4;
-  v8bf ra0[SPIPE], ra1[SPIPE];
-#pragma unroll
-  for (int j = 0; j < SPIPE; ++j) {
-    ra0[j] = k_frag(buf, j, n, g);
-    ra1[j] = k_frag(buf, j, 16 + n, g);
-  }
-  v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < AT_D / 32; ++ks) {
-    const int slot = ks % SPIPE;
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra0[slot], qf[ks], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra1[slot], qf[ks], s1, 0, 0, 0);
-    if (ks + SPIPE < AT_D / 32) {
-      ra0[slot] = k_frag(buf, ks + SPIPE, n, g);
-      ra1[slot] = k_frag(buf, ks + SPIPE, 16 + n, g);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep the ring order
-  }
-  return softmax_from_scores(s0, s1, valid, scale_log2, g, m_ref, l_part, corr, rescaled);
-}
-
-// V^T fragment of dim tile mt (16 dims) for the 32 rows of a tile: through
-// the LDS transpose read, source lane s of group g points at keys s/4 (+16
-// for the upper half), dims 16mt + 4(s%4)..+3.
-__device__ __forceinline__ v8bf vt_frag(const LDS_AS uint8_t* __restrict__ nope, int mt, int n, int g) {
-  const LDS_AS uint8_t* vsrc0 = nope + (4 * g + (n >> 2)) * NOPE_STRIDE + 8 * (n & 3) + 32 * mt;
-  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)vsrc0);
-  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(vsrc0 + 16 * NOPE_STRIDE));
-  return __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// Scores, online softmax and value product for one tile held in `buf`.
-// `valid` has bit j set when row j of the tile is a selected row.
-__device__ __forceinline__ void attend_tile(const LDS_AS uint8_t* __restrict__ buf, u32 valid, const v8bf* qf,
-                                           float scale_log2, int n, int g, float& m_ref, float& l_part, v4f* o) {
-  float corr;
-  bool rescaled;
-  const v8bf pb = tile_softmax(buf, valid, qf, scale_log2, n, g, m_ref, l_part, corr, rescaled);
-  if (rescaled) {
-#pragma unroll
-    for (int mt = 0; mt < AT_DV / 16; ++mt) o[mt] *= corr;
-  }
-  // ---- values O^T += V^T P^T; P already sits in the B-operand layout
+  // ---- values O^T += V^T P^T; V^T rows through the LDS transpose read:
+  // source lane s of group g points at keys kb + s/4, dims 16mt + 4(s%4)..+3
+  const LDS_AS uint8_t* vsrc0 = nope + (4 * g + (n >> 2)) * NOPE_STRIDE + 8 * (n & 3);
+  const LDS_AS uint8_t* vsrc1 = vsrc0 + 16 * NOPE_STRIDE;
 #pragma unroll
   for (int mt = 0; mt < AT_DV / 16; ++mt) {
-    o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt_frag(buf, mt, n, g), pb, o[mt], 0, 0, 0);
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(vsrc0 + 32 * mt));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(vsrc1 + 32 * mt));
+    const v8bf av = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, o[mt], 0, 0, 0);
     if ((mt & 7) == 7) __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -345,333 +285,6 @@ __global__ __launch_bounds__(NW * 64) void sparse_mla_kernel(const uint16_t* __r
   }
 }
 
-// The same attention for 64 heads per workgroup (H a multiple of 64), with
-// the value product split by dims instead of heads and the tile loop
-// software-pipelined.  Each wave forms the scores and P of its own 16 heads
-// and writes P (already in the B-operand layout) to LDS; wave w then computes
-// O^T for dims 128w..128w+127 of all 64 heads, so it reads only its quarter
-// of V^T (16 transposed reads per tile instead of 64) and uses each V^T
-// fragment for the four head tiles.  Step j of the loop interleaves the value
-// product of tile j with the score product of tile j+1 and forms P of tile
-// j+1 beside the rest of the value product, while tile j+2 moves from memory
-// into LDS by DMA (no staging registers); one barrier per step publishes P
-// and the staged tile.  Three LDS
-// tile buffers and three P buffers rotate.  A head whose reference maximum
-// moves passes its factor to the other waves beside P.  Every output element
-// accumulates the same MFMA products in the same order as in
-// sparse_mla_kernel, so the two agree bit for bit.
-constexpr int SP_P_BYTES = 4 * 64 * 16;  // P of the four waves: [head tile][lane][8 bf16]
-
-__global__ __launch_bounds__(256) void sparse_mla_pipe_kernel(const uint16_t* __restrict__ q,
-                                                              const uint8_t* __restrict__ kv,
-                                                              const int32_t* __restrict__ idx,
-                                                              const int32_t* __restrict__ seq_id, Layout lay, int H,
-                                                              int k, int split_len, int n_splits, float scale_log2,
-                                                              uint16_t* __restrict__ out, float* __restrict__ lse,
-                                                              uint16_t* __restrict__ ws_o, float* __restrict__ ws_ml,
-                                                              int n_tokens) {
-  constexpr int NW = 4;
-  constexpr int NT = NW * 64;
-  constexpr int DT = AT_DV / 16 / NW;  // dim tiles per wave: 8
-  constexpr int NB = 3;                // tile buffers and P buffers
-  constexpr int SPIPE = 4;             // K fragments read ahead
-  constexpr int PF = 4;                // L2 warm-up distance in tiles
-  // separate arrays, so that reads of one buffer are seen not to alias the
-  // DMA in flight into another
-  __shared__ __attribute__((aligned(16))) uint8_t s_b0[BUF_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t s_b1[BUF_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t s_b2[BUF_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t s_p[NB * SP_P_BYTES];
-  __shared__ float s_corr[NB][NW * 16];
-  __shared__ __attribute__((aligned(16))) u32 s_flag[NB][NW];
-  __shared__ float s_l[NW * 16];
-  __shared__ u32 s_row[AT_MAX_SPLIT];
-  __shared__ u32 s_valid[AT_MAX_SPLIT / AT_TILE];
-  __shared__ __attribute__((aligned(16))) uint8_t s_trash[256];
-
-  // Workgroup -> (token, split, head group).  Workgroups are dealt to the 8
-  // XCDs round-robin by linear id; unit u = (t * n_splits + split) * n_hg + hg
-  // goes to XCD u / (grid / 8), so every split and head group of a token (and
-  // neighbouring tokens) share one XCD's L2: the token's Q is fetched from
-  // memory once, and the head groups of a split gather the same rows.
-  const int n_hg = H / (16 * NW);
-  const int lin = blockIdx.x;
-  const int unit = (lin & 7) * (int)(gridDim.x >> 3) + (lin >> 3);
-  const int hg = unit % n_hg;
-  const int pair = unit / n_hg;
-  const int t = pair / n_splits;
-  const int split = pair - t * n_splits;
-  if (t >= n_tokens) return;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15;
-  const int g = lane >> 4;
-  const int h0 = hg * (16 * NW) + wid * 16;  // first head of this wave's scores
-  const int b = seq_id[t];
-  const int32_t* __restrict__ idx_row = idx + (int64_t)t * k;
-  const int j_begin = split * split_len;
-  const int nrows = max(0, min(k, j_begin + split_len) - j_begin);
-
-  v8bf qf[AT_D / 32];
-  auto load_q = [&] {
-    const uint16_t* qrow = q + ((int64_t)t * H + h0 + n) * AT_D + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < AT_D / 32; ++ks) qf[ks] = *reinterpret_cast<const v8bf*>(qrow + 32 * ks);
-  };
-  __shared__ u32 scan_scratch[NT / 64 + 1];
-  const int nvalid = compact_selection<NT>(idx_row + j_begin, nrows, lay, b, s_row, s_valid, scan_scratch, tid, load_q);
-  const int ntiles = (nvalid + AT_TILE - 1) / AT_TILE;
-
-  float m_ref = -INFINITY;  // reference max (log2 units) of score head h0+n
-  float l_part = 0.f;
-  v4f o[DT][NW];            // O^T: dims 128 wid + 16 dt, head tile ht
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int ht = 0; ht < NW; ++ht) o[dt][ht] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  LDS_AS uint8_t* const bufs[NB] = {(LDS_AS uint8_t*)s_b0, (LDS_AS uint8_t*)s_b1, (LDS_AS uint8_t*)s_b2};
-  LDS_AS uint8_t* pl = (LDS_AS uint8_t*)s_p;
-  lds_barrier();  // s_row / s_valid visible; the Q loads stay in flight
-
-  // P, and the factors of heads whose reference moved, of a tile into P buffer pi
-  auto publish = [&](int pi, v8bf pb, float corr, bool rescaled) {
-    *reinterpret_cast<LDS_AS v8bf*>(pl + pi * SP_P_BYTES + (wid * 64 + lane) * 16) = pb;
-    if (rescaled && g == 0) s_corr[pi][wid * 16 + n] = corr;
-    if (lane == 0) s_flag[pi][wid] = rescaled ? 1u : 0u;
-  };
-  // before the value product of the tile in P buffer pi: read the four head
-  // tiles' P and the rescale flags, then rescale the heads whose reference
-  // moved (read_p issues the LDS reads; rescale waits for the flags only)
-  auto read_p = [&](int pi, v8bf* pbs) -> v4i {
-    const v4i fl = *reinterpret_cast<const LDS_AS v4i*>((LDS_AS u32*)&s_flag[pi][0]);
-#pragma unroll
-    for (int ht = 0; ht < NW; ++ht)
-      pbs[ht] = *reinterpret_cast<const LDS_AS v8bf*>(pl + pi * SP_P_BYTES + (ht * 64 + lane) * 16);
-    return fl;
-  };
-  auto rescale = [&](int pi, v4i fl) {
-    u32 flag[NW];
-#pragma unroll
-    for (int ht = 0; ht < NW; ++ht) flag[ht] = __builtin_amdgcn_readfirstlane((u32)fl[ht]);
-    if (flag[0] | flag[1] | flag[2] | flag[3]) {
-#pragma unroll
-      for (int ht = 0; ht < NW; ++ht) {
-        if (flag[ht]) {
-          const float c = s_corr[pi][ht * 16 + n];
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) o[dt][ht] *= c;
-        }
-      }
-    }
-  };
-  // rows of tile i (tiles past the last one repeat it: the same traffic
-  // pattern on every path, and never read)
-  auto tile_rows = [&](int i) { return s_row + min(i, ntiles - 1) * AT_TILE; };
-  // Warm L2 with the rows of a tile: one 4-byte read per 128-byte line (9
-  // lines a row; wave w takes lines 72w..72w+71 in two reads per lane, the
-  // second repeating lines 72w+64..+71), by DMA into a scratch word of LDS
-  // that nobody reads, so no register waits for them.
-  const int wl0 = 72 * wid + lane, wl1 = 72 * wid + 64 + (lane & 7);  // this lane's warm-up lines
-  auto warm_rows = [&](const u32* rows, u32* pw) {
-    pw[0] = rows[wl0 / 9];
-    pw[1] = rows[wl1 / 9];
-  };
-  auto warm_l2 = [&](const u32* pw) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int line = i == 0 ? wl0 : wl1;
-      const u32 phys = pw[i] & ~ROW_INVALID;
-      __builtin_amdgcn_global_load_lds(kv + (int64_t)phys * AT_ROW_BYTES + 128 * (line - 9 * (line / 9)),
-                                       (LDS_AS void*)s_trash, 4, 0, 0);
-    }
-  };
-  // the rows a wave stages of a tile: no-rope rows 8 wid .. 8 wid + 7
-  // (wave-uniform) and this lane's rope row 8 wid + lane/8
-  struct DmaRows {
-    v4i a, b;
-    u32 rope;
-  };
-  auto dma_rows = [&](const u32* rows) {
-    DmaRows d;
-    d.a = *reinterpret_cast<const v4i*>(rows + 8 * wid);
-    d.b = *reinterpret_cast<const v4i*>(rows + 8 * wid + 4);
-    d.rope = rows[8 * wid + (lane >> 3)];
-    return d;
-  };
-  const u32 lane16 = 16u * (u32)lane;
-  auto dma_issue = [&](LDS_AS uint8_t* buf, const DmaRows& d) {
-    // row bases in scalar registers (uniform), so each DMA is one
-    // instruction with a scalar base and the lane's 16-byte offset
-    const uint8_t* base[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const u32 phys = __builtin_amdgcn_readfirstlane((u32)(i < 4 ? d.a[i] : d.b[i - 4])) & ~ROW_INVALID;
-      base[i] = kv + (uint64_t)phys * AT_ROW_BYTES;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds(base[i] + lane16, (LDS_AS void*)(buf + (8 * wid + i) * NOPE_STRIDE), 16, 0, 0);
-    const int r = 8 * wid + (lane >> 3);
-    const u32 phys = d.rope & ~ROW_INVALID;
-    __builtin_amdgcn_global_load_lds(kv + (int64_t)phys * AT_ROW_BYTES + 1024 + 16 * ((lane & 7) ^ (r & 7)),
-                                     (LDS_AS void*)(buf + NOPE_BYTES + 8 * wid * 128), 16, 0, 0);
-  };
-
-  if (ntiles > 0) {
-    dma_issue(bufs[0], dma_rows(tile_rows(0)));
-    dma_issue(bufs[1], dma_rows(tile_rows(1)));
-    u32 pw[2];
-    warm_rows(tile_rows(2), pw);
-    warm_l2(pw);
-    warm_rows(tile_rows(3), pw);
-    warm_l2(pw);
-    __builtin_amdgcn_s_waitcnt(DSA_VMCNT(4));  // tiles 0 and 1 landed
-    lds_barrier();
-    float corr;
-    bool rescaled;
-    const v8bf pb = tile_softmax(bufs[0], s_valid[0], qf, scale_log2, n, g, m_ref, l_part, corr, rescaled);
-    publish(0, pb, corr, false);  // O is still zero: scaling it changes nothing
-    lds_barrier();  // P of tile 0 published
-  }
-
-  // Steps j = 0 .. ntiles-2, three per trip so that buffer indices are
-  // compile-time constants; the last tile's value product follows the loop.
-  // The row indices a step needs for its DMA and L2 warm-up are read during
-  // the step before, so the step issues them without waiting on LDS.
-  DmaRows nd = dma_rows(tile_rows(2));
-  u32 npw[2];
-  warm_rows(tile_rows(PF), npw);
-  for (int j0 = 0; j0 + 1 < ntiles; j0 += NB) {
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int j = j0 + u;
-      if (j + 1 >= ntiles) break;  // uniform
-      const LDS_AS uint8_t* bv = bufs[u];             // tile j: values
-      const LDS_AS uint8_t* bs = bufs[(u + 1) % NB];  // tile j+1: scores
-      v8bf ra0[SPIPE], ra1[SPIPE], av[2], pbs[NW];
-      // rescale flags first, alone, so that waiting for them is one LDS trip
-      rescale(u, *reinterpret_cast<const LDS_AS v4i*>((LDS_AS u32*)&s_flag[u][0]));
-      __builtin_amdgcn_sched_barrier(0);
-      // tile j+2 into the buffer of tile j-1 (free since the last barrier),
-      // then the rows of tile j+PF into L2
-      dma_issue(bufs[(u + 2) % NB], nd);
-      warm_l2(npw);
-      read_p(u, pbs);
-#pragma unroll
-      for (int r = 0; r < SPIPE; ++r) {
-        ra0[r] = k_frag(bs, r, n, g);
-        ra1[r] = k_frag(bs, r, 16 + n, g);
-      }
-      av[0] = vt_frag(bv, wid * DT + 0, n, g);
-      av[1] = vt_frag(bv, wid * DT + 1, n, g);
-      // scores of tile j+1 with the first half of tile j's value product
-      v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < AT_D / 32; ++ks) {
-        const int r = ks % SPIPE;
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra0[r], qf[ks], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra1[r], qf[ks], s1, 0, 0, 0);
-        if (ks + SPIPE < AT_D / 32) {
-          ra0[r] = k_frag(bs, ks + SPIPE, n, g);
-          ra1[r] = k_frag(bs, ks + SPIPE, 16 + n, g);
-        }
-        if (ks >= 2) {
-          // value product, dim tiles 0..3: one MFMA per step
-          const int m = ks - 2, dt = m >> 2, ht = m & 3;
-          o[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[dt & 1], pbs[ht], o[dt][ht], 0, 0, 0);
-          if (ht == 3) av[dt & 1] = vt_frag(bv, wid * DT + dt + 2, n, g);
-        }
-        if (ks == 8) {
-          nd = dma_rows(tile_rows(j + 3));  // for the next step
-          warm_rows(tile_rows(j + 1 + PF), npw);
-        }
-        __builtin_amdgcn_sched_barrier(0);  // keep the interleave
-      }
-      // P of tile j+1, beside the second half of tile j's value product
-      float corr;
-      bool rescaled;
-      const v8bf pb = softmax_from_scores_nb(s0, s1, s_valid[j + 1], scale_log2, g, m_ref, l_part, corr, rescaled);
-#pragma unroll
-      for (int dt = DT / 2; dt < DT; ++dt) {
-#pragma unroll
-        for (int ht = 0; ht < NW; ++ht)
-          o[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[dt & 1], pbs[ht], o[dt][ht], 0, 0, 0);
-        if (dt + 2 < DT) av[dt & 1] = vt_frag(bv, wid * DT + dt + 2, n, g);
-      }
-      publish((u + 1) % NB, pb, corr, rescaled);
-      __builtin_amdgcn_s_waitcnt(DSA_VMCNT(2));  // tile j+2 landed (the two L2 reads may still fly)
-      lds_barrier();  // tile j+2 staged, P of tile j+1 published
-    }
-  }
-  if (ntiles > 0) {
-    // value product of the last tile
-    const int jl = ntiles - 1;
-    const int ul = jl % NB;
-    const LDS_AS uint8_t* bv = (ul == 0) ? bufs[0] : (ul == 1) ? bufs[1] : bufs[2];
-    v8bf pbs[NW];
-    rescale(ul, read_p(ul, pbs));
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const v8bf a = vt_frag(bv, wid * DT + dt, n, g);
-#pragma unroll
-      for (int ht = 0; ht < NW; ++ht) o[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pbs[ht], o[dt][ht], 0, 0, 0);
-    }
-  }
-
-  // ---- finish: l of the score heads over the four lane groups, shared
-  float l = l_part;
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-  if (g == 0) s_l[wid * 16 + n] = l;
-  lds_barrier();
-  if (n_splits == 1) {
-#pragma unroll
-    for (int ht = 0; ht < NW; ++ht) {
-      const float lh = s_l[ht * 16 + n];
-      const float inv = (lh > 0.f) ? 1.f / lh : 0.f;
-      const int h = hg * 64 + ht * 16 + n;
-      uint16_t* orow = out + ((int64_t)t * H + h) * AT_DV + 4 * g + 16 * (wid * DT);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        v2i pk;
-        pk[0] = (int)((u32)f2bf(o[dt][ht][0] * inv) | ((u32)f2bf(o[dt][ht][1] * inv) << 16));
-        pk[1] = (int)((u32)f2bf(o[dt][ht][2] * inv) | ((u32)f2bf(o[dt][ht][3] * inv) << 16));
-        *reinterpret_cast<v2i*>(orow + 16 * dt) = pk;
-      }
-    }
-    if (lse != nullptr && g == 0)
-      lse[(int64_t)t * H + h0 + n] = (l > 0.f) ? (m_ref + log2f(l)) * 0.69314718055994531f : -INFINITY;
-  } else {
-    // split partials in the fragment order the combine reads: per 16 heads
-    // [dim-tile pair][lane][8]; this wave's pairs are 4 wid .. 4 wid + 3
-#pragma unroll
-    for (int ht = 0; ht < NW; ++ht) {
-      const float lh = s_l[ht * 16 + n];
-      const float inv = (lh > 0.f) ? 1.f / lh : 0.f;
-      const int64_t base = ((int64_t)t * n_splits + split) * H + hg * 64 + ht * 16;
-      uint16_t* orow = ws_o + base * AT_DV + 8 * lane;
-#pragma unroll
-      for (int dp = 0; dp < DT / 2; ++dp) {
-        v4i pk;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const v4f& a = o[2 * dp + i][ht];
-          pk[2 * i] = (int)((u32)f2bf(a[0] * inv) | ((u32)f2bf(a[1] * inv) << 16));
-          pk[2 * i + 1] = (int)((u32)f2bf(a[2] * inv) | ((u32)f2bf(a[3] * inv) << 16));
-        }
-        *reinterpret_cast<v4i*>(orow + 512 * (wid * (DT / 2) + dp)) = pk;
-      }
-    }
-    if (g == 0) {
-      const int64_t slot_o = ((int64_t)t * n_splits + split) * H + h0 + n;
-      ws_ml[slot_o * 2 + 0] = m_ref;
-      ws_ml[slot_o * 2 + 1] = l;
-    }
-  }
-}
-
 // Merge the splits: with o_s the normalised partial of split s,
 //   O = sum_s w_s o_s / sum_s w_s,   w_s = 2^(m_s - M) l_s,   M = max_s m_s.
 // The partials are in the attention kernel's fragment order (per 16 heads:
@@ -811,12 +424,8 @@ static hipError_t launch_attn_t(int T, int H, const uint16_t* q, const uint16_t*
   const int pairs = T * n_splits;
   const int blocks = ((pairs + 7) / 8) * 8 * n_hg;
   const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv);
-  if (!DENSE && H % 64 == 0)
-    hipLaunchKernelGGL(sparse_mla_pipe_kernel, dim3(blocks), dim3(4 * 64), 0, stream, q, kvb, idx, seq_id, lay, H,
-                       k, split_len, n_splits, scale_log2, out, lse, ws_o, ws_ml, T);
-  else
-    hipLaunchKernelGGL((sparse_mla_kernel<4, DENSE>), dim3(blocks), dim3(4 * 64), 0, stream, q, kvb, idx, seq_id, pos,
-                       lay, H, k, split_len, n_splits, scale_log2, out, lse, ws_o, ws_ml, T);
+  hipLaunchKernelGGL((sparse_mla_kernel<4, DENSE>), dim3(blocks), dim3(4 * 64), 0, stream, q, kvb, idx, seq_id, pos,
+                     lay, H, k, split_len, n_splits, scale_log2, out, lse, ws_o, ws_ml, T);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_splits == 1) return e;
   const int waves = T * (H / 16) * (AT_DV / 32);

@@ -1,9 +1,9 @@
-"""The sparse attention with 64 or 128 heads (value product split by dims
-over the workgroup's waves, P shared through LDS) against the same heads
-taken 16 at a time (one wave per head group, the whole value product in that
-wave).  Heads do not interact, and both routes accumulate every output
-element from the same matrix-core products in the same order over the same
-splits, so out and lse must agree bit for bit.
+"""The sparse attention with 64 or 128 heads against the same heads taken 16
+at a time.  Heads do not interact: each wave of the attention kernel holds
+its own 16 heads, and a call with 16 heads runs the same wave code over the
+same splits of the selection (the split count depends on the token count and
+the number of 64-head groups, equal here), so out and lse must agree bit for
+bit whatever the head count of the call.
 """
 
 import pytest
