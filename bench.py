@@ -43,9 +43,9 @@ REPLICAS = 4
 # device copy in the same pass.  Valid only for the kernel sources they were
 # taken on (hash below); otherwise the field is reported as null.
 TRAFFIC = {
-    "sources_sha256": "23a62ccf96890fc35f66d0c9ef4d2dfc1b2033d978fca80c3b7bdaae4bd07e6c",
-    # FETCH_SIZE 135767.5 KiB/launch x 1.99982 (copy: 131083.9 KiB counted for 262144 KiB read)
-    "fetch_bytes": 278026607,
+    "sources_sha256": "fd012d6308c027b2ee7f211949ed0a5efb0423a09767dbd9a1560a6b3554a5bc",
+    # FETCH_SIZE 135767.5 KiB/launch x 1.99981 (copy: 131084.2 KiB counted for 262144 KiB read)
+    "fetch_bytes": 278026032,
     # WRITE_SIZE 8192.0 KiB/launch x 1.0 (copy: 262144 KiB counted for 262144 KiB written)
     "write_bytes": 8388608,
 }
