@@ -156,25 +156,50 @@ __global__ __launch_bounds__(PJ_NT) void proj_gemm_kernel(const uint16_t* __rest
   }
 }
 
-// V = Nq / 256 query values per thread.  The split partial sums are added in
-// split order, so the result does not depend on the launch.
-template <int V>
-__global__ __launch_bounds__(PJ_NT) void proj_finish_kernel(const float* __restrict__ part, int T, int N, int Nq,
+// V = Nq / NT query values per thread: from V = 4 on, groups of four
+// consecutive values at 4 tid + 4 NT c (16-byte loads, consecutive threads
+// on consecutive bytes), else single values at tid + NT e.  A wide query
+// (8192 values) takes 1024 threads, so that all of a token's partial sums are
+// in flight at once.  The split partial sums are added in split order, so
+// the result does not depend on the launch.
+template <int V, int NT>
+__global__ __launch_bounds__(NT) void proj_finish_kernel(const float* __restrict__ part, int T, int N, int Nq,
                                                             int Nw, int Nk, int splits, uint8_t* __restrict__ q8,
                                                             float* __restrict__ qs, float* __restrict__ w,
                                                             float* __restrict__ k_new) {
-  __shared__ float red[PJ_NT / 64];
+  __shared__ float red[NT / 64];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const float* __restrict__ row = part + (int64_t)t * N;
   const int64_t zs = (int64_t)T * N;
+  auto at = [&](int e) { return V >= 4 ? 4 * tid + 4 * NT * (e >> 2) + (e & 3) : tid + NT * e; };
 
   float v[V];
+  if constexpr (V >= 4) {
 #pragma unroll
-  for (int e = 0; e < V; ++e) v[e] = row[tid * V + e];
-  for (int z = 1; z < splits; ++z)
+    for (int c = 0; c < V / 4; ++c) {
+      const float4 a = *reinterpret_cast<const float4*>(row + 4 * tid + 4 * NT * c);
+      v[4 * c + 0] = a.x;
+      v[4 * c + 1] = a.y;
+      v[4 * c + 2] = a.z;
+      v[4 * c + 3] = a.w;
+    }
+    for (int z = 1; z < splits; ++z)
 #pragma unroll
-    for (int e = 0; e < V; ++e) v[e] += row[z * zs + tid * V + e];
+      for (int c = 0; c < V / 4; ++c) {
+        const float4 a = *reinterpret_cast<const float4*>(row + z * zs + 4 * tid + 4 * NT * c);
+        v[4 * c + 0] += a.x;
+        v[4 * c + 1] += a.y;
+        v[4 * c + 2] += a.z;
+        v[4 * c + 3] += a.w;
+      }
+  } else {
+#pragma unroll
+    for (int e = 0; e < V; ++e) v[e] = row[at(e)];
+    for (int z = 1; z < splits; ++z)
+#pragma unroll
+      for (int e = 0; e < V; ++e) v[e] += row[z * zs + at(e)];
+  }
   float amax = 0.f;
 #pragma unroll
   for (int e = 0; e < V; ++e) amax = fmaxf(amax, fabsf(v[e]));
@@ -182,25 +207,27 @@ __global__ __launch_bounds__(PJ_NT) void proj_finish_kernel(const float* __restr
   for (int s = 1; s < 64; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 64));
   if ((tid & 63) == 0) red[tid >> 6] = amax;
   __syncthreads();
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  amax = red[0];
+#pragma unroll
+  for (int i = 1; i < NT / 64; ++i) amax = fmaxf(amax, red[i]);
   const float scale = e4m3fn_scale(amax);
 
-  uint8_t* __restrict__ dst = q8 + (int64_t)t * Nq + tid * V;
+  uint8_t* __restrict__ dst = q8 + (int64_t)t * Nq;
   if constexpr (V >= 4) {
 #pragma unroll
     for (int c = 0; c < V / 4; ++c) {
       u32 word = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) word |= e4m3fn_quantise(v[4 * c + e], scale) << (8 * e);
-      reinterpret_cast<u32*>(dst)[c] = word;
+      *reinterpret_cast<u32*>(dst + 4 * tid + 4 * NT * c) = word;
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < V; ++e) dst[e] = (uint8_t)e4m3fn_quantise(v[e], scale);
+    for (int e = 0; e < V; ++e) dst[at(e)] = (uint8_t)e4m3fn_quantise(v[e], scale);
   }
   if (tid == 0) qs[t] = scale;
 
-  for (int j = tid; j < Nw + Nk; j += PJ_NT) {
+  for (int j = tid; j < Nw + Nk; j += NT) {
     float s = row[Nq + j];
     for (int z = 1; z < splits; ++z) s += row[z * zs + Nq + j];
     if (j < Nw)
@@ -250,14 +277,14 @@ hipError_t launch_indexer_project(int T, int d, int H_I, int D_I, const uint16_t
                        part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-#define DSA_PJ_FINISH(VV)                                                                                         \
-  hipLaunchKernelGGL(proj_finish_kernel<VV>, dim3(T), dim3(PJ_NT), 0, stream, part, T, N, Nq, Nw, Nk, splits, q8, qs, \
-                     w, k_new)
-  switch (Nq / PJ_NT) {
-    case 32: DSA_PJ_FINISH(32); break;
-    case 16: DSA_PJ_FINISH(16); break;
-    case 2: DSA_PJ_FINISH(2); break;
-    case 1: DSA_PJ_FINISH(1); break;
+#define DSA_PJ_FINISH(VV, NTT)                                                                                  \
+  hipLaunchKernelGGL((proj_finish_kernel<VV, NTT>), dim3(T), dim3(NTT), 0, stream, part, T, N, Nq, Nw, Nk, splits, q8, \
+                     qs, w, k_new)
+  switch (Nq) {
+    case 8192: DSA_PJ_FINISH(8, 1024); break;
+    case 4096: DSA_PJ_FINISH(4, 1024); break;
+    case 512: DSA_PJ_FINISH(2, 256); break;
+    case 256: DSA_PJ_FINISH(1, 256); break;
     default: return hipErrorInvalidValue;
   }
 #undef DSA_PJ_FINISH
