@@ -402,6 +402,28 @@ int dsa_forward_noalloc(const dsa_queries* q, const dsa_kv_layout* layout, int32
 #define DSA_OP_KL_TARGET_DENSE 9
 size_t dsa_workspace_bytes(int32_t op, int32_t T, int32_t max_len, int32_t H, int32_t k);
 
+/* ---------------------------------------------------------------------------
+ * dsa_workspace_layout: the regions a call with these sizes carves out of its
+ * workspace, for checking and debugging.  Same arguments as
+ * dsa_workspace_bytes.  Each region starts on a 256-byte boundary at `offset`
+ * bytes from the workspace base; regions a sub-step keeps inside its own part
+ * of the workspace are listed one by one, with that part's name in `parent`
+ * (NULL for a region of the call itself); names are static strings.  The
+ * regions are disjoint and, with each size rounded up to 256 bytes, tile
+ * [0, dsa_workspace_bytes(...)).  The call writes at most max_regions entries
+ * and returns the number of regions (0 when the operation needs no
+ * workspace), or DSA_ERR_INVALID_ARG (negative sizes or max_regions, regions
+ * NULL with max_regions > 0, unknown op).  Host only: no device is touched.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  const char* parent;
+  const char* name;
+  uint64_t offset;
+  uint64_t bytes;
+} dsa_ws_region;
+int32_t dsa_workspace_layout(int32_t op, int32_t T, int32_t max_len, int32_t H, int32_t k, dsa_ws_region* regions,
+                             int32_t max_regions);
+
 /* Static string for a status code (never NULL). */
 const char* dsa_status_str(int32_t status);
 

@@ -45,10 +45,15 @@ class dsa_kv_layout(ctypes.Structure):
                 ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("seq_capacity", ctypes.c_int64)]
 
 
+class dsa_ws_region(ctypes.Structure):
+    _fields_ = [("parent", ctypes.c_char_p), ("name", ctypes.c_char_p), ("offset", ctypes.c_uint64),
+                ("bytes", ctypes.c_uint64)]
+
+
 EXPORTS = ("dsa_cache_write", "dsa_indexer_project", "dsa_indexer_logits", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_attn",
            "dsa_sparse_mla_attn_bwd", "dsa_sparse_mla_attn_bwd_dq", "dsa_sparse_mla_attn_bwd_dkv",
            "dsa_indexer_kl_target", "dsa_indexer_kl_target_dense", "dsa_indexer_kl", "dsa_masked_dense_attn", "dsa_forward", "dsa_forward_noalloc",
-           "dsa_workspace_bytes",
+           "dsa_workspace_bytes", "dsa_workspace_layout",
            "dsa_status_str", "dsa_abi_version")
 
 _lib = None
@@ -82,6 +87,8 @@ def lib() -> ctypes.CDLL:
     L.dsa_forward_noalloc.argtypes = [Q, KV, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, i32, f32, vp, vp, vp, vp]
     L.dsa_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     L.dsa_workspace_bytes.restype = sz
+    L.dsa_workspace_layout.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(dsa_ws_region), i32]
+    L.dsa_workspace_layout.restype = i32
     L.dsa_status_str.argtypes = [i32]
     L.dsa_status_str.restype = ctypes.c_char_p
     L.dsa_abi_version.restype = i32
@@ -146,6 +153,17 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
 
 def dsa_workspace_bytes(op: int, T: int, max_len: int, H: int, k: int) -> int:
     return int(lib().dsa_workspace_bytes(op, T, max_len, H, k))
+
+
+def dsa_workspace_layout(op: int, T: int, max_len: int, H: int, k: int):
+    """[(parent or None, name, offset, bytes)] of the regions the call carves."""
+    n = int(lib().dsa_workspace_layout(op, T, max_len, H, k, None, 0))
+    _check(min(n, 0), "dsa_workspace_layout")
+    regions = (dsa_ws_region * max(n, 1))()
+    n2 = int(lib().dsa_workspace_layout(op, T, max_len, H, k, regions, n))
+    assert n2 == n
+    return [(None if r.parent is None else r.parent.decode(), r.name.decode(), int(r.offset), int(r.bytes))
+            for r in regions[:n]]
 
 
 def dsa_status_str(status: int) -> str:

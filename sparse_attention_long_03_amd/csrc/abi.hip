@@ -54,18 +54,26 @@ constexpr int32_t kFusedMinT = 2048;
 
 bool forward_fused(int32_t T) { return T >= kFusedMinT; }
 
-size_t forward_ws(int32_t T, int32_t max_len, int32_t H, int32_t k, bool with_idx) {
+// dsa_forward's workspace: the selection (when the caller passes no idx_out),
+// then either the fused selection's candidate lists (from kFusedMinT query
+// tokens) or the logits and the top-k workspace, then the attention's split
+// partials.
+WsLayout forward_layout(int32_t T, int32_t max_len, int32_t H, int32_t k, bool with_idx) {
   const int64_t ld = ((int64_t)max_len + 3) & ~int64_t(3);
-  size_t s = 0;
-  if (with_idx) s += align256((size_t)T * k * 4);       // selection
+  WsLayout L;
+  if (with_idx) L.add("sel", (size_t)T * k * 4);
   if (forward_fused(T)) {
-    s += align256(fused_topk_workspace_bytes(T, fused_topk_cap(max_len, k)));
+    L.add_sub("fused", fused_topk_layout(T, fused_topk_cap(max_len, k)));
   } else {
-    s += align256((size_t)T * ld * 4);                  // logits
-    s += topk_workspace_bytes(T, max_len, k);
+    L.add("logits", (size_t)T * ld * 4);
+    L.add_sub("topk", topk_layout(T, max_len, k));
   }
-  s += align256(attn_workspace_bytes(T, H, k));
-  return s;
+  L.add_sub("attn", attn_layout(T, H, k));
+  return L;
+}
+
+size_t forward_ws(int32_t T, int32_t max_len, int32_t H, int32_t k, bool with_idx) {
+  return forward_layout(T, max_len, H, k, with_idx).total;
 }
 
 // the indexer's inputs (shared by the logits and the fused selection calls)
@@ -141,6 +149,29 @@ size_t dsa_workspace_bytes(int32_t op, int32_t T, int32_t max_len, int32_t H, in
       return proj_supported(H, k, max_len) ? proj_workspace_bytes(T, max_len, H, k) : 0;
     default: return 0;
   }
+}
+
+int32_t dsa_workspace_layout(int32_t op, int32_t T, int32_t max_len, int32_t H, int32_t k, dsa_ws_region* regions,
+                             int32_t max_regions) {
+  if (T < 0 || max_len < 0 || H < 0 || k < 0 || max_regions < 0 || (max_regions > 0 && regions == nullptr))
+    return DSA_ERR_INVALID_ARG;
+  if (dsa_workspace_bytes(op, T, max_len, H, k) == 0) return 0;  // none needed, or not supported
+  WsLayout L;
+  switch (op) {
+    case DSA_OP_TOPK: L = topk_layout(T, max_len, k); break;
+    case DSA_OP_ATTN: L = attn_layout(T, H, k); break;
+    case DSA_OP_FORWARD: L = forward_layout(T, max_len, H, k, true); break;
+    case DSA_OP_INDEXER_TOPK: L = fused_topk_layout(T, fused_topk_cap(max_len, k)); break;
+    case DSA_OP_DENSE_ATTN: L = dense_attn_layout(T, H, max_len); break;
+    case DSA_OP_ATTN_BWD: L = attn_bwd_layout(T, H, k); break;
+    case DSA_OP_INDEXER_KL: L = kl_layout(T, k); break;
+    case DSA_OP_KL_TARGET_DENSE: L = kl_target_dense_layout(T, H, max_len); break;
+    case DSA_OP_INDEXER_PROJ: L = proj_layout(T, max_len, H, k); break;  // (T, d, H_I, D_I)
+    default: return DSA_ERR_INVALID_ARG;
+  }
+  for (int i = 0; i < L.nflat && i < max_regions; ++i)
+    regions[i] = dsa_ws_region{L.flat[i].parent, L.flat[i].name, (uint64_t)L.flat[i].off, (uint64_t)L.flat[i].bytes};
+  return L.nflat;
 }
 
 int dsa_indexer_logits(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,
@@ -414,26 +445,19 @@ int run_forward(const dsa_queries* q, const Layout& lay, int32_t H_I, int32_t D_
                 const void* q_bf16, const void* kv_bf16, int32_t k, float sm_scale, void* out_bf16, float* lse,
                 int32_t* idx_out, void* workspace, hipStream_t stream) {
   const int64_t ld = ((int64_t)q->max_len + 3) & ~int64_t(3);
-  char* p = static_cast<char*>(workspace);
-  int32_t* idx = idx_out;
-  if (idx == nullptr) {
-    idx = reinterpret_cast<int32_t*>(p);
-    p += align256((size_t)q->T * k * 4);
-  }
+  const WsLayout L = forward_layout(q->T, q->max_len, H, k, idx_out == nullptr);
+  int32_t* idx = idx_out != nullptr ? idx_out : static_cast<int32_t*>(L.at(workspace, L.index("sel")));
   hipError_t e;
   if (forward_fused(q->T)) {
     // many query tokens: indexer and selection in one pass, no logits stored
     const int cap = fused_topk_cap(q->max_len, k);
-    void* ws_sel = p;
-    p += align256(fused_topk_workspace_bytes(q->T, cap));
+    void* ws_sel = L.at(workspace, L.index("fused"));
     e = launch_indexer_topk(q->T, q->max_len, H_I, D_I, iq_fp8, iq_scale, iw, ik_fp8, ik_scale, q->seq_id, q->pos,
                             lay, k, cap, idx, ws_sel, stream);
     if (e != hipSuccess) return DSA_ERR_HIP;
   } else {
-    float* logits = reinterpret_cast<float*>(p);
-    p += align256((size_t)q->T * ld * 4);
-    void* ws_topk = p;
-    p += topk_workspace_bytes(q->T, q->max_len, k);
+    float* logits = static_cast<float*>(L.at(workspace, L.index("logits")));
+    void* ws_topk = L.at(workspace, L.index("topk"));
     e = launch_topk_zero_hist(ws_topk, q->T, stream);
     if (e != hipSuccess) return DSA_ERR_HIP;
     e = launch_indexer(q->T, q->max_len, H_I, D_I, iq_fp8, iq_scale, iw, ik_fp8, ik_scale, q->seq_id, q->pos, lay,
@@ -442,7 +466,7 @@ int run_forward(const dsa_queries* q, const Layout& lay, int32_t H_I, int32_t D_
     e = launch_topk(logits, ld, q->pos, 1, q->T, q->max_len, k, idx, ws_topk, true, stream);
     if (e != hipSuccess) return DSA_ERR_HIP;
   }
-  void* ws_attn = p;
+  void* ws_attn = L.at(workspace, L.index("attn"));
   e = launch_attn(q->T, H, static_cast<const uint16_t*>(q_bf16), static_cast<const uint16_t*>(kv_bf16), idx, q->seq_id,
                   lay, k, sm_scale, static_cast<uint16_t*>(out_bf16), lse, ws_attn, stream);
   return hip_status(e);

@@ -541,11 +541,17 @@ bool kl_supported(int H_I, int D_I) { return H_I == KL_HI && D_I == KL_DI; }
 
 static int kl_kp(int k) { return ((k + KL_TILE - 1) / KL_TILE) * KL_TILE; }
 
-size_t kl_workspace_bytes(int T, int k) {
-  if (T == 0) return 0;
+WsLayout kl_layout(int T, int k) {
+  WsLayout L;
+  if (T == 0) return L;
   const size_t N = (size_t)T * kl_kp(k);
-  return align256(N * KL_DI * 2) + align256(N * 4) + row_scatter_workspace_bytes(N);
+  L.add("slot_dk", N * KL_DI * 2);
+  L.add("rows", N * 4);
+  L.add_sub("scatter", scatter_layout(N));
+  return L;
 }
+
+size_t kl_workspace_bytes(int T, int k) { return kl_layout(T, k).total; }
 
 bool kl_size_ok(int T, int k) { return (int64_t)T * kl_kp(k) < (int64_t(1) << 31); }
 
@@ -561,16 +567,20 @@ hipError_t launch_kl_target(int T, int H, const uint16_t* q, const uint16_t* kv,
 
 static int dense_target_chunks(int max_len) { return (max_len + AT_MAX_SPLIT - 1) / AT_MAX_SPLIT; }
 
-size_t kl_target_dense_workspace_bytes(int T, int H, int max_len) {
-  return align256((size_t)T * dense_target_chunks(max_len) * H * 2 * 4);
+WsLayout kl_target_dense_layout(int T, int H, int max_len) {
+  WsLayout L;
+  L.add("ml", (size_t)T * dense_target_chunks(max_len) * H * 2 * 4);  // per chunk and head: max, sum
+  return L;
 }
+
+size_t kl_target_dense_workspace_bytes(int T, int H, int max_len) { return kl_target_dense_layout(T, H, max_len).total; }
 
 hipError_t launch_kl_target_dense(int T, int H, int max_len, const uint16_t* q, const uint16_t* kv,
                                   const int32_t* seq_id, const int32_t* pos, const Layout& lay, float sm_scale,
                                   float* target, int64_t ld, float* lse_out, void* ws, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const int nch = dense_target_chunks(max_len);
-  float* ml = static_cast<float*>(ws);
+  float* ml = static_cast<float*>(kl_target_dense_layout(T, H, max_len).at(ws, 0));
   const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv);
   hipLaunchKernelGGL(kl_target_kernel<KT_DENSE_LSE>, dim3(T, nch), dim3(KT_NW * 64), 0, stream, q, kvb, nullptr,
                      seq_id, pos, lay, H, 0, sm_scale * LOG2E, nullptr, nullptr, (int64_t)0, ml, nch, nullptr, T);
@@ -588,16 +598,15 @@ hipError_t launch_kl(int T, const uint8_t* q8, const float* qs, const float* w, 
   if (T == 0) return hipSuccess;
   const int kp = kl_kp(k);
   const size_t N = (size_t)T * kp;
-  char* p = static_cast<char*>(ws);
-  uint16_t* slot_dk = reinterpret_cast<uint16_t*>(p);
-  p += align256(N * KL_DI * 2);
-  u32* rows = reinterpret_cast<u32*>(p);
-  p += align256(N * 4);
+  const WsLayout L = kl_layout(T, k);
+  uint16_t* slot_dk = static_cast<uint16_t*>(L.at(ws, 0));
+  u32* rows = static_cast<u32*>(L.at(ws, 1));
+  void* scatter_ws = L.at(ws, 2);
   hipLaunchKernelGGL(indexer_kl_kernel, dim3(T), dim3(256), 0, stream, q8, qs, w, k8, ks, idx, seq_id, lay, k, kp,
                      target, loss, dq, dw, slot_dk, rows, T);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_row_scatter_add(rows, (int)N, num_rows, slot_dk, KL_DI, dk, p, stream);
+  return launch_row_scatter_add(rows, (int)N, num_rows, slot_dk, KL_DI, dk, scatter_ws, stream);
 }
 
 }  // namespace dsa

@@ -253,10 +253,16 @@ static int proj_splits(int T, int d, int H_I, int D_I) {
   return s;
 }
 
-size_t proj_workspace_bytes(int T, int d, int H_I, int D_I) {
+// fp32 partial sums per hidden-dim slice (N = H_I D_I + H_I + D_I columns;
+// the key columns are carved whether or not the call asks for the key)
+WsLayout proj_layout(int T, int d, int H_I, int D_I) {
+  WsLayout L;
   const size_t N = (size_t)H_I * D_I + H_I + D_I;
-  return align256((size_t)proj_splits(T, d, H_I, D_I) * T * N * 4);
+  L.add("part", (size_t)proj_splits(T, d, H_I, D_I) * T * N * 4);
+  return L;
 }
+
+size_t proj_workspace_bytes(int T, int d, int H_I, int D_I) { return proj_layout(T, d, H_I, D_I).total; }
 
 hipError_t launch_indexer_project(int T, int d, int H_I, int D_I, const uint16_t* h, const uint16_t* wq,
                                   const uint16_t* ww, const uint16_t* wk, uint8_t* q8, float* qs, float* w,
@@ -267,7 +273,7 @@ hipError_t launch_indexer_project(int T, int d, int H_I, int D_I, const uint16_t
   const int splits = proj_splits(T, d, H_I, D_I);
   const int kchunk = d / splits;
   const int tm = proj_tm(T);
-  float* part = static_cast<float*>(ws);
+  float* part = static_cast<float*>(proj_layout(T, d, H_I, D_I).at(ws, 0));
   const dim3 grid((N + PJ_BN - 1) / PJ_BN, (T + tm - 1) / tm, splits);
   if (tm == 16)
     hipLaunchKernelGGL(proj_gemm_kernel<16>, grid, dim3(PJ_NT), 0, stream, h, wq, ww, wk, T, d, Nq, Nw, N, kchunk,

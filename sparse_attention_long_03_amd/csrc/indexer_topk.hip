@@ -407,7 +407,14 @@ int fused_topk_cap_from_bytes(int T, size_t bytes) {
 }
 
 // keys then positions; T * cap * 4 is a multiple of 256 (cap is a multiple of 64)
-size_t fused_topk_workspace_bytes(int T, int cap) { return 8 * (size_t)T * cap; }
+WsLayout fused_topk_layout(int T, int cap) {
+  WsLayout L;
+  L.add("ckey", (size_t)T * cap * 4);
+  L.add("cpos", (size_t)T * cap * 4);
+  return L;
+}
+
+size_t fused_topk_workspace_bytes(int T, int cap) { return fused_topk_layout(T, cap).total; }
 
 // a compacted list (k entries) must take FT_AHEAD more tiles before the next
 // check, plus one tile of margin
@@ -419,8 +426,9 @@ template <int H_I, int D_I>
 static hipError_t launch_fused_t(int T, int max_len, const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8,
                                  const float* ks, const int32_t* seq_id, const int32_t* pos, const Layout& lay,
                                  int k, int cap, int32_t* idx, void* ws, hipStream_t stream) {
-  u32* ckey = static_cast<u32*>(ws);
-  int32_t* cpos = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + (size_t)T * cap * 4);
+  const WsLayout L = fused_topk_layout(T, cap);
+  u32* ckey = static_cast<u32*>(L.at(ws, 0));
+  int32_t* cpos = static_cast<int32_t*>(L.at(ws, 1));
   const int blocks = (T + FT_QB - 1) / FT_QB;
   hipLaunchKernelGGL((indexer_topk_kernel<H_I, D_I>), dim3(blocks), dim3(FT_WAVES * 64), 0, stream, q8, qs, w, k8,
                      ks, seq_id, pos, lay, T, max_len, k, cap, idx, ckey, cpos);

@@ -10,6 +10,67 @@
 
 namespace dsa {
 
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// A workspace layout: named regions, each starting on a 256-byte boundary at
+// an offset from the workspace base.  Every call that takes a workspace
+// computes both its stated size (total) and its pointers from one of these,
+// so the two cannot disagree; dsa_workspace_layout reports them.  A region
+// may hold a sub-step's own layout (add_sub); `flat` lists the leaf regions
+// with offsets from this layout's base and the name of the region they sit in.
+struct WsRegion {
+  const char* parent;  // null for a region of this layout itself
+  const char* name;
+  size_t off, bytes;
+};
+
+struct WsLayout {
+  static constexpr int MAX = 8, MAX_FLAT = 16;
+  const char* name[MAX] = {};
+  size_t off[MAX] = {};
+  size_t bytes[MAX] = {};
+  int n = 0;
+  size_t total = 0;
+  WsRegion flat[MAX_FLAT] = {};
+  int nflat = 0;
+
+  int add(const char* nm, size_t b) {
+    name[n] = nm;
+    off[n] = total;
+    bytes[n] = b;
+    total += align256(b);
+    flat[nflat++] = WsRegion{nullptr, nm, off[n], b};
+    return n++;
+  }
+  int add_sub(const char* nm, const WsLayout& sub) {
+    const int i = add(nm, sub.total);
+    --nflat;  // the container is reported through its regions
+    for (int j = 0; j < sub.nflat; ++j) flat[nflat++] = WsRegion{nm, sub.flat[j].name, off[i] + sub.flat[j].off, sub.flat[j].bytes};
+    return i;
+  }
+  int index(const char* nm) const {
+    for (int i = 0; i < n; ++i) {
+      const char *a = name[i], *b = nm;
+      while (*a && *a == *b) ++a, ++b;
+      if (*a == *b) return i;
+    }
+    return -1;
+  }
+  void* at(void* base, int i) const { return static_cast<char*>(base) + off[i]; }
+};
+
+// Layouts of the workspaces, one per operation (T == 0 gives an empty one)
+WsLayout topk_layout(int T, int64_t max_len, int k);          // hist, counts, above, ckey, cpos
+WsLayout fused_topk_layout(int T, int cap);                    // ckey, cpos
+WsLayout attn_layout(int T, int H, int k);                     // o, ml (none with one split)
+WsLayout dense_attn_layout(int T, int H, int max_len);         // o, ml (none with one split)
+WsLayout scatter_layout(int64_t N);                            // keys_b, vals_a, vals_b, hist, totals
+WsLayout attn_bwd_layout(int T, int H, int k);                 // dsp, slot_grad, rows, cnt, scatter
+WsLayout kl_layout(int T, int k);                              // slot_dk, rows, scatter
+WsLayout kl_target_dense_layout(int T, int H, int max_len);    // ml
+WsLayout proj_layout(int T, int d, int H_I, int D_I);          // part
+
+
 // (1) indexer logits; `hist` (nullable) receives the per-row 2048-bin
 // histogram of the top 11 key bits (must be zeroed first).
 bool indexer_supported(int H_I, int D_I);
@@ -103,7 +164,5 @@ hipError_t launch_kl(int T, const uint8_t* q8, const float* qs, const float* w, 
                      const int32_t* idx, const int32_t* seq_id, const Layout& lay, int64_t num_rows, int k,
                      const float* target, float* loss, float* dq, float* dw, float* dk, void* ws,
                      hipStream_t stream);
-
-inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace dsa

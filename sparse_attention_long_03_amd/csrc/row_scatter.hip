@@ -220,27 +220,27 @@ struct ScatterWorkspace {
   u32 *keys_b, *vals_a, *vals_b, *hist, *totals;
 };
 
-// Carves the workspace (base may be null: then only the size is computed).
-static size_t carve_scatter(int64_t N, void* base, ScatterWorkspace* w) {
+WsLayout scatter_layout(int64_t N) {
+  WsLayout L;
   const size_t nblocks = ((size_t)N + RS_BLOCK - 1) / RS_BLOCK;
-  const size_t sizes[5] = {(size_t)N * 4, (size_t)N * 4, (size_t)N * 4, 256 * nblocks * 4, 256 * 4};
-  size_t off[5], total = 0;
-  for (int i = 0; i < 5; ++i) {
-    off[i] = total;
-    total += align256(sizes[i]);
-  }
-  if (base != nullptr) {
-    char* p = static_cast<char*>(base);
-    w->keys_b = reinterpret_cast<u32*>(p + off[0]);
-    w->vals_a = reinterpret_cast<u32*>(p + off[1]);
-    w->vals_b = reinterpret_cast<u32*>(p + off[2]);
-    w->hist = reinterpret_cast<u32*>(p + off[3]);
-    w->totals = reinterpret_cast<u32*>(p + off[4]);
-  }
-  return total;
+  L.add("keys_b", (size_t)N * 4);
+  L.add("vals_a", (size_t)N * 4);
+  L.add("vals_b", (size_t)N * 4);
+  L.add("hist", 256 * nblocks * 4);
+  L.add("totals", 256 * 4);
+  return L;
 }
 
-size_t row_scatter_workspace_bytes(int64_t N) { return carve_scatter(N, nullptr, nullptr); }
+static void carve_scatter(int64_t N, void* base, ScatterWorkspace* w) {
+  const WsLayout L = scatter_layout(N);
+  w->keys_b = static_cast<u32*>(L.at(base, 0));
+  w->vals_a = static_cast<u32*>(L.at(base, 1));
+  w->vals_b = static_cast<u32*>(L.at(base, 2));
+  w->hist = static_cast<u32*>(L.at(base, 3));
+  w->totals = static_cast<u32*>(L.at(base, 4));
+}
+
+size_t row_scatter_workspace_bytes(int64_t N) { return scatter_layout(N).total; }
 
 hipError_t launch_row_scatter_add(u32* rows, int N, int64_t num_rows, const uint16_t* src_rows, int W, float* dst,
                                   void* ws, hipStream_t stream) {

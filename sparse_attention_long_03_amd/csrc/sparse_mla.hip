@@ -390,17 +390,20 @@ static int dense_splits(int T, int H, int max_len) {
 
 bool dense_attn_supported(int max_len) { return max_len <= AT_MAX_SPLITS * AT_MAX_SPLIT; }
 
-static size_t split_workspace(int T, int H, int s) {
-  if (s == 1) return 0;
+// split partials (bf16, normalised) and their (max, sum) pairs; none with one split
+static WsLayout split_layout(int T, int H, int s) {
+  WsLayout L;
+  if (s == 1) return L;
   const size_t slots = (size_t)T * s * H;
-  return align256(slots * AT_DV * 2) + align256(slots * 2 * 4);
+  L.add("o", slots * AT_DV * 2);
+  L.add("ml", slots * 2 * 4);
+  return L;
 }
 
-size_t attn_workspace_bytes(int T, int H, int k) { return split_workspace(T, H, attn_splits(T, H, k)); }
-
-size_t dense_attn_workspace_bytes(int T, int H, int max_len) {
-  return split_workspace(T, H, dense_splits(T, H, max_len));
-}
+WsLayout attn_layout(int T, int H, int k) { return split_layout(T, H, attn_splits(T, H, k)); }
+WsLayout dense_attn_layout(int T, int H, int max_len) { return split_layout(T, H, dense_splits(T, H, max_len)); }
+size_t attn_workspace_bytes(int T, int H, int k) { return attn_layout(T, H, k).total; }
+size_t dense_attn_workspace_bytes(int T, int H, int max_len) { return dense_attn_layout(T, H, max_len).total; }
 
 template <bool DENSE>
 static hipError_t launch_attn_t(int T, int H, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
@@ -416,9 +419,9 @@ static hipError_t launch_attn_t(int T, int H, const uint16_t* q, const uint16_t*
   uint16_t* ws_o = nullptr;
   float* ws_ml = nullptr;
   if (n_splits > 1) {
-    const size_t slots = (size_t)T * n_splits * H;
-    ws_o = reinterpret_cast<uint16_t*>(ws);
-    ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256(slots * AT_DV * 2));
+    const WsLayout L = split_layout(T, H, n_splits);
+    ws_o = static_cast<uint16_t*>(L.at(ws, 0));
+    ws_ml = static_cast<float*>(L.at(ws, 1));
   }
   // (token, split) pairs rounded up to a multiple of 8 (one per XCD per slot)
   const int pairs = T * n_splits;

@@ -381,31 +381,28 @@ struct BwdWorkspace {
   void* scatter;
 };
 
-// Carves the workspace (base may be null: then only the size is computed).
-static size_t carve_bwd(int T, int H, int k, void* base, BwdWorkspace* w) {
-  const size_t kp = (size_t)bwd_kp(k);
-  const size_t N = (size_t)T * kp;
-  const size_t sizes[5] = {N * 2 * H * 2, N * AT_D * 2, N * 4, (size_t)T * 4, row_scatter_workspace_bytes(N)};
-  size_t off[5], total = 0;
-  for (int i = 0; i < 5; ++i) {
-    off[i] = total;
-    total += align256(sizes[i]);
-  }
-  if (base != nullptr) {
-    char* p = static_cast<char*>(base);
-    w->dsp = reinterpret_cast<uint16_t*>(p + off[0]);
-    w->slot_grad = reinterpret_cast<uint16_t*>(p + off[1]);
-    w->rows = reinterpret_cast<u32*>(p + off[2]);
-    w->cnt = reinterpret_cast<int32_t*>(p + off[3]);
-    w->scatter = p + off[4];
-  }
-  return total;
+WsLayout attn_bwd_layout(int T, int H, int k) {
+  WsLayout L;
+  if (T == 0) return L;
+  const size_t N = (size_t)T * bwd_kp(k);
+  L.add("dsp", N * 2 * H * 2);
+  L.add("slot_grad", N * AT_D * 2);
+  L.add("rows", N * 4);
+  L.add("cnt", (size_t)T * 4);
+  L.add_sub("scatter", scatter_layout(N));
+  return L;
 }
 
-size_t attn_bwd_workspace_bytes(int T, int H, int k) {
-  if (T == 0) return 0;
-  return carve_bwd(T, H, k, nullptr, nullptr);
+static void carve_bwd(int T, int H, int k, void* base, BwdWorkspace* w) {
+  const WsLayout L = attn_bwd_layout(T, H, k);
+  w->dsp = static_cast<uint16_t*>(L.at(base, 0));
+  w->slot_grad = static_cast<uint16_t*>(L.at(base, 1));
+  w->rows = static_cast<u32*>(L.at(base, 2));
+  w->cnt = static_cast<int32_t*>(L.at(base, 3));
+  w->scatter = L.at(base, 4);
 }
+
+size_t attn_bwd_workspace_bytes(int T, int H, int k) { return attn_bwd_layout(T, H, k).total; }
 
 bool attn_bwd_size_ok(int T, int k) { return (int64_t)T * bwd_kp(k) < (int64_t(1) << 31); }
 

@@ -387,29 +387,32 @@ static int topk_nch(int64_t max_len) {
   return c > 0 ? (int)c : 1;
 }
 
+WsLayout topk_layout(int T, int64_t max_len, int k) {
+  WsLayout L;
+  const size_t slots = (size_t)T * topk_nch(max_len);
+  const size_t cap_above = k < TK_CH ? k : TK_CH;
+  L.add("hist", (size_t)T * TK_BINS * 4);  // first: the indexer's fused histogram lives here
+  L.add("counts", slots * 2 * 4);
+  L.add("above", slots * cap_above * 4);
+  L.add("ckey", slots * TK_CH * 4);
+  L.add("cpos", slots * TK_CH * 4);
+  return L;
+}
+
 static TopkWs carve(void* ws, int T, int64_t max_len, int k) {
+  const WsLayout L = topk_layout(T, max_len, k);
   TopkWs w;
   w.nch = topk_nch(max_len);
   w.cap_above = k < TK_CH ? k : TK_CH;
-  char* p = static_cast<char*>(ws);
-  const size_t slots = (size_t)T * w.nch;
-  w.hist = reinterpret_cast<u32*>(p);
-  p += align256((size_t)T * TK_BINS * 4);
-  w.counts = reinterpret_cast<u32*>(p);
-  p += align256(slots * 2 * 4);
-  w.above = reinterpret_cast<int32_t*>(p);
-  p += align256(slots * w.cap_above * 4);
-  w.ckey = reinterpret_cast<u32*>(p);
-  p += align256(slots * TK_CH * 4);
-  w.cpos = reinterpret_cast<int32_t*>(p);
+  w.hist = static_cast<u32*>(L.at(ws, 0));
+  w.counts = static_cast<u32*>(L.at(ws, 1));
+  w.above = static_cast<int32_t*>(L.at(ws, 2));
+  w.ckey = static_cast<u32*>(L.at(ws, 3));
+  w.cpos = static_cast<int32_t*>(L.at(ws, 4));
   return w;
 }
 
-size_t topk_workspace_bytes(int T, int64_t max_len, int k) {
-  const size_t slots = (size_t)T * topk_nch(max_len);
-  return align256((size_t)T * TK_BINS * 4) + align256(slots * 2 * 4) + align256(slots * (size_t)(k < TK_CH ? k : TK_CH) * 4) +
-         2 * align256(slots * TK_CH * 4);
-}
+size_t topk_workspace_bytes(int T, int64_t max_len, int k) { return topk_layout(T, max_len, k).total; }
 
 u32* topk_hist_buffer(void* ws) { return static_cast<u32*>(ws); }
 
