@@ -114,10 +114,16 @@ struct IndexerQuery {
 // lane 16j + n returns the sum for key 16j + n of the group.  Within a lane,
 // each 16-head tile sums its four heads in a short chain of its own and the
 // tiles are added pairwise, so the dependent adds stay few; then the sums of
-// the four lane groups are added across lanes.
+// the four lane groups are added across lanes (lane ^ 16, then lane ^ 32).
+//
+// The chain is spelled out (one product, then fused multiply-adds in head
+// order) and contraction is off: left to itself the compiler may fuse either
+// product of w0*r0 + w1*r1, and it chooses per unrolled copy, so copies (and
+// kernels) would round the same key differently.
 template <int H_I, int D_I>
 __device__ __forceinline__ float group_scores(const IndexerQuery<H_I, D_I>& q, const KeyFrag<H_I, D_I> (&kb)[4],
                                               int g) {
+#pragma clang fp contract(off)
   constexpr int MT = IndexerQuery<H_I, D_I>::MT;
   float res = 0.f;
 #pragma unroll
@@ -130,7 +136,7 @@ __device__ __forceinline__ float group_scores(const IndexerQuery<H_I, D_I>& q, c
     for (int mt = 0; mt < MT; ++mt) {
       pm[mt] = q.wv[mt][0] * relu(acc[mt][0]);
 #pragma unroll
-      for (int i = 1; i < 4; ++i) pm[mt] += q.wv[mt][i] * relu(acc[mt][i]);
+      for (int i = 1; i < 4; ++i) pm[mt] = __builtin_fmaf(q.wv[mt][i], relu(acc[mt][i]), pm[mt]);
     }
 #pragma unroll
     for (int w = 1; w < MT; w *= 2)
