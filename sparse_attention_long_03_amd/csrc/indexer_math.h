@@ -143,8 +143,14 @@ __device__ __forceinline__ float group_scores(const IndexerQuery<H_I, D_I>& q, c
 #pragma unroll
       for (int mt = 0; mt + w < MT; mt += 2 * w) pm[mt] += pm[mt + w];
     float part = pm[0];
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
+    // lane ^ 16, then lane ^ 32, with gfx950's VALU row swaps: a ds_bpermute
+    // shuffle would count on the in-order LDS counter and so wait behind the
+    // key-fragment reads in flight.  Each swap returns the lane's own value
+    // and its partner's; their sum is the same in either order.
+    const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+    part = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+    part = __uint_as_float(y[0]) + __uint_as_float(y[1]);
     if (g == j) res = part;
   }
   return res;
