@@ -7,12 +7,15 @@
 // indexer, keep the k highest-scoring ones (lowest position first among
 // equal scores, -0 equal to +0).
 //
-// Work split.  A workgroup takes 8 consecutive query tokens, two per wave,
+// Work split.  A workgroup takes 4 consecutive query tokens, one per wave,
 // and streams the keys of their sequence from position 0 in tiles of 64 keys
-// staged through LDS (one global read of a tile serves all 8 tokens).  Each
-// wave computes its two tokens' logits for the tile with the same arithmetic
-// as the logits kernel (indexer_math.h), so every logit is bit-identical to
-// the one dsa_indexer_logits would store.
+// staged through LDS (one global read of a tile serves all 4 tokens).  With
+// one token a wave fits in 168 registers (a 20-byte spill outside the tile
+// loop), so three waves share each SIMD; two tokens a wave took 250 registers
+// and two waves per SIMD, and ran 2% slower at the 64K prefill.  Each wave
+// computes its token's logits for the tile with the same arithmetic as the
+// logits kernel (indexer_math.h), so every logit is bit-identical to the one
+// dsa_indexer_logits would store.
 //
 // Streaming selection.  Per token, the wave keeps a candidate list in the
 // workspace: (order key, position) pairs in increasing position, plus a
@@ -34,7 +37,7 @@
 namespace dsa {
 
 constexpr int FT_WAVES = 4;
-constexpr int FT_QPW = 2;                 // query tokens per wave
+constexpr int FT_QPW = 1;                 // query tokens per wave
 constexpr int FT_QB = FT_WAVES * FT_QPW;  // query tokens per workgroup
 constexpr int FT_TILE = 64;               // keys per tile
 constexpr int FT_AHEAD = 4;               // key tiles in flight (register stages)
@@ -211,7 +214,7 @@ struct TileRegs<64> {
 };
 
 template <int H_I, int D_I>
-__global__ __launch_bounds__(FT_WAVES * 64) void indexer_topk_kernel(
+__global__ __launch_bounds__(FT_WAVES * 64, 3) void indexer_topk_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
     const uint8_t* __restrict__ k8, const float* __restrict__ ks, const int32_t* __restrict__ seq_id,
     const int32_t* __restrict__ pos, Layout lay, int T, int max_len, int k, int cap, int32_t* __restrict__ idx,
