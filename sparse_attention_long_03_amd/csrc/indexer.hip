@@ -146,7 +146,7 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void indexer_kernel(const uint8_t* 
     for (int j = 0; j < 4; ++j) kb[j] = Stage::frag(slab, j, n, g);
     const int base = first + it * IDX_WAVES * 64;
     const int s_me = base + lane;
-    const float res = group_scores<H_I, D_I>(qq, kb, g);
+    const float res = group_scores<H_I, D_I>(qq, kb);
     if (s_me <= p) {
       const float v = scaled_logit(res, qq.qscale, ksv);
       out_row[s_me] = v;

@@ -358,7 +358,7 @@ __global__ __launch_bounds__(256) void indexer_kl_kernel(
     const int e = it * KL_TILE + lane;
     const u32 row = s_row[e];
     const float ksv = ks[row & ~ROW_INVALID];
-    const float res = group_scores<KL_HI, KL_DI>(qy, kb, g);
+    const float res = group_scores<KL_HI, KL_DI>(qy, kb);
     s_lg[e] = (row & ROW_INVALID) ? -INFINITY : scaled_logit(res, qscale, ksv);
   }
   __syncthreads();

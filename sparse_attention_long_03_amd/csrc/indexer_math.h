@@ -13,8 +13,8 @@
 // v_mfma_f32_16x16x128_f8f6f4 computes 16 heads x 16 keys of dot products
 // (D_I = 64 uses two 16x16x32 fp8 MFMAs).  In the 16x16 result a lane holds
 // one key (column) and four heads (rows), so the ReLU and the per-head
-// weights are applied in registers and the sum over heads needs only two
-// cross-lane steps (lanes n, n+16, n+32, n+48).
+// weights are applied in registers and the sum over heads needs only three
+// cross-lane swaps for all 64 keys of a group (lanes n, n+16, n+32, n+48).
 //
 // Each lane group g (lanes 16g..16g+15) feeds the same byte range of the head
 // dim for both operands; the contraction is a plain sum over the K index, so
@@ -113,19 +113,32 @@ struct IndexerQuery {
 // Head-weighted ReLU sums of one query against 64 keys (4 N tiles of 16):
 // lane 16j + n returns the sum for key 16j + n of the group.  Within a lane,
 // each 16-head tile sums its four heads in a short chain of its own and the
-// tiles are added pairwise, so the dependent adds stay few; then the sums of
-// the four lane groups are added across lanes (lane ^ 16, then lane ^ 32).
+// tiles are added pairwise, so the dependent adds stay few; that leaves each
+// lane (group g, column n) with p[j], its four heads' share of key 16j + n,
+// for the four key groups j.  The sum over the four lane groups then ends in
+// lane group j for key group j, by recursive halving on gfx950's VALU row
+// swaps (a ds_bpermute shuffle would count on the in-order LDS counter and
+// wait behind the key-fragment reads in flight):
+//   permlane16_swap(p[0], p[1]) swaps the odd rows (lane groups) of its first
+//   operand with the even rows of its second, so in lane group g the two
+//   results are p[g & 1] of groups g and g ^ 1: their sum is key group g & 1
+//   over that pair of lane groups; the same for p[2], p[3] (key group
+//   2 + (g & 1));
+//   permlane32_swap(u, v) swaps the upper half of u with the lower half of v,
+//   so the two results are u (lower half) or v (upper half) of lane groups g
+//   and g ^ 2: their sum is key group g over all four lane groups.
+// Every key is the sum (groups 0 + 1) + (groups 2 + 3), in one order or the
+// other of each addition, which gives the same value.
 //
 // The chain is spelled out (one product, then fused multiply-adds in head
 // order) and contraction is off: left to itself the compiler may fuse either
 // product of w0*r0 + w1*r1, and it chooses per unrolled copy, so copies (and
 // kernels) would round the same key differently.
 template <int H_I, int D_I>
-__device__ __forceinline__ float group_scores(const IndexerQuery<H_I, D_I>& q, const KeyFrag<H_I, D_I> (&kb)[4],
-                                              int g) {
+__device__ __forceinline__ float group_scores(const IndexerQuery<H_I, D_I>& q, const KeyFrag<H_I, D_I> (&kb)[4]) {
 #pragma clang fp contract(off)
   constexpr int MT = IndexerQuery<H_I, D_I>::MT;
-  float res = 0.f;
+  float p[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     v4f acc[MT];
@@ -142,18 +155,14 @@ __device__ __forceinline__ float group_scores(const IndexerQuery<H_I, D_I>& q, c
     for (int w = 1; w < MT; w *= 2)
 #pragma unroll
       for (int mt = 0; mt + w < MT; mt += 2 * w) pm[mt] += pm[mt + w];
-    float part = pm[0];
-    // lane ^ 16, then lane ^ 32, with gfx950's VALU row swaps: a ds_bpermute
-    // shuffle would count on the in-order LDS counter and so wait behind the
-    // key-fragment reads in flight.  Each swap returns the lane's own value
-    // and its partner's; their sum is the same in either order.
-    const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-    part = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-    const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-    part = __uint_as_float(y[0]) + __uint_as_float(y[1]);
-    if (g == j) res = part;
+    p[j] = pm[0];
   }
-  return res;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(p[0]), __float_as_uint(p[1]), false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(p[2]), __float_as_uint(p[3]), false, false);
+  const float u = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const float v = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(u), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
 // The logit from the head sum and the two per-token scales.

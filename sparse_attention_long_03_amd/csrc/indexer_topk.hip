@@ -328,7 +328,7 @@ __global__ __launch_bounds__(FT_WAVES * 64, 3) void indexer_topk_kernel(
 #pragma unroll
         for (int qi = 0; qi < FT_QPW; ++qi) {
           if (!row_on[qi]) continue;
-          const float res = group_scores<H_I, D_I>(qq[qi], kb, g);
+          const float res = group_scores<H_I, D_I>(qq[qi], kb);
           const u32 key = order_key(scaled_logit(res, qq[qi].qscale, ksv));
           const bool take = s <= my_pos[qi] && key > tau[qi];
           const uint64_t m = __ballot(take);
