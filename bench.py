@@ -43,9 +43,9 @@ REPLICAS = 4
 # device copy in the same pass.  Valid only for the kernel sources they were
 # taken on (hash below); otherwise the field is reported as null.
 TRAFFIC = {
-    "sources_sha256": "0d3e5daac9573c143a931596bcc1cee7bc7a286fddaf94e88bfa441f0946ac95",
-    # FETCH_SIZE 135766.0 KiB/launch x 1.99981 (copy: 131084.2 KiB counted for 262144 KiB read)
-    "fetch_bytes": 278022961,
+    "sources_sha256": "5351d7d2401fe9d357b182341292a5dd73e8f9e31745fcf393af6cc1f6153df9",
+    # FETCH_SIZE 135763.5 KiB/launch x 1.99981 (copy: 131084.2 KiB counted for 262144 KiB read)
+    "fetch_bytes": 278017797,
     # WRITE_SIZE 8192.0 KiB/launch x 1.0 (copy: 262144 KiB counted for 262144 KiB written)
     "write_bytes": 8388608,
 }
@@ -755,7 +755,9 @@ def main():
             and cfg.name == "decode128k":
         traffic = TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
     out = {
-        "metric": "DSA decode queries/s @128K ctx, k=2048 (+indexer TFLOP/s, sparse-attn GB/s)",
+        "metric": ("DSA decode queries/s @128K ctx, k=2048 (+indexer TFLOP/s, sparse-attn GB/s)"
+                   if cfg.name == "decode128k" else
+                   f"DSA decode queries/s, {cfg.name}, k={cfg.k} (+indexer TFLOP/s, sparse-attn GB/s)"),
         "value": round(value, 1),
         "unit": "queries/s",
         "n_gpus": 1,
