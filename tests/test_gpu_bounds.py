@@ -113,7 +113,7 @@ def test_fused_selection_at_its_minimum_workspace():
     x = I.make_inputs(CASES["prefill_2500"], DEV)
     c = x.cfg
     p = DSAPath(x)
-    ws = Guarded(8 * x.T * (c.k + 320))   # the smallest list capacity the call accepts
+    ws = Guarded(8 * x.T * ((c.k + 320 + 63) // 64 * 64))   # the smallest list capacity the call accepts
     gi, idx = _guarded(torch.int32, (x.T, c.k))
     B.dsa_indexer_topk(p.q, p.layout, c.H_I, c.D_I, x.iq8, x.iqs, x.iw, x.ik8, x.iks, c.k, idx, ws.bytes())
     torch.cuda.synchronize()

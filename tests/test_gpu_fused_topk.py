@@ -26,8 +26,10 @@ FUSED = {
     # prefill, every token a causal query; rows shorter than k keep everything
     "prefill_3000": I.scaled(I.CONFIGS["prefill64k"], L=3000, H=16, k=256),
     "prefill_4100_k2048": I.scaled(I.CONFIGS["prefill64k"], L=4100, H=16),
-    # three sequences of 700 tokens, all positions queries: blocks of 8 tokens straddle sequences
-    "three_sequences": I.scaled(I.CONFIGS["decode32k"], B=3, L=700, queries_per_seq=700, H=16, k=128),
+    # three sequences of 699 tokens, all positions queries: blocks of 4 tokens straddle sequences
+    "three_sequences": I.scaled(I.CONFIGS["decode32k"], B=3, L=699, queries_per_seq=699, H=16, k=128),
+    # 41 sequences of 70 keys, one query each: every block of 4 tokens holds 4 sequences
+    "one_query_per_sequence": I.scaled(I.CONFIGS["decode32k"], B=41, L=70, H=16, k=32),
     # small indexer variants
     "idx4x64": I.scaled(I.CONFIGS["prefill64k"], L=2500, H_I=4, D_I=64, H=16, k=256),
     "idx64x64": I.scaled(I.CONFIGS["prefill64k"], L=2200, D_I=64, H=16, k=512),
@@ -43,8 +45,9 @@ def _sorted(idx):
 
 
 def _min_ws(x, k):
-    """The smallest workspace the call accepts: k + 320 candidate slots per token."""
-    return 8 * x.T * (k + 320)
+    """The smallest workspace the call accepts: k + 320 candidate slots per token,
+    rounded up to a multiple of 64 (the list capacity is taken in whole tiles)."""
+    return 8 * x.T * ((k + 320 + 63) // 64 * 64)
 
 
 @pytest.mark.parametrize("small_ws", [False, True], ids=["preferred_ws", "min_ws"])
