@@ -27,7 +27,7 @@
 namespace dsa {
 
 constexpr int TK_CH = 4096;  // positions per chunk
-constexpr int TK_CHUNK_NT = 256;
+constexpr int TK_CHUNK_NT = 512;
 constexpr int TK_RES_NT = 1024;
 constexpr int TK_BINS = 2048;
 constexpr int TK_MAX_CHUNKS = TK_RES_NT;  // rows up to 4M positions
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(TK_CHUNK_NT) void topk_chunk_kernel(const float* __
                                                                  const int32_t* __restrict__ valid_len, int len_add,
                                                                  int max_len, int k, TopkWs ws) {
   constexpr int NT = TK_CHUNK_NT;
-  constexpr int E = TK_CH / NT;  // 16 positions per thread
+  constexpr int E = TK_CH / NT;  // 8 positions per thread
   __shared__ u32 scratch[NT / 64 + 1];
   __shared__ u32 sh_bin, sh_above;
   const int t = blockIdx.y;
