@@ -213,7 +213,9 @@ struct TileRegs<64> {
   __device__ __forceinline__ void store(uint8_t* dst) const { *reinterpret_cast<v4i*>(dst) = a; }
 };
 
-template <int H_I, int D_I>
+// PAGED: the layout, fixed per launch, so the contiguous loop keeps no page
+// lookup or layout select.
+template <int H_I, int D_I, bool PAGED>
 __global__ __launch_bounds__(FT_WAVES * 64, 3) void indexer_topk_kernel(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
     const uint8_t* __restrict__ k8, const float* __restrict__ ks, const int32_t* __restrict__ seq_id,
@@ -305,18 +307,16 @@ __global__ __launch_bounds__(FT_WAVES * 64, 3) void indexer_topk_kernel(
     // A tile is one 64-token page when paged.  Each stage looks up the page
     // of its next tile right after issuing its current loads, FT_AHEAD steps
     // before it is needed: loads complete in issue order, so a lookup issued
-    // just before its use would make that wait drain every stage.  (The
-    // lookup is unconditional: with a contiguous layout it reads a scale,
-    // unused.)
-    const int32_t* pg_src = lay.paged ? lay.block_table + (int64_t)seq * lay.max_pages
-                                      : reinterpret_cast<const int32_t*>(ks);
-    auto page = [&](int i) -> int { return pg_src[lay.paged ? min(i, ntiles - 1) : 0]; };
+    // just before its use would make that wait drain every stage.
+    const int32_t* pg_src = PAGED ? lay.block_table + (int64_t)seq * lay.max_pages : nullptr;
+    auto page = [&](int i) -> int { return PAGED ? pg_src[min(i, ntiles - 1)] : 0; };
+    const int64_t seq_row0 = (int64_t)seq * lay.seq_capacity;  // contiguous: the sequence's first row
     auto load = [&](Stage& S, int i) {  // S.pg is the page of tile i
       const int base = min(i, ntiles - 1) * FT_TILE;
-      const int64_t row0 = lay.paged ? (int64_t)S.pg * 64 : (int64_t)seq * lay.seq_capacity + base;
+      const int64_t row0 = PAGED ? (int64_t)S.pg * 64 : seq_row0 + base;
       S.r.load(k8 + (row0 + (min(base + sr, pmax) - base)) * D_I + sc);
       S.ks = ks[row0 + (min(base + lane, pmax) - base)];
-      S.pg = page(i + FT_AHEAD);
+      if (PAGED) S.pg = page(i + FT_AHEAD);
     };
     float ksv;
     auto step = [&](int i, Stage& S) {  // S holds tile i+1
@@ -433,8 +433,12 @@ static hipError_t launch_fused_t(int T, int max_len, const uint8_t* q8, const fl
   u32* ckey = static_cast<u32*>(L.at(ws, 0));
   int32_t* cpos = static_cast<int32_t*>(L.at(ws, 1));
   const int blocks = (T + FT_QB - 1) / FT_QB;
-  hipLaunchKernelGGL((indexer_topk_kernel<H_I, D_I>), dim3(blocks), dim3(FT_WAVES * 64), 0, stream, q8, qs, w, k8,
-                     ks, seq_id, pos, lay, T, max_len, k, cap, idx, ckey, cpos);
+  if (lay.paged)
+    hipLaunchKernelGGL((indexer_topk_kernel<H_I, D_I, true>), dim3(blocks), dim3(FT_WAVES * 64), 0, stream, q8, qs, w,
+                       k8, ks, seq_id, pos, lay, T, max_len, k, cap, idx, ckey, cpos);
+  else
+    hipLaunchKernelGGL((indexer_topk_kernel<H_I, D_I, false>), dim3(blocks), dim3(FT_WAVES * 64), 0, stream, q8, qs,
+                       w, k8, ks, seq_id, pos, lay, T, max_len, k, cap, idx, ckey, cpos);
   return hipGetLastError();
 }
 
