@@ -310,13 +310,22 @@ __global__ __launch_bounds__(FT_WAVES * 64, 3) void indexer_topk_kernel(
     // just before its use would make that wait drain every stage.
     const int32_t* pg_src = PAGED ? lay.block_table + (int64_t)seq * lay.max_pages : nullptr;
     auto page = [&](int i) -> int { return PAGED ? pg_src[min(i, ntiles - 1)] : 0; };
-    const int64_t seq_row0 = (int64_t)seq * lay.seq_capacity;  // contiguous: the sequence's first row
+    // contiguous: the sequence's first key row and scale; a row within the
+    // sequence is a 32-bit byte offset from them (max_len <= 4M, so
+    // max_len * D_I < 2^32)
+    const uint8_t* k8_seq = k8 + (int64_t)seq * lay.seq_capacity * D_I;
+    const float* ks_seq = ks + (int64_t)seq * lay.seq_capacity;
     auto load = [&](Stage& S, int i) {  // S.pg is the page of tile i
       const int base = min(i, ntiles - 1) * FT_TILE;
-      const int64_t row0 = PAGED ? (int64_t)S.pg * 64 : seq_row0 + base;
-      S.r.load(k8 + (row0 + (min(base + sr, pmax) - base)) * D_I + sc);
-      S.ks = ks[row0 + (min(base + lane, pmax) - base)];
-      if (PAGED) S.pg = page(i + FT_AHEAD);
+      if (PAGED) {
+        const int64_t row0 = (int64_t)S.pg * 64;
+        S.r.load(k8 + (row0 + (min(base + sr, pmax) - base)) * D_I + sc);
+        S.ks = ks[row0 + (min(base + lane, pmax) - base)];
+        S.pg = page(i + FT_AHEAD);
+      } else {
+        S.r.load(k8_seq + (u32)(min(base + sr, pmax) * D_I + sc));
+        S.ks = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(ks_seq) + (u32)(4 * min(base + lane, pmax)));
+      }
     };
     float ksv;
     auto step = [&](int i, Stage& S) {  // S holds tile i+1
@@ -333,10 +342,10 @@ __global__ __launch_bounds__(FT_WAVES * 64, 3) void indexer_topk_kernel(
           const bool take = s <= my_pos[qi] && key > tau[qi];
           const uint64_t m = __ballot(take);
           if (m == 0) continue;
-          if (take) {
-            const int d = cnt[qi] + (int)lanes_below(m);
-            lkey[qi][d] = key;
-            lpos[qi][d] = s;
+          if (take) {  // entry d < cap <= 12288: a 32-bit byte offset from the list bases
+            const u32 off = 4u * (u32)(cnt[qi] + (int)lanes_below(m));
+            *reinterpret_cast<u32*>(reinterpret_cast<uint8_t*>(lkey[qi]) + off) = key;
+            *reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(lpos[qi]) + off) = s;
           }
           cnt[qi] += __popcll(m);
         }
