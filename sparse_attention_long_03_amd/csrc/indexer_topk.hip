@@ -404,10 +404,13 @@ __global__ __launch_bounds__(FT_WAVES * 64, 3) void indexer_topk_kernel(
   }
 }
 
+// A capacity is a whole number of tiles (fused_topk_cap_from_bytes takes it
+// that way from a workspace size), so the minimum k + 320 is rounded up.
 int fused_topk_cap(int max_len, int k) {
   int c = ((max_len + FT_TILE - 1) / FT_TILE) * FT_TILE + FT_AHEAD * FT_TILE;  // no compaction needed
   if (c > FT_CAP_MAX) c = FT_CAP_MAX;
-  if (c < k + (FT_AHEAD + 1) * FT_TILE) c = k + (FT_AHEAD + 1) * FT_TILE;
+  const int min_cap = ((k + (FT_AHEAD + 1) * FT_TILE + FT_TILE - 1) / FT_TILE) * FT_TILE;
+  if (c < min_cap) c = min_cap;
   return c;
 }
 

@@ -155,6 +155,21 @@ def test_fused_indexer_topk_validation(lib):
     assert B.dsa_workspace_bytes(B.DSA_OP_INDEXER_TOPK, 16, 1 << 20, 0, 2048) == 8 * 16 * 12288
 
 
+def test_fused_preferred_workspace_is_accepted(lib):
+    # The call takes the list capacity as the largest multiple of 64 slots that
+    # the workspace holds per token and needs at least k + 320; the preferred
+    # size must therefore be a whole number of 64-slot tiles per token.  (A
+    # k + 320 minimum that is not a multiple of 64, e.g. k = 1 on a short row,
+    # once gave a preferred size the call rejected.)
+    for T in (1, 16, 55):
+        for max_len in (1, 55, 64, 100, 4095, 20000, 1 << 20):
+            for k in (1, 7, 32, 64, 100, 256, 300, 2047, 2048):
+                pref = B.dsa_workspace_bytes(B.DSA_OP_INDEXER_TOPK, T, max_len, 0, k)
+                assert pref % (8 * T * 64) == 0, (T, max_len, k, pref)
+                cap = pref // (8 * T)
+                assert k + 320 <= cap <= 12288, (T, max_len, k, cap)
+
+
 def test_forward_workspace_switches_to_fused_selection(lib):
     # below 2048 query tokens the logits are stored; from 2048 on they are not
     small = B.dsa_workspace_bytes(B.DSA_OP_FORWARD, 2047, 65536, 128, 2048)

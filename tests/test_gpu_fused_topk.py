@@ -30,6 +30,8 @@ FUSED = {
     "three_sequences": I.scaled(I.CONFIGS["decode32k"], B=3, L=699, queries_per_seq=699, H=16, k=128),
     # 41 sequences of 70 keys, one query each: every block of 4 tokens holds 4 sequences
     "one_query_per_sequence": I.scaled(I.CONFIGS["decode32k"], B=41, L=70, H=16, k=32),
+    # k + 320 not a whole number of 64-slot tiles, on rows shorter than a tile
+    "short_rows_k1": I.scaled(I.CONFIGS["prefill64k"], L=55, H=16, k=1),
     # small indexer variants
     "idx4x64": I.scaled(I.CONFIGS["prefill64k"], L=2500, H_I=4, D_I=64, H=16, k=256),
     "idx64x64": I.scaled(I.CONFIGS["prefill64k"], L=2200, D_I=64, H=16, k=512),
