@@ -1,0 +1,147 @@
+"""Seeded sweeps over random shapes, each case checked exactly.
+
+- the fused indexer + selection against the logits kernel followed by the
+  stand-alone selection (the same set of positions), paged and contiguous,
+  with and without tie-heavy keys, at the preferred and at the smallest
+  workspace;
+- dsa_forward against the separate calls: the same selection, and the
+  attention on the forward's own selection bit for bit;
+- dsa_topk against the oracle's selection on the same logits (heavy ties,
+  +-0, values over 60 decades, empty and ragged rows).
+
+The shapes are drawn from a fixed seed, so every run checks the same cases.
+A sweep of this kind found a workspace size the fused call rejected (k + 320
+slots not a whole number of 64-slot tiles).
+"""
+
+import random
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dsa_oracle as O
+from sparse_attention_long_03_amd import binding as B
+from sparse_attention_long_03_amd import inputs as I
+from sparse_attention_long_03_amd.path import DSAPath
+
+from test_gpu_fused_topk import _paged_copy
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _repeat_keys(x, period):
+    s = torch.arange(x.ik8.shape[1], device=DEV) % period
+    x.ik8[:] = x.ik8[:, s]
+    x.iks[:] = x.iks[:, s]
+
+
+def _sorted(idx):
+    return np.sort(idx.cpu().numpy(), axis=1)
+
+
+def _fused_cases(n, seed):
+    rng = random.Random(seed)
+    for _ in range(n):
+        kind = rng.choice(["prefill", "multi", "decode"])
+        H_I, D_I = rng.choice([(64, 128), (64, 64), (4, 128), (4, 64)])
+        k = rng.choice([1, 7, 32, 64, 100, 256, 512, 2048])
+        s = rng.randint(0, 10**6)
+        if kind == "prefill":
+            cfg = I.scaled(I.CONFIGS["prefill64k"], L=rng.randint(1, 5000), H_I=H_I, D_I=D_I, H=16, k=k, seed=s)
+        elif kind == "multi":
+            L = rng.randint(1, 900)
+            cfg = I.scaled(I.CONFIGS["decode32k"], B=rng.randint(2, 9), L=L, queries_per_seq=rng.randint(1, L),
+                           H_I=H_I, D_I=D_I, H=16, k=k, seed=s)
+        else:
+            cfg = I.scaled(I.CONFIGS["decode32k"], B=rng.randint(1, 40), L=rng.randint(1, 9000), H_I=H_I, D_I=D_I,
+                           H=16, k=k, seed=s)
+        period = rng.choice([1, 3, 37, 64, 65]) if rng.random() < 0.4 else None
+        yield cfg, period, rng.random() < 0.4, rng.random() < 0.5
+
+
+@pytest.mark.parametrize("case", range(20))
+def test_fused_selection_random_shapes(case):
+    cfg, period, paged, small = list(_fused_cases(20, 12345))[case]
+    x = I.make_inputs(cfg, DEV)
+    if period:
+        _repeat_keys(x, period)
+    if paged:
+        x = _paged_copy(x)
+    p = DSAPath(x)
+    k = cfg.k
+    ref = _sorted(p.topk(p.indexer(), k=k))
+    ws = 8 * x.T * ((k + 320 + 63) // 64 * 64) if small else None
+    got = _sorted(p.indexer_topk(k=k, ws_bytes=ws))
+    assert np.array_equal(ref, got), (cfg, period, paged, small)
+
+
+def _forward_cases(n, seed):
+    rng = random.Random(seed)
+    for _ in range(n):
+        kind = rng.choice(["prefill", "multi", "decode"])
+        H_I, D_I = rng.choice([(64, 128), (64, 64), (4, 128)])
+        H = rng.choice([16, 64, 128])
+        k = rng.choice([1, 7, 64, 100, 256, 512, 2048])
+        s = rng.randint(0, 10**6)
+        if kind == "prefill":
+            cfg = I.scaled(I.CONFIGS["prefill64k"], L=rng.randint(1, 2700), H_I=H_I, D_I=D_I, H=H, k=k, seed=s)
+        elif kind == "multi":
+            L = rng.randint(1, 700)
+            cfg = I.scaled(I.CONFIGS["decode32k"], B=rng.randint(2, 6), L=L, queries_per_seq=rng.randint(1, L),
+                           H_I=H_I, D_I=D_I, H=H, k=k, seed=s)
+        else:
+            cfg = I.scaled(I.CONFIGS["decode32k"], B=rng.randint(1, 24), L=rng.randint(1, 20000), H_I=H_I, D_I=D_I,
+                           H=H, k=k, seed=s)
+        period = rng.choice([1, 5, 37, 64]) if rng.random() < 0.3 else None
+        yield cfg, period, rng.random() < 0.4
+
+
+@pytest.mark.parametrize("case", range(15))
+def test_forward_random_shapes(case):
+    cfg, period, paged = list(_forward_cases(15, 777))[case]
+    x = I.make_inputs(cfg, DEV)
+    if period:
+        _repeat_keys(x, period)
+    if paged:
+        x = _paged_copy(x)
+    p = DSAPath(x)
+    out, lse, idx = (t.clone() for t in p.forward())
+    assert np.array_equal(_sorted(idx), _sorted(p.topk(p.indexer(), k=cfg.k))), (cfg, period, paged)
+    o2, l2 = p.attn(idx.clone())
+    assert torch.equal(out.view(torch.int16), o2.view(torch.int16)), (cfg, period, paged)
+    assert torch.equal(lse.view(torch.int32), l2.view(torch.int32)), (cfg, period, paged)
+
+
+@pytest.mark.parametrize("case", range(20))
+def test_topk_random_rows_match_oracle(case):
+    rng = random.Random(99 + case)
+    nrng = np.random.default_rng(99 + case)
+    T = rng.randint(1, 12)
+    L = rng.choice([1, 5, 63, 64, 65, 1000, 4095, 4096, 4097, 20000, 70000])
+    k = rng.choice([1, 3, 64, 100, 512, 2048])
+    kind = rng.choice(["normal", "ties", "levels", "zeros", "wide"])
+    if kind == "normal":
+        v = nrng.standard_normal((T, L)).astype(np.float32)
+    elif kind == "ties":
+        v = nrng.integers(-3, 4, (T, L)).astype(np.float32)
+    elif kind == "levels":
+        v = (nrng.integers(0, 256, (T, L)) * 0.125).astype(np.float32)
+    elif kind == "zeros":
+        v = nrng.choice(np.array([0.0, -0.0, 1.0, -1.0], dtype=np.float32), (T, L))
+    else:
+        v = (nrng.standard_normal((T, L)) * 10.0 ** nrng.integers(-30, 30, (T, L))).astype(np.float32)
+    valid = np.array([rng.randint(0, L) for _ in range(T)], dtype=np.int32)
+    ld = (L + 3) // 4 * 4
+    lg = torch.zeros((T, ld), dtype=torch.float32)
+    lg[:, :L] = torch.from_numpy(v)
+    lg = lg.to(DEV)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    ws = B.workspace(B.dsa_workspace_bytes(B.DSA_OP_TOPK, T, ld, 0, k))
+    B.dsa_topk(lg, torch.from_numpy(valid).to(DEV), ld, k, idx, ws)
+    got = idx.cpu().numpy()
+    for t in range(T):
+        ref = np.asarray(O.topk_select(v[t, :valid[t]], int(valid[t]), k))
+        assert np.array_equal(np.sort(ref), np.sort(got[t])), (T, L, k, kind, t)
