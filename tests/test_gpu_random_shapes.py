@@ -7,7 +7,10 @@
 - dsa_forward against the separate calls: the same selection, and the
   attention on the forward's own selection bit for bit;
 - dsa_topk against the oracle's selection on the same logits (heavy ties,
-  +-0, values over 60 decades, empty and ragged rows).
+  +-0, values over 60 decades, empty and ragged rows);
+- the sparse attention against the oracle, to the parity tests' bounds (16 to
+  128 heads, k not a multiple of the 32-row tile, padding inside rows,
+  paged caches).
 
 The shapes are drawn from a fixed seed, so every run checks the same cases.
 A sweep of this kind found a workspace size the fused call rejected (k + 320
@@ -25,6 +28,7 @@ from sparse_attention_long_03_amd import binding as B
 from sparse_attention_long_03_amd import inputs as I
 from sparse_attention_long_03_amd.path import DSAPath
 
+from parity_util import bf16_to_np, check_attn, host_inputs, np_
 from test_gpu_fused_topk import _paged_copy
 
 pytestmark = pytest.mark.gpu
@@ -145,3 +149,35 @@ def test_topk_random_rows_match_oracle(case):
     for t in range(T):
         ref = np.asarray(O.topk_select(v[t, :valid[t]], int(valid[t]), k))
         assert np.array_equal(np.sort(ref), np.sort(got[t])), (T, L, k, kind, t)
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_attention_random_shapes_match_oracle(case):
+    rng = random.Random(4242 + case)
+    H = rng.choice([16, 32, 64, 128])
+    k = rng.choice([1, 5, 31, 32, 33, 100, 256, 700, 2048])
+    kind = rng.choice(["decode", "multi", "prefill"])
+    s = rng.randint(0, 10**6)
+    if kind == "decode":
+        cfg = I.scaled(I.CONFIGS["decode32k"], B=rng.randint(1, 6), L=rng.randint(1, 3000), H=H, k=k, seed=s)
+    elif kind == "multi":
+        L = rng.randint(1, 300)
+        cfg = I.scaled(I.CONFIGS["decode32k"], B=rng.randint(2, 4), L=L, queries_per_seq=rng.randint(1, min(L, 8)),
+                       H=H, k=k, seed=s)
+    else:
+        cfg = I.scaled(I.CONFIGS["prefill64k"], L=rng.randint(1, 120), H=H, k=k, seed=s)
+    x = I.make_inputs(cfg, DEV)
+    if rng.random() < 0.4:
+        x = _paged_copy(x)
+    p = DSAPath(x)
+    idx = I.random_selection(cfg, x.pos, k, DEV)
+    if rng.random() < 0.3:  # padding entries inside the rows
+        g = torch.Generator(device=DEV).manual_seed(s)
+        idx = torch.where(torch.rand(idx.shape, generator=g, device=DEV) < 0.2, torch.full_like(idx, -1), idx)
+    out, lse = p.attn(idx)
+    h = host_inputs(x)
+    ro, rl = O.sparse_mla_attention(h["q"], h["kv"], idx.cpu().numpy(), h["seq_id"], cfg.scale, 512, h["bt"])
+    check_attn(bf16_to_np(out), ro, f"case {case}")
+    fin = np.isfinite(rl)
+    assert np.array_equal(fin, np.isfinite(np_(lse)))
+    np.testing.assert_allclose(np_(lse)[fin], rl[fin], rtol=1e-4, atol=1e-4)
