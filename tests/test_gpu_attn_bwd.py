@@ -62,6 +62,20 @@ def test_backward_matches_oracle(name):
     assert np.all(np_(dkv)[m_dkv.sum(axis=-1) == 0] == 0)
 
 
+def test_backward_single_selected_row():
+    """k = 1: each query attends to one row, so P = 1, dP = D and the exact
+    dS and dq are zero; what the GPU returns is the rounding of dP - D, which
+    must stay within the per-entry bound (and dkv is dO on the row's values)."""
+    cfg = I.scaled(I.CONFIGS["prefill64k"], L=151, H=64, k=1)
+    x = I.make_inputs(cfg, DEV)
+    idx = I.random_selection(cfg, x.pos, 1, DEV)
+    p, sel, dO, dq, dkv = _run(x, idx)
+    rdq, rdkv, m_dq, m_dkv = _oracle(x, sel, dO)
+    assert np.abs(rdq).max() <= 1e-12 * max(np.abs(m_dq).max(), 1.0)   # the reference gradient vanishes
+    check_bwd(np_(dq), rdq, m_dq, "k=1 dq")
+    check_bwd(np_(dkv), rdkv, m_dkv, "k=1 dkv")
+
+
 def test_backward_edge_selections():
     """Padding anywhere in a row, a row selected twice by one query, a query
     with no selection at all, and a ragged final tile."""
