@@ -10,7 +10,9 @@
   +-0, values over 60 decades, empty and ragged rows);
 - the sparse attention against the oracle, to the parity tests' bounds (16 to
   128 heads, k not a multiple of the 32-row tile, padding inside rows,
-  paged caches).
+  paged caches);
+- the attention backward (dq, dkv) against the oracle, to the backward
+  tests' per-entry bounds.
 
 The shapes are drawn from a fixed seed, so every run checks the same cases.
 A sweep of this kind found a workspace size the fused call rejected (k + 320
@@ -28,7 +30,9 @@ from sparse_attention_long_03_amd import binding as B
 from sparse_attention_long_03_amd import inputs as I
 from sparse_attention_long_03_amd.path import DSAPath
 
-from parity_util import bf16_to_np, check_attn, host_inputs, np_
+from parity_util import bf16_to_np, check_attn, check_bwd, host_inputs, np_
+from test_gpu_attn_bwd import _oracle as _bwd_oracle
+from test_gpu_attn_bwd import _run as _bwd_run
 from test_gpu_fused_topk import _paged_copy
 
 pytestmark = pytest.mark.gpu
@@ -181,3 +185,28 @@ def test_attention_random_shapes_match_oracle(case):
     fin = np.isfinite(rl)
     assert np.array_equal(fin, np.isfinite(np_(lse)))
     np.testing.assert_allclose(np_(lse)[fin], rl[fin], rtol=1e-4, atol=1e-4)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_backward_random_shapes_match_oracle(case):
+    rng = random.Random(31337 + case)
+    H = rng.choice([16, 32, 64, 128])
+    k = rng.choice([1, 5, 31, 33, 100, 256, 700])
+    kind = rng.choice(["decode", "multi", "prefill"])
+    s = rng.randint(0, 10**6)
+    if kind == "decode":
+        cfg = I.scaled(I.CONFIGS["decode32k"], B=rng.randint(1, 4), L=rng.randint(1, 2000), H=H, k=k, seed=s)
+    elif kind == "multi":
+        L = rng.randint(1, 300)
+        cfg = I.scaled(I.CONFIGS["decode32k"], B=rng.randint(2, 4), L=L, queries_per_seq=rng.randint(1, min(L, 6)),
+                       H=H, k=k, seed=s)
+    else:
+        cfg = I.scaled(I.CONFIGS["prefill64k"], L=rng.randint(1, 200), H=H, k=k, seed=s)
+    x = I.make_inputs(cfg, DEV)
+    if rng.random() < 0.4:
+        x = _paged_copy(x)
+    idx = I.random_selection(cfg, x.pos, k, DEV)
+    p, sel, dO, dq, dkv = _bwd_run(x, idx)
+    rdq, rdkv, m_dq, m_dkv = _bwd_oracle(x, sel, dO)
+    check_bwd(np_(dq), rdq, m_dq, f"case {case} dq")
+    check_bwd(np_(dkv), rdkv, m_dkv, f"case {case} dkv")
