@@ -211,8 +211,9 @@ def check_bwd(gpu, ref, mag, what="", rel=BWD_REL):
 
 # Indexer KL signal.  With indexer inputs whose FP8 values are small integers
 # (exact_indexer_inputs) every q8 . k8 dot product is exact in fp32, so the
-# logits match the oracle's up to the fp32 scaling: loss, dI and dw are
-# compared at 1e-4 relative (plus an absolute floor).  dq contracts the ReLU
+# logits match the oracle's up to the fp32 scaling: loss and dw are compared
+# at 1e-4 relative (plus an absolute floor), and dI carries the absolute error
+# of kl_exact_dI_error into every gradient term.  dq contracts the ReLU
 # mask with dI*ks*k8 rounded to bf16 (2^-8 of each term); dk contracts it with
 # w*q8 rounded to bf16, and each entry's key gradient is rounded to bf16
 # before the sum per cache row (2^-8 each): both are held to KL_BF16 = 2^-7
@@ -231,6 +232,37 @@ def exact_indexer_inputs(x, seed=5):
     x.iqs.fill_(0.125)
     x.iks.copy_((0.0625 + 0.0625 * torch.rand(tuple(x.iks.shape), generator=g)).to(x.iks.device))
     return x
+
+
+def kl_exact_dI_error(q8, qs, w, k8, ks, idx, seq_id, target, dI, block_table=None, page_size=64):
+    """Bound [T, k] on |gpu dI - oracle dI| for integer-valued FP8 codes.
+
+    The dot products are exact there, so logit j carries only the fp32
+    rounding of its head sum and scaling, E_j = IDX_FP32 sum_h |w_h| ReLU(r_hj);
+    the rest is the natural-input chain below with that E:
+    |d dI_j| <= q_j (expm1(2E) + KL_FP32) + 2^-22 (q_j + target_j).  The bound
+    is absolute: where q and target nearly cancel, dI's error is a part of q,
+    not of dI.  Padding entries get 0."""
+    qd = O.decode_e4m3fn(np.asarray(q8)) * np.asarray(qs, np.float64)[:, None, None]
+    w = np.asarray(w, np.float64)
+    k8 = np.asarray(k8)
+    ks = np.asarray(ks, np.float64)
+    out = np.zeros(np.asarray(idx).shape)
+    for t in range(qd.shape[0]):
+        js = np.nonzero(np.asarray(idx[t]) >= 0)[0]
+        if len(js) == 0:
+            continue
+        b = int(seq_id[t])
+        if block_table is None:
+            where = [(b, int(s)) for s in idx[t, js]]
+        else:
+            where = [(int(block_table[b, int(s) // page_size]), int(s) % page_size) for s in idx[t, js]]
+        kd = np.stack([O.decode_e4m3fn(k8[wh]) * ks[wh] for wh in where])
+        E = IDX_FP32 * float((np.maximum(qd[t] @ kd.T, 0.0).T @ np.abs(w[t])).max())
+        tg = np.asarray(target[t, js], np.float64)
+        qv = np.asarray(dI[t, js], np.float64) + tg
+        out[t, js] = qv * (np.expm1(2.0 * E) + KL_FP32) + 2.0 ** -22 * (qv + tg)
+    return out
 
 
 def kl_magnitudes(q8, qs, w, k8, ks, idx, seq_id, dI, block_table=None, page_size=64):

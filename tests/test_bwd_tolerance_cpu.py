@@ -96,7 +96,7 @@ def test_planted_mistakes_fail_and_roundings_pass():
 def test_kl_check_catches_planted_mistakes():
     """The KL gradients' check (2^-7 of the term magnitudes, Frobenius 1e-2)
     fails on plausible mistakes planted in the oracle's result."""
-    from parity_util import kl_magnitudes
+    from parity_util import KL_BF16, kl_exact_dI_error, kl_magnitudes
     g = np.random.default_rng(9)
     T, H_I, D_I, L, k = 3, 64, 128, 200, 40
     codes = np.array([0x00, 0x38, 0x40, 0x44, 0x48, 0xB8, 0xC0, 0xC4, 0xC8], dtype=np.uint8)
@@ -110,7 +110,12 @@ def test_kl_check_catches_planted_mistakes():
     tgt = g.uniform(size=(T, k))
     tgt /= tgt.sum(axis=1, keepdims=True)
     loss, dI, dq, dw, dk = O.indexer_kl(q8, qs, w, k8, ks, idx, seq_id, tgt)
-    m_dq, m_dk, _ = kl_magnitudes(q8, qs, w, k8, ks, idx, seq_id, dI)
+    # the magnitudes as the GPU check takes them: dI's own error bound added per term
+    args = (q8, qs, w, k8, ks, idx, seq_id)
+    m_dq, m_dk, _ = kl_magnitudes(*args, dI)
+    e_dq, e_dk, _ = kl_magnitudes(*args, kl_exact_dI_error(*args, tgt, dI))
+    m_dq = m_dq + e_dq / KL_BF16
+    m_dk = m_dk + e_dk / KL_BF16
     check_bwd(dq, dq, m_dq)
     check_bwd(dk, dk, m_dk)
 

@@ -12,11 +12,14 @@
   128 heads, k not a multiple of the 32-row tile, padding inside rows,
   paged caches);
 - the attention backward (dq, dkv) against the oracle, to the backward
-  tests' per-entry bounds.
+  tests' per-entry bounds;
+- the indexer's KL target, loss and gradients against the oracle, to the KL
+  tests' bounds.
 
 The shapes are drawn from a fixed seed, so every run checks the same cases.
 A sweep of this kind found a workspace size the fused call rejected (k + 320
-slots not a whole number of 64-slot tiles).
+slots not a whole number of 64-slot tiles), and a KL case where the check
+took dI's error as a part of |dI| although q and the target nearly cancelled.
 """
 
 import random
@@ -30,10 +33,12 @@ from sparse_attention_long_03_amd import binding as B
 from sparse_attention_long_03_amd import inputs as I
 from sparse_attention_long_03_amd.path import DSAPath
 
-from parity_util import bf16_to_np, check_attn, check_bwd, host_inputs, np_
+from parity_util import bf16_to_np, check_attn, check_bwd, exact_indexer_inputs, host_inputs, np_
 from test_gpu_attn_bwd import _oracle as _bwd_oracle
 from test_gpu_attn_bwd import _run as _bwd_run
 from test_gpu_fused_topk import _paged_copy
+from test_gpu_indexer_kl import _bt as _kl_bt
+from test_gpu_indexer_kl import _check_kl
 
 pytestmark = pytest.mark.gpu
 
@@ -187,21 +192,27 @@ def test_attention_random_shapes_match_oracle(case):
     np.testing.assert_allclose(np_(lse)[fin], rl[fin], rtol=1e-4, atol=1e-4)
 
 
-@pytest.mark.parametrize("case", range(8))
-def test_backward_random_shapes_match_oracle(case):
-    rng = random.Random(31337 + case)
+def _training_case(rng):
+    """A random training-shaped case: 16-128 heads, k from 1 to 700, one or
+    several queries per sequence or a causal prefill."""
     H = rng.choice([16, 32, 64, 128])
     k = rng.choice([1, 5, 31, 33, 100, 256, 700])
     kind = rng.choice(["decode", "multi", "prefill"])
     s = rng.randint(0, 10**6)
     if kind == "decode":
-        cfg = I.scaled(I.CONFIGS["decode32k"], B=rng.randint(1, 4), L=rng.randint(1, 2000), H=H, k=k, seed=s)
-    elif kind == "multi":
+        return I.scaled(I.CONFIGS["decode32k"], B=rng.randint(1, 4), L=rng.randint(1, 2000), H=H, k=k, seed=s)
+    if kind == "multi":
         L = rng.randint(1, 300)
-        cfg = I.scaled(I.CONFIGS["decode32k"], B=rng.randint(2, 4), L=L, queries_per_seq=rng.randint(1, min(L, 6)),
-                       H=H, k=k, seed=s)
-    else:
-        cfg = I.scaled(I.CONFIGS["prefill64k"], L=rng.randint(1, 200), H=H, k=k, seed=s)
+        return I.scaled(I.CONFIGS["decode32k"], B=rng.randint(2, 4), L=L, queries_per_seq=rng.randint(1, min(L, 6)),
+                        H=H, k=k, seed=s)
+    return I.scaled(I.CONFIGS["prefill64k"], L=rng.randint(1, 200), H=H, k=k, seed=s)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_backward_random_shapes_match_oracle(case):
+    rng = random.Random(31337 + case)
+    cfg = _training_case(rng)
+    k = cfg.k
     x = I.make_inputs(cfg, DEV)
     if rng.random() < 0.4:
         x = _paged_copy(x)
@@ -210,3 +221,26 @@ def test_backward_random_shapes_match_oracle(case):
     rdq, rdkv, m_dq, m_dkv = _bwd_oracle(x, sel, dO)
     check_bwd(np_(dq), rdq, m_dq, f"case {case} dq")
     check_bwd(np_(dkv), rdkv, m_dkv, f"case {case} dkv")
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_indexer_kl_random_shapes_match_oracle(case):
+    """The attention target and the indexer's KL loss and gradients on
+    integer-valued FP8 codes, to the KL tests' bounds."""
+    rng = random.Random(2718 + case)
+    cfg = _training_case(rng)
+    x = exact_indexer_inputs(I.make_inputs(cfg, DEV))
+    if rng.random() < 0.4:
+        x = _paged_copy(x)
+    idx = I.random_selection(cfg, x.pos, cfg.k, DEV)
+    print(f"kl case {case}: T={x.T} L={cfg.L} H={cfg.H} k={cfg.k} paged={x.block_table is not None}", flush=True)
+    p = DSAPath(x)
+    p.attn(idx)  # the forward's lse feeds the target
+    tgt = np_(p.kl_target(idx))
+    ref = O.indexer_kl_target(I.bf16_bits(x.q), I.bf16_bits(x.kv), idx.cpu().numpy(), np_(x.seq_id), cfg.scale,
+                              _kl_bt(x))
+    assert np.all(np.abs(tgt - ref) <= 1e-3 * ref + 1e-7)
+    target = ref.astype(np.float32)
+    loss, dq, dw, dk = p.indexer_kl(idx, torch.from_numpy(target).to(DEV))
+    torch.cuda.synchronize()
+    _check_kl(x, idx, target.astype(np.float64), loss, dq, dw, dk, f"case {case}")
