@@ -14,7 +14,7 @@
 - the attention backward (dq, dkv) against the oracle, to the backward
   tests' per-entry bounds;
 - the indexer's KL target, loss and gradients against the oracle, to the KL
-  tests' bounds.
+  tests' bounds, on integer FP8 codes and on the generated (natural) ones.
 
 The shapes are drawn from a fixed seed, so every run checks the same cases.
 A sweep of this kind found a workspace size the fused call rejected (k + 320
@@ -33,7 +33,8 @@ from sparse_attention_long_03_amd import binding as B
 from sparse_attention_long_03_amd import inputs as I
 from sparse_attention_long_03_amd.path import DSAPath
 
-from parity_util import bf16_to_np, check_attn, check_bwd, exact_indexer_inputs, host_inputs, np_
+from parity_util import (bf16_to_np, check_attn, check_bwd, exact_indexer_inputs, host_inputs,
+                         kl_natural_tolerances, np_)
 from test_gpu_attn_bwd import _oracle as _bwd_oracle
 from test_gpu_attn_bwd import _run as _bwd_run
 from test_gpu_fused_topk import _paged_copy
@@ -244,3 +245,32 @@ def test_indexer_kl_random_shapes_match_oracle(case):
     loss, dq, dw, dk = p.indexer_kl(idx, torch.from_numpy(target).to(DEV))
     torch.cuda.synchronize()
     _check_kl(x, idx, target.astype(np.float64), loss, dq, dw, dk, f"case {case}")
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_indexer_kl_natural_random_shapes(case):
+    """The KL loss and gradients on the generated FP8 codes (query scales
+    divided by 16: logits of order 10), each value within the bound derived
+    from the FP8 accumulation bound."""
+    rng = random.Random(8128 + case)
+    cfg = _training_case(rng)
+    x = I.make_inputs(cfg, DEV)
+    x.iqs.mul_(1.0 / 16)
+    if rng.random() < 0.4:
+        x = _paged_copy(x)
+    idx = I.random_selection(cfg, x.pos, cfg.k, DEV)
+    sel = idx.cpu().numpy()
+    print(f"kl natural case {case}: T={x.T} L={cfg.L} k={cfg.k} paged={x.block_table is not None}", flush=True)
+    target = O.indexer_kl_target(I.bf16_bits(x.q), I.bf16_bits(x.kv), sel, np_(x.seq_id), cfg.scale,
+                                 _kl_bt(x)).astype(np.float32)
+    p = DSAPath(x)
+    loss, dq, dw, dk = p.indexer_kl(idx, torch.from_numpy(target).to(DEV))
+    torch.cuda.synchronize()
+    t64 = target.astype(np.float64)
+    args = (np_(x.iq8), np_(x.iqs).astype(np.float64), np_(x.iw).astype(np.float64), np_(x.ik8),
+            np_(x.iks).astype(np.float64), sel, np_(x.seq_id), t64)
+    rl, rdI, rdq, rdw, rdk = O.indexer_kl(*args, _kl_bt(x))
+    tols = kl_natural_tolerances(*args, rdI, _kl_bt(x))
+    for what, g, r, tol in zip(("loss", "dw", "dq", "dk"), (loss, dw, dq, dk), (rl, rdw, rdq, rdk), tols):
+        err = np.abs(np_(g).astype(np.float64) - r)
+        assert np.all(err <= tol), f"case {case} {what}: {int((err > tol).sum())} values beyond the derived bound"
