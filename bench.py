@@ -512,6 +512,18 @@ def bench_kl_dense(args, cfg):
     nbytes = 2 * n * cfg.D * 2 + n * 4 + 2 * x0.T * cfg.H * cfg.D * 2
     flops = 2 * 2 * n * cfg.H * cfg.D
     gbs = nbytes / (avg * 1e-3) / 1e9
+    # the one-pass form (dsa_indexer_kl_target_dense_lse), given each replica's
+    # dense lse as a dense attention forward would return it: one read of the rows
+    lses = []
+    for f in fns[:REPLICAS]:
+        f()
+        lses.append(lse.clone())
+    fns1 = [(lambda p=p, x=x, l=l: B.dsa_indexer_kl_target_dense_lse(p.q, p.layout, cfg.H, x.q, x.kv, cfg.scale, l,
+                                                                     target)) for p, x, l in zip(paths, xs, lses)]
+    timed_rotation(fns1, 2 * REPLICAS, stream)
+    avg1 = batch_rotation(fns1, n_launch, stream)
+    nbytes1 = n * cfg.D * 2 + n * 4 + x0.T * cfg.H * (cfg.D * 2 + 4)
+    gbs1 = nbytes1 / (avg1 * 1e-3) / 1e9
     out = {"metric": "dense warm-up KL target query tokens/s @128K ctx (every position)",
            "value": round(x0.T / (avg * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": n_launch,
            "warmup": 2 * REPLICAS, "ms_per_step": round(avg, 4), "higher_is_better": True, "scaling": "weak",
@@ -523,7 +535,9 @@ def bench_kl_dense(args, cfg):
                         "bytes_per_launch": nbytes, "avg_launch_us": round(avg * 1e3, 1),
                         "p10_us": round(sorted(ts)[len(ts) // 10] * 1e3, 1),
                         "p90_us": round(sorted(ts)[(9 * len(ts)) // 10] * 1e3, 1)},
-           "kernels": {"tflops": round(flops / (avg * 1e-3) / 1e12, 1)}}
+           "kernels": {"tflops": round(flops / (avg * 1e-3) / 1e12, 1),
+                       "one_pass_given_lse_ms": round(avg1, 4), "one_pass_gbs": round(gbs1, 1),
+                       "one_pass_frac_hbm": round(gbs1 / HBM_PEAK_GBS, 4), "one_pass_bytes": nbytes1}}
     print(json.dumps(out), flush=True)
 
 

@@ -311,6 +311,23 @@ int dsa_indexer_kl_target_dense(const dsa_queries* q, const dsa_kv_layout* layou
                                 const void* kv_bf16, float sm_scale, float* target, int64_t ld_target, float* lse_out,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* dsa_indexer_kl_target_dense_lse: the same dense warm-up target as
+ * dsa_indexer_kl_target_dense, given the dense attention's lse:
+ *     target[t * ld_target + s] = (1/H) sum_h exp(z[t,h,s] - lse[t,h])
+ * for s = 0..pos[t].  During the warm-up the main model runs dense attention
+ * over every position, and its forward returns exactly this lse ("Teaching
+ * signal": the target is the main attention's head-summed distribution), so
+ * the target needs one pass over the rows instead of two and no workspace.
+ * Entries past pos[t] are left unwritten.
+ *   arguments : q, layout, H, q_bf16, kv_bf16, sm_scale as for dsa_sparse_mla_attn
+ *   lse       : device float[T, H], natural log, over positions 0..pos[t]
+ *               (the rows sum to 1 only when it is that lse)
+ *   target    : device float[T, ld_target], ld_target >= max_len
+ * ------------------------------------------------------------------------- */
+int dsa_indexer_kl_target_dense_lse(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H, const void* q_bf16,
+                                    const void* kv_bf16, float sm_scale, const float* lse, float* target,
+                                    int64_t ld_target, hipStream_t stream);
+
 /* dsa_indexer_kl: with the indexer logits I (as dsa_indexer_logits) at the
  * selected entries, q[t, j] = softmax_j I[t, idx[t, j]] over the entries != -1:
  *     loss[t] = sum_j target[t,j] (log target[t,j] - log q[t,j])

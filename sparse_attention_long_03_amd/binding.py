@@ -52,7 +52,8 @@ class dsa_ws_region(ctypes.Structure):
 
 EXPORTS = ("dsa_cache_write", "dsa_indexer_project", "dsa_indexer_logits", "dsa_indexer_topk", "dsa_topk", "dsa_sparse_mla_attn",
            "dsa_sparse_mla_attn_bwd", "dsa_sparse_mla_attn_bwd_dq", "dsa_sparse_mla_attn_bwd_dkv",
-           "dsa_indexer_kl_target", "dsa_indexer_kl_target_dense", "dsa_indexer_kl", "dsa_masked_dense_attn", "dsa_forward", "dsa_forward_noalloc",
+           "dsa_indexer_kl_target", "dsa_indexer_kl_target_dense", "dsa_indexer_kl_target_dense_lse",
+           "dsa_indexer_kl", "dsa_masked_dense_attn", "dsa_forward", "dsa_forward_noalloc",
            "dsa_workspace_bytes", "dsa_workspace_layout",
            "dsa_status_str", "dsa_abi_version")
 
@@ -81,6 +82,7 @@ def lib() -> ctypes.CDLL:
     L.dsa_indexer_kl_target.argtypes = [Q, KV, i32, vp, vp, vp, i32, f32, vp, vp, vp]
     L.dsa_indexer_kl_target_dense.argtypes = [Q, KV, i32, vp, vp, f32, vp, i64, vp, vp, sz, vp]
     L.dsa_indexer_kl_target_dense.restype = ctypes.c_int
+    L.dsa_indexer_kl_target_dense_lse.argtypes = [Q, KV, i32, vp, vp, f32, vp, vp, i64, vp]
     L.dsa_indexer_kl.argtypes = [Q, KV, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_masked_dense_attn.argtypes = [Q, KV, i32, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
     L.dsa_forward.argtypes = [Q, KV, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]
@@ -261,6 +263,14 @@ def dsa_indexer_kl_target_dense(q: dsa_queries, layout: dsa_kv_layout, H: int, q
                                            float(sm_scale), _ptr(target), int(target.shape[-1]), _ptr(lse_out),
                                            _ptr(ws), nbytes, _stream(stream))
     _check(st, "dsa_indexer_kl_target_dense")
+
+
+def dsa_indexer_kl_target_dense_lse(q: dsa_queries, layout: dsa_kv_layout, H: int, q_bf16, kv_bf16,
+                                    sm_scale: float, lse: torch.Tensor, target: torch.Tensor, stream=None):
+    st = lib().dsa_indexer_kl_target_dense_lse(ctypes.byref(q), ctypes.byref(layout), H, _ptr(q_bf16), _ptr(kv_bf16),
+                                               float(sm_scale), _ptr(lse), _ptr(target), int(target.shape[-1]),
+                                               _stream(stream))
+    _check(st, "dsa_indexer_kl_target_dense_lse")
 
 
 def dsa_indexer_kl(q: dsa_queries, layout: dsa_kv_layout, H_I: int, D_I: int, q_fp8, q_scale, w, k_fp8, k_scale,

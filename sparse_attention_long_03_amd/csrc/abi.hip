@@ -388,6 +388,25 @@ int dsa_indexer_kl_target_dense(const dsa_queries* q, const dsa_kv_layout* layou
                                            target, ld_target, lse_out, workspace, stream));
 }
 
+int dsa_indexer_kl_target_dense_lse(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H,
+                                    const void* q_bf16, const void* kv_bf16, float sm_scale, const float* lse,
+                                    float* target, int64_t ld_target, hipStream_t stream) {
+  Layout lay;
+  int st = check_queries(q);
+  if (st) return st;
+  if ((st = check_layout(layout, q, &lay))) return st;
+  if (H < 1 || !(sm_scale > 0.f)) return DSA_ERR_INVALID_ARG;
+  if (!attn_supported(H)) return DSA_ERR_UNSUPPORTED;
+  if (q->T == 0) return DSA_OK;
+  if (!q_bf16 || !kv_bf16 || !lse || !target || !aligned(q_bf16, 16) || !aligned(kv_bf16, 16) || !aligned(lse, 4) ||
+      !aligned(target, 4))
+    return DSA_ERR_INVALID_ARG;
+  if (ld_target < q->max_len) return DSA_ERR_INVALID_ARG;
+  return hip_status(launch_kl_target_dense_lse(q->T, H, q->max_len, static_cast<const uint16_t*>(q_bf16),
+                                               static_cast<const uint16_t*>(kv_bf16), q->seq_id, q->pos, lay,
+                                               sm_scale, lse, target, ld_target, stream));
+}
+
 int dsa_indexer_kl(const dsa_queries* q, const dsa_kv_layout* layout, int32_t H_I, int32_t D_I,
                    const uint8_t* q_fp8, const float* q_scale, const float* w, const uint8_t* k_fp8,
                    const float* k_scale, const int32_t* idx, int32_t k, const float* target, float* loss, float* dq,

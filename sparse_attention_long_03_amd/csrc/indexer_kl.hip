@@ -45,8 +45,11 @@ constexpr float LOG2E = 1.4426950408889634f;
 //   KT_DENSE_TARGET  every lane first merges the chunks' (m, l) of its head
 //                    into the dense lse (the warm-up's attention runs over
 //                    every position), then the target of each position.
+// When the caller has the dense lse already (the warm-up's dense attention
+// forward returns it), KT_DENSE_GIVEN takes it as input and runs the second
+// launch alone: every row is read once instead of twice.
 constexpr int KT_NW = 8;
-enum KtMode { KT_SELECTED = 0, KT_DENSE_LSE = 1, KT_DENSE_TARGET = 2 };
+enum KtMode { KT_SELECTED = 0, KT_DENSE_LSE = 1, KT_DENSE_TARGET = 2, KT_DENSE_GIVEN = 3 };
 
 template <int MODE>
 __global__ __launch_bounds__(KT_NW * 64) void kl_target_kernel(const uint16_t* __restrict__ q,
@@ -108,7 +111,7 @@ __global__ __launch_bounds__(KT_NW * 64) void kl_target_kernel(const uint16_t* _
   // lse of head hq in log2 units: given (the forward's), or merged from the
   // dense chunks' (m, l)
   float lse2 = 0.f;
-  if constexpr (MODE == KT_SELECTED) {
+  if constexpr (MODE == KT_SELECTED || MODE == KT_DENSE_GIVEN) {
     lse2 = lse[(int64_t)t * H + hq] * LOG2E;
   } else if constexpr (MODE == KT_DENSE_TARGET) {
     const int nch = min(n_chunks, (pos[t] + AT_MAX_SPLIT) / AT_MAX_SPLIT);
@@ -588,6 +591,17 @@ hipError_t launch_kl_target_dense(int T, int H, int max_len, const uint16_t* q, 
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kl_target_kernel<KT_DENSE_TARGET>, dim3(T, nch), dim3(KT_NW * 64), 0, stream, q, kvb, nullptr,
                      seq_id, pos, lay, H, 0, sm_scale * LOG2E, nullptr, target, ld, ml, nch, lse_out, T);
+  return hipGetLastError();
+}
+
+hipError_t launch_kl_target_dense_lse(int T, int H, int max_len, const uint16_t* q, const uint16_t* kv,
+                                      const int32_t* seq_id, const int32_t* pos, const Layout& lay, float sm_scale,
+                                      const float* lse, float* target, int64_t ld, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int nch = dense_target_chunks(max_len);
+  const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv);
+  hipLaunchKernelGGL(kl_target_kernel<KT_DENSE_GIVEN>, dim3(T, nch), dim3(KT_NW * 64), 0, stream, q, kvb, nullptr,
+                     seq_id, pos, lay, H, 0, sm_scale * LOG2E, lse, target, ld, nullptr, nch, nullptr, T);
   return hipGetLastError();
 }
 

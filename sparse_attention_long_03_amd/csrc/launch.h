@@ -160,6 +160,9 @@ size_t kl_target_dense_workspace_bytes(int T, int H, int max_len);
 hipError_t launch_kl_target_dense(int T, int H, int max_len, const uint16_t* q, const uint16_t* kv,
                                   const int32_t* seq_id, const int32_t* pos, const Layout& lay, float sm_scale,
                                   float* target, int64_t ld, float* lse_out, void* ws, hipStream_t stream);
+hipError_t launch_kl_target_dense_lse(int T, int H, int max_len, const uint16_t* q, const uint16_t* kv,
+                                      const int32_t* seq_id, const int32_t* pos, const Layout& lay, float sm_scale,
+                                      const float* lse, float* target, int64_t ld, hipStream_t stream);
 hipError_t launch_kl(int T, const uint8_t* q8, const float* qs, const float* w, const uint8_t* k8, const float* ks,
                      const int32_t* idx, const int32_t* seq_id, const Layout& lay, int64_t num_rows, int k,
                      const float* target, float* loss, float* dq, float* dw, float* dk, void* ws,

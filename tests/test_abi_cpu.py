@@ -332,3 +332,21 @@ def test_kl_target_dense_validation(lib):
     assert call(target=None) == B.DSA_ERR_INVALID_ARG
     assert call(nbytes=need - 1) == B.DSA_ERR_WORKSPACE
     assert call(q_=_q(T=0, seq=None, pos=None)) == B.DSA_OK
+
+
+
+def test_kl_target_dense_lse_validation(lib):
+    f = lib.dsa_indexer_kl_target_dense_lse
+    lay = _lay(5000)
+
+    def call(q_=None, H=128, ld=5000, lse=FAKE, target=FAKE, scale=0.04):
+        q_ = q_ or _q(T=4, max_len=5000)
+        return f(ctypes.byref(q_), ctypes.byref(lay), H, FAKE, FAKE, scale, lse, target, ld, None)
+
+    assert call(H=24) == B.DSA_ERR_UNSUPPORTED
+    assert call(scale=0.0) == B.DSA_ERR_INVALID_ARG
+    assert call(ld=4999) == B.DSA_ERR_INVALID_ARG
+    assert call(lse=None) == B.DSA_ERR_INVALID_ARG
+    assert call(lse=ctypes.c_void_p((1 << 20) + 2)) == B.DSA_ERR_INVALID_ARG   # misaligned
+    assert call(target=None) == B.DSA_ERR_INVALID_ARG
+    assert call(q_=_q(T=0, seq=None, pos=None)) == B.DSA_OK

@@ -162,3 +162,8 @@ def test_dense_warmup_target_stays_in_its_buffers():
     B.dsa_indexer_kl_target_dense(p.q, p.layout, cfg.H, x.q, x.kv, cfg.scale, tgt, lse, ws.bytes())
     torch.cuda.synchronize()
     assert ws.intact() and gt.intact() and gl.intact()
+    # the one-pass form, given that lse
+    g1, tgt1 = _guarded(torch.float32, (x.T, p.ld))
+    B.dsa_indexer_kl_target_dense_lse(p.q, p.layout, cfg.H, x.q, x.kv, cfg.scale, lse, tgt1)
+    torch.cuda.synchronize()
+    assert g1.intact() and gl.intact()

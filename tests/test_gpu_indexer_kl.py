@@ -258,6 +258,56 @@ def test_dense_warmup_target_at_128k():
     _check_dense_row(x, 0, tgt[0], lse[0], "128K")
 
 
+def _dense_oracle_lse(x, t):
+    n = int(x.pos[t]) + 1
+    sel = np.arange(n, dtype=np.int32)[None]
+    q_t, sid = I.bf16_bits(x.q[t:t + 1]), np.array([int(x.seq_id[t])])
+    _, rl = O.sparse_mla_attention(q_t, I.bf16_bits(x.kv), sel, sid, x.cfg.scale, 512, _bt(x))
+    return rl[0]
+
+
+@pytest.mark.parametrize("name", ["decode_16k", "paged"])
+def test_dense_target_given_lse_matches_oracle(name):
+    """The one-pass dense target, given the oracle's dense lse (as a dense
+    attention forward would return it), against the oracle's target."""
+    x = I.make_inputs(DENSE[name], DEV)
+    c = x.cfg
+    p = DSAPath(x)
+    print(f"dense target given lse {name}: T={x.T} H={c.H} max_len={x.max_len}", flush=True)
+    lse = torch.from_numpy(np.stack([_dense_oracle_lse(x, t) for t in range(x.T)]).astype(np.float32)).to(DEV)
+    target = torch.full((x.T, p.ld), -7.0, dtype=torch.float32, device=DEV)
+    B.dsa_indexer_kl_target_dense_lse(p.q, p.layout, c.H, x.q, x.kv, c.scale, lse, target)
+    torch.cuda.synchronize()
+    tgt = np_(target)
+    for t in range(x.T):
+        n = int(x.pos[t]) + 1
+        sel = np.arange(n, dtype=np.int32)[None]
+        q_t, sid = I.bf16_bits(x.q[t:t + 1]), np.array([int(x.seq_id[t])])
+        ref = O.indexer_kl_target(q_t, I.bf16_bits(x.kv), sel, sid, c.scale, _bt(x))[0]
+        err = np.abs(tgt[t, :n] - ref)
+        assert np.all(err <= 1e-3 * ref + 1e-12), f"query {t}: max relative err {np.max(err / ref):.3g}"
+        assert np.all(tgt[t, n:] == -7.0), f"query {t}: written past pos"
+        np.testing.assert_allclose(tgt[t, :n].sum(), 1.0, rtol=1e-4)
+
+
+def test_dense_target_one_pass_equals_two_pass():
+    """Given the two-pass form's own lse, the one-pass form computes the same
+    target (up to the lse's rounding through natural-log units)."""
+    cfg = I.scaled(I.CONFIGS["decode32k"], B=2, L=9000, queries_per_seq=2, H=64, k=512)
+    x = I.make_inputs(cfg, DEV)
+    p = DSAPath(x)
+    tgt2, lse = _dense_target(x)
+    target = torch.full((x.T, p.ld), -7.0, dtype=torch.float32, device=DEV)
+    B.dsa_indexer_kl_target_dense_lse(p.q, p.layout, cfg.H, x.q, x.kv, cfg.scale, torch.from_numpy(lse).to(DEV),
+                                      target)
+    torch.cuda.synchronize()
+    tgt1 = np_(target)
+    for t in range(x.T):
+        n = int(x.pos[t]) + 1
+        np.testing.assert_allclose(tgt1[t, :n], tgt2[t, :n], rtol=1e-5, atol=0)
+        assert np.all(tgt1[t, n:] == -7.0)
+
+
 def test_dense_warmup_target_equals_selected_target_with_every_position():
     """Below 2048 positions the sparse-stage target over a selection holding
     every position is the same computation: equal up to the lse rounding."""
