@@ -51,6 +51,16 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr int KT_NW = 8;
 enum KtMode { KT_SELECTED = 0, KT_DENSE_LSE = 1, KT_DENSE_TARGET = 2, KT_DENSE_GIVEN = 3 };
 
+// Sum over the 16 lanes of each row of the wave (every lane ends with its
+// row's sum): row rotations by 8, 4, 2 and 1 lanes.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror:8
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));  // row_ror:4
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false));  // row_ror:2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false));  // row_ror:1
+  return v;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(KT_NW * 64) void kl_target_kernel(const uint16_t* __restrict__ q,
                                                              const uint8_t* __restrict__ kv,
@@ -183,10 +193,11 @@ __global__ __launch_bounds__(KT_NW * 64) void kl_target_kernel(const uint16_t* _
         p[i] = __builtin_amdgcn_exp2f(s0[i] * scale_log2 - lse2);
         p[4 + i] = __builtin_amdgcn_exp2f(s1[i] * scale_log2 - lse2);
       }
+      // sum over the 16 heads of the lane group: rotations within each row
+      // of 16 lanes (DPP, on the VALU, not through LDS); lane n = 0 ends
+      // with the row's sum
 #pragma unroll
-      for (int d = 1; d < 16; d <<= 1)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) p[i] += __shfl_xor(p[i], d, 64);
+      for (int i = 0; i < 8; ++i) p[i] = row_sum16(p[i]);
       if (n == 0 && has_heads) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
