@@ -180,10 +180,12 @@ __global__ __launch_bounds__(KT_NW * 64) void kl_target_kernel(const uint16_t* _
 #pragma unroll
       for (int i = 0; i < 8; ++i) mx = fmaxf(mx, z[i]);
       if (mx > -INFINITY) {
+        // v_exp_f32: arguments are <= 0, and results below 2^-126 flush to 0
+        // (terms under 2^-126 of the running maximum's)
         float add = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) add += exp2f(z[i] - mx);
-        l_run = l_run * exp2f(m_run - mx) + add;  // exp2(-inf) = 0 on the first tile
+        for (int i = 0; i < 8; ++i) add += __builtin_amdgcn_exp2f(z[i] - mx);
+        l_run = l_run * __builtin_amdgcn_exp2f(m_run - mx) + add;  // exp2(-inf) = 0 on the first tile
         m_run = mx;
       }
     } else {
