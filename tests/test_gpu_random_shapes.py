@@ -14,7 +14,10 @@
 - the attention backward (dq, dkv) against the oracle, to the backward
   tests' per-entry bounds;
 - the indexer's KL target, loss and gradients against the oracle, to the KL
-  tests' bounds, on integer FP8 codes and on the generated (natural) ones.
+  tests' bounds, on integer FP8 codes and on the generated (natural) ones;
+- the masked dense variant against the oracle and the sparse gather; the
+  cache write and the indexer projection bit for bit; the dense warm-up
+  target in both forms against the oracle.
 
 The shapes are drawn from a fixed seed, so every run checks the same cases.
 A sweep of this kind found a workspace size the fused call rejected (k + 320
@@ -38,7 +41,10 @@ from parity_util import (bf16_to_np, check_attn, check_bwd, exact_indexer_inputs
 from test_gpu_attn_bwd import _oracle as _bwd_oracle
 from test_gpu_attn_bwd import _run as _bwd_run
 from test_gpu_fused_topk import _paged_copy
+from test_gpu_cache_write import _run as _cache_write_run
 from test_gpu_indexer_kl import _bt as _kl_bt
+from test_gpu_indexer_kl import _check_dense_row, _dense_oracle_lse, _dense_target
+from test_gpu_indexer_proj import _run as _proj_run
 from test_gpu_indexer_kl import _check_kl
 
 pytestmark = pytest.mark.gpu
@@ -274,3 +280,105 @@ def test_indexer_kl_natural_random_shapes(case):
     for what, g, r, tol in zip(("loss", "dw", "dq", "dk"), (loss, dw, dq, dk), (rl, rdw, rdq, rdk), tols):
         err = np.abs(np_(g).astype(np.float64) - r)
         assert np.all(err <= tol), f"case {case} {what}: {int((err > tol).sum())} values beyond the derived bound"
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_masked_dense_random_shapes_match_oracle(case):
+    """The masked dense variant (rows up to 16K positions, the longest it
+    takes) against the oracle's masked dense definition and against the
+    sparse gather on the same selection."""
+    rng = random.Random(6060 + case)
+    H = rng.choice([16, 32, 64, 128])
+    k = rng.choice([1, 31, 100, 700, 2048])
+    s = rng.randint(0, 10**6)
+    if rng.random() < 0.5:
+        cfg = I.scaled(I.CONFIGS["decode32k"], B=rng.randint(1, 3), L=rng.randint(1, 16384), H=H, k=k, seed=s)
+    else:
+        L = rng.randint(1, 400)
+        cfg = I.scaled(I.CONFIGS["decode32k"], B=rng.randint(2, 4), L=L, queries_per_seq=rng.randint(1, min(L, 5)),
+                       H=H, k=k, seed=s)
+    x = I.make_inputs(cfg, DEV)
+    if rng.random() < 0.4:
+        x = _paged_copy(x)
+    idx = I.random_selection(cfg, x.pos, k, DEV)
+    print(f"masked dense case {case}: T={x.T} L={cfg.L} H={H} k={k} paged={x.block_table is not None}", flush=True)
+    p = DSAPath(x)
+    o_s = p.attn(idx)[0].clone()
+    o_d, l_d = p.dense_attn(idx)
+    torch.cuda.synchronize()
+    check_attn(bf16_to_np(o_d), bf16_to_np(o_s).astype(np.float64), f"case {case} dense vs sparse")
+    h = host_inputs(x)
+    rows = sorted({0, x.T // 2, x.T - 1})
+    ro, rl = O.masked_dense_attention(h["q"][rows], h["kv"], np_(idx)[rows], h["seq_id"][rows], h["pos"][rows],
+                                      cfg.scale, block_table=h["bt"])
+    check_attn(bf16_to_np(o_d[rows]), ro, f"case {case} dense vs oracle")
+    fin = np.isfinite(rl)
+    assert np.array_equal(fin, np.isfinite(np_(l_d)[rows]))
+    np.testing.assert_allclose(np_(l_d)[rows][fin], rl[fin], rtol=1e-4, atol=1e-4)
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_cache_write_random_shapes_bit_exact(case):
+    """FP8 codes, scales and latent rows of random batches of new tokens
+    (hard key values included), bit-exact against the oracle."""
+    rng = random.Random(7070 + case)
+    T, D = rng.randint(1, 400), rng.choice([64, 128])
+    paged, with_kv = rng.random() < 0.5, rng.random() < 0.7
+    print(f"cache write case {case}: T={T} D={D} paged={paged} rows={with_kv}", flush=True)
+    (g8, gs, gkv), (r8, rs, rkv) = _cache_write_run(T=T, D=D, paged=paged, with_kv=with_kv, seed=rng.randint(0, 10**6))
+    assert np.array_equal(g8, r8)
+    assert np.array_equal(gs.view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(gkv, rkv)
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_projection_random_shapes_bit_exact(case):
+    """The indexer projection on integer-valued inputs (every sum exact in
+    any order): codes, scales, weights and keys bit for bit."""
+    rng = random.Random(8080 + case)
+    T = rng.randint(1, 150)
+    d = 64 * rng.randint(1, 64)
+    H_I, D_I = rng.choice([(64, 128), (64, 64), (4, 128), (4, 64)])
+    with_k = rng.random() < 0.6
+    print(f"projection case {case}: T={T} d={d} H_I={H_I} D_I={D_I} key={with_k}", flush=True)
+    (q8, qs, w, k), (rq8, rqs, rw, rk), _ = _proj_run(T, d, H_I, D_I, with_k, exact=True, seed=rng.randint(0, 10**6))
+    assert np.array_equal(qs, rqs)
+    assert np.array_equal(q8, rq8)
+    assert np.array_equal(w, rw)
+    if with_k:
+        assert np.array_equal(k, rk)
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_dense_target_random_shapes_match_oracle(case):
+    """The dense warm-up target, in two passes and given the oracle's dense
+    lse in one, against the oracle with every position selected."""
+    rng = random.Random(9090 + case)
+    H = rng.choice([16, 32, 64, 128])
+    s = rng.randint(0, 10**6)
+    if rng.random() < 0.5:
+        cfg = I.scaled(I.CONFIGS["decode32k"], B=rng.randint(1, 3), L=rng.randint(1, 9000), H=H, k=256, seed=s)
+    else:
+        L = rng.randint(1, 300)
+        cfg = I.scaled(I.CONFIGS["decode32k"], B=rng.randint(2, 4), L=L, queries_per_seq=rng.randint(1, min(L, 4)),
+                       H=H, k=256, seed=s)
+    x = I.make_inputs(cfg, DEV)
+    if rng.random() < 0.4:
+        x = _paged_copy(x)
+    print(f"dense target case {case}: T={x.T} L={cfg.L} H={H} paged={x.block_table is not None}", flush=True)
+    tgt, lse = _dense_target(x)
+    for t in range(x.T):
+        _check_dense_row(x, t, tgt[t], lse[t], f"case {case}")
+    p = DSAPath(x)
+    rlse = torch.from_numpy(np.stack([_dense_oracle_lse(x, t) for t in range(x.T)]).astype(np.float32)).to(DEV)
+    target = torch.full((x.T, p.ld), -7.0, dtype=torch.float32, device=DEV)
+    B.dsa_indexer_kl_target_dense_lse(p.q, p.layout, H, x.q, x.kv, cfg.scale, rlse, target)
+    torch.cuda.synchronize()
+    one = np_(target)
+    for t in range(x.T):
+        n = int(x.pos[t]) + 1
+        sel = np.arange(n, dtype=np.int32)[None]
+        q_t, sid = I.bf16_bits(x.q[t:t + 1]), np.array([int(x.seq_id[t])])
+        ref = O.indexer_kl_target(q_t, I.bf16_bits(x.kv), sel, sid, cfg.scale, _kl_bt(x))[0]
+        assert np.all(np.abs(one[t, :n] - ref) <= 1e-3 * ref + 1e-12), f"case {case} one pass, query {t}"
+        assert np.all(one[t, n:] == -7.0)
