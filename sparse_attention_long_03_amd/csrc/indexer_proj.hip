@@ -12,7 +12,7 @@
 // Two kernels.
 //   proj_gemm_kernel   [T x d] x [d x N] on 16x16x32 bf16 MFMAs, N the
 //                      concatenated output columns (q, then w, then k).  A
-//                      workgroup takes TM tokens x 128 columns (32 per wave)
+//                      workgroup takes TM tokens x 64 or 128 columns (16 or 32 per wave)
 //                      over one slice of the hidden dims: the h tile is staged
 //                      in LDS (shared by the four waves), each wave streams
 //                      its own weight rows straight into B fragments.  The
@@ -30,7 +30,6 @@
 namespace dsa {
 
 constexpr int PJ_NT = 256;                  // threads per workgroup (4 waves)
-constexpr int PJ_BN = 128;                  // output columns per workgroup (32 per wave)
 constexpr int PJ_BK = 64;                   // hidden dims per stage
 constexpr int PJ_ASTRIDE = PJ_BK * 2 + 16;  // bytes per staged h row (padded: rotates LDS banks)
 constexpr int PJ_MAX_SPLITS = 8;
@@ -39,13 +38,14 @@ constexpr int PJ_MAX_SPLITS = 8;
 #define LDS_AS __attribute__((address_space(3)))
 #endif
 
-template <int TM>
+template <int TM, int JC>
 __global__ __launch_bounds__(PJ_NT) void proj_gemm_kernel(const uint16_t* __restrict__ h,
                                                           const uint16_t* __restrict__ wq,
                                                           const uint16_t* __restrict__ ww,
                                                           const uint16_t* __restrict__ wk, int T, int d, int Nq,
                                                           int Nw, int N, int kchunk, float* __restrict__ part) {
   constexpr int MT = TM / 16;                         // 16-token tiles
+  constexpr int BN = 4 * 16 * JC;                     // output columns per workgroup (16 JC per wave)
   constexpr int ACH = TM * (PJ_BK / 8);               // 16-byte chunks of one staged h tile
   constexpr int APER = (ACH + PJ_NT - 1) / PJ_NT;     // chunks per thread
   __shared__ __align__(16) uint8_t a_lds[2][TM * PJ_ASTRIDE];
@@ -59,12 +59,12 @@ __global__ __launch_bounds__(PJ_NT) void proj_gemm_kernel(const uint16_t* __rest
   const int k_begin = blockIdx.z * kchunk;
   const int nsteps = kchunk / PJ_BK;
 
-  // the weight rows of this lane's two output columns (columns past N read
+  // the weight rows of this lane's JC output columns (columns past N read
   // the last one; their results are not stored)
-  const int c0 = blockIdx.x * PJ_BN + wid * 32;
-  const uint16_t* wrow[2];
+  const int c0 = blockIdx.x * BN + wid * 16 * JC;
+  const uint16_t* wrow[JC];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < JC; ++j) {
     const int col = min(c0 + 16 * j + n, N - 1);
     const uint16_t* base = col < Nq ? wq + (int64_t)col * d
                                     : (col < Nq + Nw ? ww + (int64_t)(col - Nq) * d : wk + (int64_t)(col - Nq - Nw) * d);
@@ -93,20 +93,20 @@ __global__ __launch_bounds__(PJ_NT) void proj_gemm_kernel(const uint16_t* __rest
     }
   };
   // B fragments of one stage: [column tile][half of the 64 dims]
-  v4i breg[2][2];
+  v4i breg[JC][2];
   auto b_load = [&](int step) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < JC; ++j)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
         breg[j][hh] = *reinterpret_cast<const v4i*>(wrow[j] + step * PJ_BK + 32 * hh);
   };
 
-  v4f acc[MT][2];
+  v4f acc[MT][JC];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[mt][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < JC; ++j) acc[mt][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   a_load(0);
   b_load(0);
@@ -114,9 +114,9 @@ __global__ __launch_bounds__(PJ_NT) void proj_gemm_kernel(const uint16_t* __rest
   __syncthreads();
   for (int step = 0; step < nsteps; ++step) {
     const int buf = step & 1;
-    v4i bcur[2][2];
+    v4i bcur[JC][2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < JC; ++j)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) bcur[j][hh] = breg[j][hh];
     const bool more = step + 1 < nsteps;
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(PJ_NT) void proj_gemm_kernel(const uint16_t* __rest
         // A fragment: token 16mt + n, dims 32hh + 8g .. +8 of the stage
         const v8bf a = *reinterpret_cast<const LDS_AS v8bf*>(abuf + (16 * mt + n) * PJ_ASTRIDE + 64 * hh + 16 * g);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < JC; ++j)
           acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, bcur[j][hh]), acc[mt][j],
                                                                0, 0, 0);
       }
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(PJ_NT) void proj_gemm_kernel(const uint16_t* __rest
   // lane holds column c0 + 16j + n for tokens t0 + 16mt + 4g + i
   float* __restrict__ out = part + (int64_t)blockIdx.z * T * N;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < JC; ++j) {
     const int col = c0 + 16 * j + n;
     if (col >= N) continue;
 #pragma unroll
@@ -242,14 +242,19 @@ bool proj_supported(int H_I, int D_I, int d) {
 }
 
 static int proj_tm(int T) { return T <= 32 ? 16 : 64; }
+// output columns per workgroup: with 16-token tiles (decode) one 16-column
+// tile per wave, so that the weight stream is spread over twice as many
+// workgroups (a read of this size reaches about 3.5 TB/s from 528 workgroups
+// and 5.5 from 1024); two per wave otherwise
+static int proj_bn(int T) { return proj_tm(T) == 16 ? 64 : 128; }
 
-// splits of the hidden dims: enough workgroups to fill the chip, each slice
-// at least 256 dims and a whole number of stages
+// splits of the hidden dims: enough workgroups to fill the chip (about 1024),
+// each slice at least 256 dims and a whole number of stages
 static int proj_splits(int T, int d, int H_I, int D_I) {
   const int N = H_I * D_I + H_I + D_I;
-  const int base = ((N + PJ_BN - 1) / PJ_BN) * ((T + proj_tm(T) - 1) / proj_tm(T));
+  const int base = ((N + proj_bn(T) - 1) / proj_bn(T)) * ((T + proj_tm(T) - 1) / proj_tm(T));
   int s = 1;
-  while (base * s < 512 && 2 * s <= PJ_MAX_SPLITS && d % (2 * s * PJ_BK) == 0 && d / (2 * s) >= 256) s *= 2;
+  while (base * s < 1024 && 2 * s <= PJ_MAX_SPLITS && d % (2 * s * PJ_BK) == 0 && d / (2 * s) >= 256) s *= 2;
   return s;
 }
 
@@ -274,12 +279,13 @@ hipError_t launch_indexer_project(int T, int d, int H_I, int D_I, const uint16_t
   const int kchunk = d / splits;
   const int tm = proj_tm(T);
   float* part = static_cast<float*>(proj_layout(T, d, H_I, D_I).at(ws, 0));
-  const dim3 grid((N + PJ_BN - 1) / PJ_BN, (T + tm - 1) / tm, splits);
+  const int bn = proj_bn(T);
+  const dim3 grid((N + bn - 1) / bn, (T + tm - 1) / tm, splits);
   if (tm == 16)
-    hipLaunchKernelGGL(proj_gemm_kernel<16>, grid, dim3(PJ_NT), 0, stream, h, wq, ww, wk, T, d, Nq, Nw, N, kchunk,
+    hipLaunchKernelGGL((proj_gemm_kernel<16, 1>), grid, dim3(PJ_NT), 0, stream, h, wq, ww, wk, T, d, Nq, Nw, N, kchunk,
                        part);
   else
-    hipLaunchKernelGGL(proj_gemm_kernel<64>, grid, dim3(PJ_NT), 0, stream, h, wq, ww, wk, T, d, Nq, Nw, N, kchunk,
+    hipLaunchKernelGGL((proj_gemm_kernel<64, 2>), grid, dim3(PJ_NT), 0, stream, h, wq, ww, wk, T, d, Nq, Nw, N, kchunk,
                        part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
