@@ -290,6 +290,27 @@ def test_dense_target_given_lse_matches_oracle(name):
         np.testing.assert_allclose(tgt[t, :n].sum(), 1.0, rtol=1e-4)
 
 
+def test_dense_target_given_lse_at_128k():
+    """The one-pass form over all 131072 positions of one sequence (64
+    chunks), given the oracle's dense lse, against the oracle's target."""
+    cfg = I.scaled(I.CONFIGS["decode128k"], B=1, planted_frac=0.0)
+    x = I.make_inputs(cfg, DEV)
+    p = DSAPath(x)
+    print(f"dense target given lse 128K: T={x.T} max_len={x.max_len}", flush=True)
+    lse = torch.from_numpy(_dense_oracle_lse(x, 0)[None].astype(np.float32)).to(DEV)
+    target = torch.full((x.T, p.ld), -7.0, dtype=torch.float32, device=DEV)
+    B.dsa_indexer_kl_target_dense_lse(p.q, p.layout, cfg.H, x.q, x.kv, cfg.scale, lse, target)
+    torch.cuda.synchronize()
+    n = int(x.pos[0]) + 1
+    sel = np.arange(n, dtype=np.int32)[None]
+    ref = O.indexer_kl_target(I.bf16_bits(x.q[0:1]), I.bf16_bits(x.kv), sel, np.array([int(x.seq_id[0])]), cfg.scale,
+                              _bt(x))[0]
+    tgt = np_(target)[0]
+    err = np.abs(tgt[:n] - ref)
+    assert np.all(err <= 1e-3 * ref + 1e-12), f"max relative err {np.max(err / ref):.3g}"
+    np.testing.assert_allclose(tgt[:n].sum(), 1.0, rtol=1e-4)
+
+
 def test_dense_target_one_pass_equals_two_pass():
     """Given the two-pass form's own lse, the one-pass form computes the same
     target (up to the lse's rounding through natural-log units)."""
