@@ -80,6 +80,27 @@ def test_projection_bit_exact_on_exact_inputs(T, d, H_I, D_I, with_k):
         assert np.array_equal(k, rk)
 
 
+def test_projection_full_chunk_sampled():
+    """The 4096-token chunk at the model's width (the launch the chunk
+    benchmark times), on exact inputs: sampled tokens bit for bit."""
+    T, d, H_I, D_I = 4096, 7168, 64, 128
+    h = _gen(3, (T, d), "int")
+    wq, ww, wk = (_gen(4, (H_I * D_I, d), "int8th"), _gen(5, (H_I, d), "int8th"), _gen(6, (D_I, d), "int8th"))
+    q8 = torch.empty((T, H_I, D_I), dtype=torch.uint8, device=DEV)
+    qs = torch.empty((T,), dtype=torch.float32, device=DEV)
+    w = torch.empty((T, H_I), dtype=torch.float32, device=DEV)
+    k = torch.empty((T, D_I), dtype=torch.float32, device=DEV)
+    ws = B.workspace(B.dsa_workspace_bytes(B.DSA_OP_INDEXER_PROJ, T, d, H_I, D_I))
+    B.dsa_indexer_project(d, H_I, D_I, h, wq, ww, wk, q8, qs, w, k, ws)
+    torch.cuda.synchronize()
+    rows = [0, 1, 63, 64, 2047, 2048, 3000, 4095]
+    ref = O.indexer_projection(I.bf16_bits(h[rows]), I.bf16_bits(wq), I.bf16_bits(ww), H_I, D_I, I.bf16_bits(wk))
+    assert np.array_equal(np_(qs)[rows], ref[1])
+    assert np.array_equal(np_(q8)[rows], ref[0])
+    assert np.array_equal(np_(w)[rows], ref[2])
+    assert np.array_equal(np_(k)[rows], ref[3])
+
+
 @pytest.mark.parametrize("T,d,H_I,D_I", [(16, 7168, 64, 128), (70, 1024, 64, 128), (9, 512, 4, 64)])
 def test_projection_natural_inputs(T, d, H_I, D_I):
     (q8, qs, w, k), (rq8, rqs, rw, rk), (mq, mw, mk) = _run(T, d, H_I, D_I, True, exact=False, seed=7)
